@@ -1,0 +1,379 @@
+"""Pins for the fp64 oracle: each test checks it against something other than
+itself (brute force, torch library routines, identities of the mathematics,
+closed forms). CPU only."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import trimul_ref as ref
+from pair_rep_triangle_amd.inputs import make_random
+from tests.bruteforce import brute_force
+
+DIRS = ("outgoing", "incoming")
+
+
+def _case(B=1, N=4, c_z=3, c=2, seed=0, **kw):
+    d = make_random(B, N, c_z, c, seed=seed, **kw)
+    return d["z"].astype(np.float64), d["mask"].astype(np.float64), d["weights"]
+
+
+def _tolist(w):
+    return {k: np.asarray(v, dtype=np.float64).tolist() for k, v in w.items()}
+
+
+# --- brute force on tiny inputs ------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("B,N,c_z,c,mask", [
+    (1, 1, 1, 1, "ones"), (1, 2, 2, 1, "ones"), (2, 3, 3, 2, "random_residues"),
+    (1, 4, 2, 3, "block"), (1, 5, 4, 4, "random_residues"), (2, 3, 1, 3, "ones"),
+    (2, 4, 3, 2, "random_pairs"),
+])
+def test_bruteforce(direction, B, N, c_z, c, mask):
+    z, m, w = _case(B, N, c_z, c, seed=N * 7 + c_z, mask=mask)
+    got = ref.tri_mul_ref(z, m, w, direction)
+    want = np.array(brute_force(z.tolist(), m.tolist(), _tolist(w), direction))
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
+
+
+# --- independent composition of torch library routines in float64 -------------------------
+
+def torch_compose(z, m, w, direction, eps=1e-5):
+    F = torch.nn.functional
+    t = {k: torch.as_tensor(np.asarray(v, dtype=np.float64)) for k, v in w.items()}
+    z = torch.as_tensor(z, dtype=torch.float64)
+    m = torch.as_tensor(m, dtype=torch.float64)
+    c_z = z.shape[-1]
+    c = t["b_a_gate"].shape[0]
+    zn = F.layer_norm(z, (c_z,), t["ln_in_gamma"], t["ln_in_beta"], eps)
+    a = m[..., None] * torch.sigmoid(F.linear(zn, t["w_a_gate"], t["b_a_gate"])) \
+        * F.linear(zn, t["w_a_proj"], t["b_a_proj"])
+    b = m[..., None] * torch.sigmoid(F.linear(zn, t["w_b_gate"], t["b_b_gate"])) \
+        * F.linear(zn, t["w_b_proj"], t["b_b_proj"])
+    eq = "bikc,bjkc->bijc" if direction == "outgoing" else "bkic,bkjc->bijc"
+    x = torch.einsum(eq, a, b)
+    xn = F.layer_norm(x, (c,), t["ln_out_gamma"], t["ln_out_beta"], eps)
+    out = m[..., None] * torch.sigmoid(F.linear(zn, t["w_gate"], t["b_gate"])) \
+        * F.linear(xn, t["w_out"], t["b_out"])
+    return out.numpy()
+
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("B,N,c_z,c,mask", [(2, 7, 12, 10, "random_residues"),
+                                            (1, 9, 16, 16, "block")])
+def test_torch_library_composition(direction, B, N, c_z, c, mask):
+    z, m, w = _case(B, N, c_z, c, seed=3, mask=mask)
+    np.testing.assert_allclose(ref.tri_mul_ref(z, m, w, direction),
+                               torch_compose(z, m, w, direction), rtol=1e-11, atol=1e-12)
+
+
+# --- identities of the mathematics ---------------------------------------------------------
+
+def _swap_ab(w):
+    s = dict(w)
+    for part in ("gate", "proj"):
+        s[f"w_a_{part}"], s[f"w_b_{part}"] = w[f"w_b_{part}"], w[f"w_a_{part}"]
+        s[f"b_a_{part}"], s[f"b_b_{part}"] = w[f"b_b_{part}"], w[f"b_a_{part}"]
+    return s
+
+
+def _T(x):  # swap the two residue axes
+    return np.swapaxes(x, 1, 2)
+
+
+def test_transpose_identity_full_op():
+    """incoming(z, m; W_a, W_b) == outgoing(z^T, m^T; W_b, W_a)^T at every (i, j)."""
+    z, m, w = _case(2, 6, 5, 4, seed=11, mask="random_residues")
+    m = m * (np.random.default_rng(1).random(m.shape) < 0.8)  # non-symmetric mask
+    inc = ref.tri_mul_ref(z, m, w, "incoming")
+    out_t = _T(ref.tri_mul_ref(_T(z), _T(m), _swap_ab(w), "outgoing"))
+    np.testing.assert_allclose(inc, out_t, rtol=1e-12, atol=1e-13)
+
+
+def test_transpose_identity_literal():
+    """With a constant output gate and a symmetric mask, incoming(z) == outgoing(z^T)
+    element by element, with the same weights."""
+    z, m, w = _case(1, 6, 5, 4, seed=12, mask="block", valid=[4])
+    w = dict(w, w_gate=np.zeros_like(w["w_gate"]))
+    np.testing.assert_allclose(ref.tri_mul_ref(z, m, w, "incoming"),
+                               ref.tri_mul_ref(_T(z), _T(m), w, "outgoing"),
+                               rtol=1e-12, atol=1e-13)
+
+
+def test_contraction_is_edge_pattern():
+    """Pre-gate tensors: x_incoming(z) == x_outgoing(z^T) for any weights."""
+    z, m, w = _case(1, 5, 4, 3, seed=13)
+    xi = ref.tri_mul_intermediates(z, m, w, "incoming")["x"]
+    xo = ref.tri_mul_intermediates(_T(z), _T(m), w, "outgoing")["x"]
+    np.testing.assert_allclose(xi, xo, rtol=1e-12, atol=1e-13)
+
+
+def test_symmetric_z_directions_agree():
+    z, m, w = _case(1, 6, 4, 3, seed=14)
+    z = 0.5 * (z + _T(z))
+    np.testing.assert_allclose(ref.tri_mul_ref(z, m, w, "outgoing"),
+                               ref.tri_mul_ref(z, m, w, "incoming"), rtol=1e-12, atol=1e-13)
+
+
+def test_asymmetric_z_directions_differ():
+    z, m, w = _case(1, 6, 4, 3, seed=15)
+    d = ref.tri_mul_ref(z, m, w, "outgoing") - ref.tri_mul_ref(z, m, w, "incoming")
+    assert np.abs(d).max() > 1e-3
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_permutation_equivariance(direction):
+    z, m, w = _case(1, 7, 4, 3, seed=16, mask="random_residues")
+    P = np.random.default_rng(2).permutation(7)
+    got = ref.tri_mul_ref(z[:, P][:, :, P], m[:, P][:, :, P], w, direction)
+    want = ref.tri_mul_ref(z, m, w, direction)[:, P][:, :, P]
+    np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_crop_invariance_block_mask(direction):
+    """Padded residues contribute nothing: the valid block equals the op on the
+    cropped L x L input; padded outputs are 0; padding values are irrelevant."""
+    N, L = 9, 6
+    z, m, w = _case(1, N, 5, 4, seed=17, mask="block", valid=[L])
+    full = ref.tri_mul_ref(z, m, w, direction)
+    crop = ref.tri_mul_ref(z[:, :L, :L], np.ones((1, L, L)), w, direction)
+    np.testing.assert_allclose(full[:, :L, :L], crop, rtol=1e-12, atol=1e-13)
+    assert np.all(full[:, L:, :] == 0) and np.all(full[:, :, L:] == 0)
+    z2 = z.copy()
+    z2[:, L:, :] = 1e3 * np.random.default_rng(3).standard_normal(z2[:, L:, :].shape)
+    z2[:, :, L:] = -7.0
+    np.testing.assert_allclose(ref.tri_mul_ref(z2, m, w, direction), full, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_crop_invariance_scattered_residues(direction):
+    """Residue mask r_i r_j with holes anywhere: the valid rows/cols equal the op
+    on the compacted tensor."""
+    z, m, w = _case(1, 8, 4, 3, seed=18)
+    r = np.array([1, 0, 1, 1, 0, 1, 0, 1], dtype=np.float64)
+    m = (r[:, None] * r[None, :])[None]
+    idx = np.flatnonzero(r)
+    full = ref.tri_mul_ref(z, m, w, direction)
+    comp = ref.tri_mul_ref(z[:, idx][:, :, idx], np.ones((1, idx.size, idx.size)), w, direction)
+    np.testing.assert_allclose(full[:, idx][:, :, idx], comp, rtol=1e-12, atol=1e-13)
+
+
+# --- closed forms --------------------------------------------------------------------------
+
+def test_n1_directions_agree_and_x_is_product():
+    z, m, w = _case(2, 1, 6, 5, seed=19)
+    io = ref.tri_mul_intermediates(z, m, w, "outgoing")
+    ii = ref.tri_mul_intermediates(z, m, w, "incoming")
+    np.testing.assert_allclose(io["x"], io["a"] * io["b"], rtol=1e-14)
+    np.testing.assert_allclose(io["out"], ii["out"], rtol=1e-14)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("N,L", [(5, 5), (7, 3), (6, 1)])
+def test_constant_z_block_mask(direction, N, L):
+    """z_ij = v everywhere, mask on the L x L block: x = L * (alpha (.) beta) on the
+    block (the sum over k counts exactly L terms) and 0 outside; out constant on
+    the block and 0 outside. alpha, beta are evaluated with scalar math here."""
+    import math
+    rng = np.random.default_rng(20)
+    c_z, c = 4, 3
+    d = make_random(1, N, c_z, c, seed=21, mask="block", valid=[L])
+    w = {k: np.asarray(v, dtype=np.float64) for k, v in d["weights"].items()}
+    v = rng.standard_normal(c_z)
+    z = np.broadcast_to(v, (1, N, N, c_z)).copy()
+    mu = sum(v) / c_z
+    var = sum((t - mu) ** 2 for t in v) / c_z
+    vh = [(v[t] - mu) / math.sqrt(var + 1e-5) * w["ln_in_gamma"][t] + w["ln_in_beta"][t]
+          for t in range(c_z)]
+
+    def gp(which, ch):
+        g = sum(w[f"w_{which}_gate"][ch][t] * vh[t] for t in range(c_z)) + w[f"b_{which}_gate"][ch]
+        p = sum(w[f"w_{which}_proj"][ch][t] * vh[t] for t in range(c_z)) + w[f"b_{which}_proj"][ch]
+        return p / (1.0 + math.exp(-g))
+
+    x_block = np.array([L * gp("a", ch) * gp("b", ch) for ch in range(c)])
+    it = ref.tri_mul_intermediates(z, d["mask"], w, direction)
+    np.testing.assert_allclose(it["x"][0, :L, :L], np.broadcast_to(x_block, (L, L, c)), rtol=1e-12)
+    assert np.all(it["x"][0, L:, :] == 0) and np.all(it["x"][0, :, L:] == 0)
+    out = it["out"][0]
+    np.testing.assert_allclose(out[:L, :L], np.broadcast_to(out[0, 0], (L, L, c_z)), rtol=1e-12)
+    assert np.all(out[L:, :] == 0) and np.all(out[:, L:] == 0)
+
+
+def test_zero_gate_weights_give_half():
+    z, m, w = _case(1, 5, 4, 3, seed=22)
+    w0 = dict(w, w_gate=np.zeros_like(w["w_gate"]), b_gate=np.zeros_like(w["b_gate"]))
+    it = ref.tri_mul_intermediates(z, m, w0, "outgoing")
+    xn = torch.nn.functional.layer_norm(torch.as_tensor(it["x"]), (3,),
+                                        torch.as_tensor(w["ln_out_gamma"], dtype=torch.float64),
+                                        torch.as_tensor(w["ln_out_beta"], dtype=torch.float64))
+    p = xn.numpy() @ np.asarray(w["w_out"], np.float64).T + np.asarray(w["b_out"], np.float64)
+    np.testing.assert_allclose(it["out"], 0.5 * m[..., None] * p, rtol=1e-12, atol=1e-14)
+
+
+def test_linear_in_output_projection():
+    z, m, w = _case(1, 5, 4, 3, seed=23)
+    w2 = dict(w, w_out=2.5 * np.asarray(w["w_out"], np.float64),
+              b_out=2.5 * np.asarray(w["b_out"], np.float64))
+    np.testing.assert_allclose(ref.tri_mul_ref(z, m, w2, "incoming"),
+                               2.5 * ref.tri_mul_ref(z, m, w, "incoming"), rtol=1e-12, atol=1e-14)
+
+
+def test_layernorm_scale_invariance():
+    """LN_in: scaling z changes out only through eps; LN_out: scaling the a-projection
+    (W_ap, b_ap) scales x, which LN_out removes. Checked with a tiny eps so the
+    invariance is exact to rounding."""
+    z, m, w = _case(1, 5, 6, 4, seed=24)
+    e = 1e-14
+    base = ref.tri_mul_ref(z, m, w, "outgoing", eps=e)
+    np.testing.assert_allclose(ref.tri_mul_ref(30.0 * z, m, w, "outgoing", eps=e), base,
+                               rtol=1e-9, atol=1e-11)
+    w3 = dict(w, w_a_proj=40.0 * np.asarray(w["w_a_proj"], np.float64),
+              b_a_proj=40.0 * np.asarray(w["b_a_proj"], np.float64))
+    np.testing.assert_allclose(ref.tri_mul_ref(z, m, w3, "outgoing", eps=e), base, rtol=1e-9, atol=1e-11)
+    # with the default eps the same changes are visible but small
+    d = ref.tri_mul_ref(z, m, w3, "outgoing") - ref.tri_mul_ref(z, m, w, "outgoing")
+    assert 0 < np.abs(d).max() < 1e-2
+
+
+def test_batch_independence():
+    z, m, w = _case(3, 5, 4, 3, seed=25, mask="random_residues")
+    full = ref.tri_mul_ref(z, m, w, "incoming")
+    for b in range(3):
+        np.testing.assert_allclose(full[b:b + 1], ref.tri_mul_ref(z[b:b + 1], m[b:b + 1], w, "incoming"),
+                                   rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_sampled_pairs_match_full(direction):
+    z, m, w = _case(2, 9, 6, 5, seed=26, mask="random_residues")
+    full = ref.tri_mul_ref(z, m, w, direction)
+    rng = np.random.default_rng(4)
+    bi, ii, jj = rng.integers(0, 2, 20), rng.integers(0, 9, 20), rng.integers(0, 9, 20)
+    np.testing.assert_allclose(ref.tri_mul_ref_pairs(z, m, w, direction, bi, ii, jj),
+                               full[bi, ii, jj], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(ref.tri_mul_ref_pairs(z, None, w, direction, bi, ii, jj),
+                               ref.tri_mul_ref(z, None, w, direction)[bi, ii, jj], rtol=1e-12, atol=1e-13)
+
+
+# --- the pins are sharp: plausible mistakes planted in the oracle (on the CPU) fail them ---
+
+def _pins_pass():
+    ok = True
+    for direction in DIRS:
+        z, m, w = _case(1, 3, 3, 2, seed=31, mask="random_pairs")
+        got = ref.tri_mul_ref(z, m, w, direction)
+        want = np.array(brute_force(z.tolist(), m.tolist(), _tolist(w), direction))
+        ok &= np.allclose(got, want, rtol=1e-9, atol=1e-12)
+        z, m, w = _case(1, 5, 6, 4, seed=32, mask="block", valid=[4])
+        ok &= np.allclose(ref.tri_mul_ref(z, m, w, direction), torch_compose(z, m, w, direction),
+                          rtol=1e-9, atol=1e-12)
+    return bool(ok)
+
+
+_orig = {name: getattr(ref, name) for name in
+         ("layer_norm", "sigmoid", "linear", "input_operands", "contract", "output_stage")}
+
+
+def _mut_ln_no_beta(x, gamma, beta, eps=ref.EPS):
+    return _orig["layer_norm"](x, gamma, np.zeros_like(np.asarray(beta, np.float64)), eps)
+
+
+def _mut_ln_unbiased(x, gamma, beta, eps=ref.EPS):
+    x = np.asarray(x, np.float64)
+    mu = x.mean(-1, keepdims=True)
+    var = x.var(-1, ddof=1, keepdims=True) if x.shape[-1] > 1 else np.zeros_like(mu)
+    return (x - mu) / np.sqrt(var + eps) * gamma + beta
+
+
+def _mut_ln_eps_outside(x, gamma, beta, eps=ref.EPS):
+    x = np.asarray(x, np.float64)
+    mu = x.mean(-1, keepdims=True)
+    return (x - mu) / (np.sqrt(((x - mu) ** 2).mean(-1, keepdims=True)) + eps) * gamma + beta
+
+
+def _mut_sigmoid_sign(t):
+    return 1.0 / (1.0 + np.exp(np.asarray(t, np.float64)))
+
+
+def _mut_linear_no_bias(x, w, b):
+    return np.asarray(x, np.float64) @ np.asarray(w, np.float64).T
+
+
+def _mut_contract_transposed_b(a, b, direction):
+    return _orig["contract"](a, np.swapaxes(b, 1, 2), direction)
+
+
+def _mut_contract_same_pattern(a, b, direction):
+    return _orig["contract"](a, b, "outgoing")
+
+
+def _mut_contract_mean(a, b, direction):
+    return _orig["contract"](a, b, direction) / a.shape[1]
+
+
+def _mut_operands_unmasked_b(z, mask, w, eps=ref.EPS):
+    zhat, a, _ = _orig["input_operands"](z, mask, w, eps)
+    _, _, b = _orig["input_operands"](z, np.ones_like(np.asarray(mask, np.float64)), w, eps)
+    return zhat, a, b
+
+
+def _mut_operands_swapped_roles(z, mask, w, eps=ref.EPS):
+    w2 = dict(w, w_a_gate=w["w_a_proj"], w_a_proj=w["w_a_gate"],
+              b_a_gate=w["b_a_proj"], b_a_proj=w["b_a_gate"])
+    return _orig["input_operands"](z, mask, w2, eps)
+
+
+def _mut_output_gate_raw_z(x, zhat, mask, w, eps=ref.EPS):
+    # gate fed with a rescaled (un-normalised-looking) input
+    return _orig["output_stage"](x, 2.0 * zhat + 0.3, mask, w, eps)
+
+
+def _mut_output_no_mask(x, zhat, mask, w, eps=ref.EPS):
+    return _orig["output_stage"](x, zhat, np.ones_like(np.asarray(mask, np.float64)), w, eps)
+
+
+MUTANTS = {
+    "ln_no_beta": ("layer_norm", _mut_ln_no_beta),
+    "ln_unbiased_var": ("layer_norm", _mut_ln_unbiased),
+    "ln_eps_outside_root": ("layer_norm", _mut_ln_eps_outside),
+    "sigmoid_sign": ("sigmoid", _mut_sigmoid_sign),
+    "linear_no_bias": ("linear", _mut_linear_no_bias),
+    "contract_transposed_b": ("contract", _mut_contract_transposed_b),
+    "contract_same_pattern_both_dirs": ("contract", _mut_contract_same_pattern),
+    "contract_mean_not_sum": ("contract", _mut_contract_mean),
+    "b_operand_unmasked": ("input_operands", _mut_operands_unmasked_b),
+    "gate_proj_roles_swapped": ("input_operands", _mut_operands_swapped_roles),
+    "output_gate_wrong_input": ("output_stage", _mut_output_gate_raw_z),
+    "output_unmasked": ("output_stage", _mut_output_no_mask),
+}
+
+
+def test_pins_pass_unmutated():
+    assert _pins_pass()
+
+
+@pytest.mark.parametrize("mutant", sorted(MUTANTS))
+def test_planted_mistake_is_caught(mutant, monkeypatch):
+    name, fn = MUTANTS[mutant]
+    monkeypatch.setattr(ref, name, fn)
+    assert not _pins_pass(), f"planted mistake {mutant!r} slipped through the pins"
+
+
+def test_golden_regression_fixture():
+    """The oracle still reproduces the fixture written by tests/golden/make_golden.py
+    (inputs are stored in the file, so this does not depend on the RNG)."""
+    import json
+    import os
+    with open(os.path.join(os.path.dirname(__file__), "golden", "oracle_small.json")) as f:
+        rec = json.load(f)
+    z, m = np.array(rec["z"]), np.array(rec["mask"])
+    w = {k: np.array(v) for k, v in rec["weights"].items()}
+    for direction in DIRS:
+        it = ref.tri_mul_intermediates(z, m, w, direction)
+        np.testing.assert_allclose(it["x"], np.array(rec[direction]["x"]), rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(it["out"], np.array(rec[direction]["out"]), rtol=1e-13, atol=1e-15)
+        want = np.array(brute_force(rec["z"], rec["mask"], rec["weights"], direction))
+        np.testing.assert_allclose(np.array(rec[direction]["out"]), want, rtol=1e-12, atol=1e-13)
