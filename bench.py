@@ -1,0 +1,206 @@
+#!/usr/bin/env python3
+"""Benchmark of the triangle multiplicative update on one MI355X.
+
+One step = the outgoing update and the incoming update (each: input gate,
+contraction, output gate) on one seeded synthetic batch resident in HBM.
+Prints ONE JSON line:
+  value         TFLOP/s over the step (matmul flops of both directions)
+  roofline      the dominant kernel's algorithmic GB/s (or TFLOP/s) against the
+                MI355X peak, from HIP events around that kernel in the timed region
+  cpu_baseline  the fp64 oracle timed on this host (rank 0, N=1 only)
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "triangle-mult-update TFLOP/s & pair-updates/s at N=512,c_z=128 bf16 (1 GPU)"
+KERNELS = ("k1_input_gate", "k2_contract", "k3_output_gate")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", default=None)
+    p.add_argument("--seed", type=int, default=0)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-kernel-events", action="store_true",
+                   help="time whole steps only (no events between the kernels)")
+    return p.parse_args()
+
+
+def cpu_baseline(d, directions, threads):
+    """The fp64 oracle as it stands, on the same workload, both directions."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    from oracle import tri_mul_ref
+    z = torch.from_numpy(d["z"]).to(torch.bfloat16).to(torch.float64).numpy()
+    with threadpool_limits(limits=threads):
+        t0 = time.perf_counter()
+        for direction, w in directions:
+            tri_mul_ref(z, d["mask"], w, direction)
+        dt = time.perf_counter() - t0
+    return dt
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the operator is not sharded "
+              "across GPUs (run with --gpus 1).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from pair_rep_triangle_amd.inputs import HEADLINE, WORKLOADS, make_weights, make_workload
+    from pair_rep_triangle_amd.metrics import MI355X_PEAK, flops_per_pair, kernel_work
+    from pair_rep_triangle_amd.trimul import TriMul
+
+    name = args.workload or HEADLINE
+    spec = WORKLOADS[name]
+    d = make_workload(name, seed=args.seed)
+    B, n, c_z, c, dtype = spec["batch"], spec["n"], spec["c_z"], spec["c"], spec["dtype"]
+    w_out = d["weights"]
+    w_in = make_weights(np.random.default_rng(args.seed + 1), c_z, c)  # second module
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    esz = 2 if dtype == "bf16" else 4
+
+    dev = torch.device("cuda:0")
+    z = torch.from_numpy(d["z"]).to(tdt).to(dev)
+    mask = torch.from_numpy(d["mask"]).to(tdt).to(dev)
+    mods = [("outgoing", TriMul(w_out, c_z, c, dtype)), ("incoming", TriMul(w_in, c_z, c, dtype))]
+    ws = mods[0][1].new_workspace(B, n, device=dev)
+    outs = [torch.empty_like(z) for _ in mods]
+    stream = torch.cuda.current_stream(dev)
+
+    def step(events=None):
+        k = 0
+        for (direction, mod), out in zip(mods, outs):
+            if events is None:
+                mod.forward(z, mask, out=out, direction=direction, workspace=ws)
+                continue
+            for s in (1, 2, 3):
+                mod.stage(s, z, mask, out=out, direction=direction, workspace=ws)
+                events[k + 1].record(stream)
+                k += 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    use_ev = not args.no_kernel_events
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for k in range(args.steps):
+        if use_ev:
+            evs[k][0].record(stream)
+            step(evs[k])
+        else:
+            step()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    ms_step = total_ms / args.steps
+
+    pairs = B * n * n
+    fl_dir = flops_per_pair(n, c_z, c) * pairs
+    tflops = 2 * fl_dir / (ms_step * 1e-3) / 1e12
+    pair_updates = 2 * pairs / (ms_step * 1e-3)
+
+    work = kernel_work(n, c_z, c, esz)
+    kernels = {}
+    if use_ev:
+        per = np.zeros((args.steps, 6))
+        for k in range(args.steps):
+            for j in range(6):
+                per[k, j] = evs[k][j].elapsed_time(evs[k][j + 1])
+        for idx, kname in enumerate(KERNELS):
+            samples = np.concatenate([per[:, idx], per[:, idx + 3]])  # both directions
+            avg_ms = float(samples.mean())
+            wk = work[kname]
+            gbps = wk["bytes"] * pairs / (avg_ms * 1e-3) / 1e9
+            tfl = wk["flops"] * pairs / (avg_ms * 1e-3) / 1e12
+            ai = wk["flops"] / wk["bytes"]
+            peak_fl = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+            ridge = peak_fl * 1e12 / (MI355X_PEAK["hbm_GBps"] * 1e9)
+            bound = "hbm" if ai < ridge else "mfma"
+            kernels[kname] = {
+                "avg_us": round(avg_ms * 1e3, 3), "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1),
+                "hbm_frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4),
+                "mfma_frac": round(tfl / peak_fl, 4), "bound": bound,
+                "bytes_per_launch": wk["bytes"] * pairs, "flops_per_launch": wk["flops"] * pairs,
+            }
+
+    roofline = None
+    if kernels:
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+        kd = kernels[dom]
+        traffic = None
+        try:
+            with open(TRAFFIC_FILE) as f:
+                tr = json.load(f).get(name, {}).get(dom)
+            if tr and tr.get("source_sha") == _kernel_source_sha():
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+        if kd["bound"] == "hbm":
+            roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GBps"],
+                        "peak": MI355X_PEAK["hbm_GBps"], "unit": "GB/s",
+                        "frac": round(kd["GBps"] / MI355X_PEAK["hbm_GBps"], 4), "traffic": traffic}
+        else:
+            pk = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+            roofline = {"kernel": dom, "bound": "mfma", "achieved": kd["TFLOPs"], "peak": pk,
+                        "unit": "TFLOP/s", "frac": round(kd["TFLOPs"] / pk, 4), "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        threads = min(16, len(os.sched_getaffinity(0)))
+        dt = cpu_baseline(d, [("outgoing", w_out), ("incoming", w_in)], threads)
+        cpu = {"value": round(2 * fl_dir / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+               "kind": "oracle", "seconds": round(dt, 2),
+               "pair_updates_per_s": round(2 * pairs / dt, 1),
+               "sample": f"whole workload {name}, outgoing + incoming, fp64 NumPy oracle"}
+
+    rec = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "batch": B, "n": n, "c_z": c_z, "c": c,
+                   "valid_length": d["meta"].get("valid_length", n),
+                   "directions": "outgoing+incoming", "mask": spec["mask"]},
+        "pair_updates_per_s": round(pair_updates, 1),
+        "wall_s": round(wall, 3),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def _kernel_source_sha():
+    import hashlib
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "pair_rep_triangle_amd", "csrc", "kernels.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+if __name__ == "__main__":
+    main()

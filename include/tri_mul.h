@@ -1,0 +1,134 @@
+/*
+ * tri_mul.h -- C ABI of the MI355X (gfx950) triangle multiplicative update.
+ *
+ * The operator (per batch item b and residue pair (i, j)):
+ *   zhat = LayerNorm_cz(z_bij; gamma_in, beta_in)            eps 1e-5, biased var
+ *   a_bij = m_bij * sigmoid(W_ag zhat + b_ag) * (W_ap zhat + b_ap)     [c]
+ *   b_bij = m_bij * sigmoid(W_bg zhat + b_bg) * (W_bp zhat + b_bp)     [c]
+ *   outgoing: x_bij = sum_k a_bik * b_bjk     incoming: x_bij = sum_k a_bki * b_bkj
+ *   out_bij = m_bij * sigmoid(W_g zhat + b_g) * (W_o LayerNorm_c(x_bij; gamma_out, beta_out) + b_o)
+ * Sources: RFProteína architecture page (BioNeMo Inference Runtime docs),
+ * "Triangle multiplication on SM90" (the K1 -> K2 -> K3 chain: input projection
+ * with the input LayerNorm folded in, the contraction compiled per direction,
+ * output gate and projection with both LayerNorms folded in) and "Dual-GEMM
+ * gates" (the x_x form sigma(x W_g^T + b_g) * (x W_p^T + b_p) for the input
+ * gate, which absorbs the pair mask and emits its output transposed for the
+ * contraction; the x0_x1 form for the output gate, x0 = normalized input pair
+ * tensor, x1 = contracted hidden tensor). The index pattern of the two
+ * directions and the zero output on padded pairs are readings, not printed on
+ * the pages.
+ *
+ * Conventions
+ *   - Every function returns TRI_MUL_OK (0) or a negative TRI_MUL_ERR_* code;
+ *     tri_mul_strerror() names it. There is no fallback path: an unsupported
+ *     request is rejected, never silently run another way.
+ *   - Device pointers are HIP device memory on the device that was current at
+ *     tri_mul_create(); that device must be current at every forward call.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Forward calls only enqueue work: they never allocate, never synchronise
+ *     and return before the GPU has finished.
+ */
+#ifndef TRI_MUL_H
+#define TRI_MUL_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TRI_MUL_OK 0
+#define TRI_MUL_ERR_INVALID_ARG -1        /* NULL pointer, size out of range, bad enum   */
+#define TRI_MUL_ERR_UNSUPPORTED -2        /* c_z or c not a multiple of 16 / too large    */
+#define TRI_MUL_ERR_UNSUPPORTED_DEVICE -3 /* current device is not gfx950 / wrong device */
+#define TRI_MUL_ERR_ALIGNMENT -4          /* a device pointer not 16-byte aligned         */
+#define TRI_MUL_ERR_ALIAS -5              /* out or workspace overlaps another buffer     */
+#define TRI_MUL_ERR_WORKSPACE_TOO_SMALL -6
+#define TRI_MUL_ERR_HIP -7                /* a HIP runtime call or launch failed          */
+#define TRI_MUL_ERR_OUT_OF_MEMORY -8      /* tri_mul_create could not allocate weights    */
+
+#define TRI_MUL_MAX_N 32768               /* residues per side                            */
+#define TRI_MUL_MAX_WIDTH 1024            /* largest c_z and c                            */
+#define TRI_MUL_LN_EPS 1e-5f              /* epsilon of both LayerNorms                   */
+
+typedef enum { TRI_MUL_FP32 = 0, TRI_MUL_BF16 = 1 } tri_mul_dtype;
+typedef enum { TRI_MUL_OUTGOING = 0, TRI_MUL_INCOMING = 1 } tri_mul_direction;
+
+/* Host fp32 weights, nn.Linear orientation: a matrix is [out][in], row-major.
+ * NULL gamma means all ones; NULL beta and NULL bias mean zeros; the weight
+ * matrices themselves are required. The arrays are read during
+ * tri_mul_create() only and may be freed when it returns. */
+typedef struct tri_mul_weights {
+  const float *ln_in_gamma, *ln_in_beta;                  /* [c_z]               */
+  const float *w_a_gate, *b_a_gate, *w_a_proj, *b_a_proj; /* [c][c_z], [c]       */
+  const float *w_b_gate, *b_b_gate, *w_b_proj, *b_b_proj; /* [c][c_z], [c]       */
+  const float *ln_out_gamma, *ln_out_beta;                /* [c]                 */
+  const float *w_out, *b_out;                             /* [c_z][c], [c_z]     */
+  const float *w_gate, *b_gate;                           /* [c_z][c_z], [c_z]   */
+} tri_mul_weights;
+
+typedef struct tri_mul_handle tri_mul_handle;
+
+/* Where the intermediates live inside a workspace (byte offsets from its
+ * start). a, b and x are each [batch][c][n_pad][n_pad] in the handle's dtype,
+ * n_pad = n rounded up to a multiple of 128, entries outside n x n are zero
+ * for a and b. For outgoing, a[b][ch][i][k] = a_bik; for incoming the input
+ * kernel stores the operands transposed, a[b][ch][i][k] = a_bki (same for b),
+ * so the contraction is x[b][ch][i][j] = sum_k a[..][i][k] * b[..][j][k] in
+ * both directions. */
+typedef struct tri_mul_layout {
+  size_t a_offset, b_offset, x_offset; /* bytes                         */
+  size_t total_bytes;                  /* = tri_mul_workspace_bytes()   */
+  int n_pad;                           /* padded side of a, b and x     */
+  int elem_bytes;                      /* 2 (bf16) or 4 (fp32)          */
+} tri_mul_layout;
+
+/* Build a handle: checks c_z, c (multiples of 16, at most TRI_MUL_MAX_WIDTH)
+ * and dtype, checks that the current device is gfx950, folds both LayerNorm
+ * affines into the projection weights (in double precision), converts them to
+ * `dtype` and copies them to the current device. The only call that allocates.
+ * On error *out is set to NULL. */
+int tri_mul_create(const tri_mul_weights* weights, int c_z, int c, int dtype,
+                   tri_mul_handle** out);
+
+/* Bytes of workspace a forward call needs for (batch, n). */
+int tri_mul_workspace_bytes(const tri_mul_handle* h, int batch, int n, size_t* bytes);
+
+/* Offsets of a, b and x inside the workspace (see tri_mul_layout). */
+int tri_mul_workspace_layout(const tri_mul_handle* h, int batch, int n, tri_mul_layout* out);
+
+/* The whole update for one direction: enqueues the three kernels on `stream`.
+ *   z          [batch][n][n][c_z]  contiguous, handle dtype, 16-byte aligned
+ *   pair_mask  [batch][n][n]       contiguous, handle dtype (0/1); NULL = all ones
+ *   out        [batch][n][n][c_z]  contiguous, handle dtype; must not overlap
+ *                                  z, pair_mask or the workspace
+ *   workspace  >= tri_mul_workspace_bytes(h, batch, n) bytes, 16-byte aligned,
+ *              must not overlap z, pair_mask or out; contents on entry ignored.
+ * Several streams may share a handle if each call has its own workspace. */
+int tri_mul_forward(tri_mul_handle* h, const void* z, const void* pair_mask, void* out,
+                    int batch, int n, int direction, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* One kernel of the chain, same arguments as tri_mul_forward:
+ *   stage 1: input LayerNorm + gated dual projection + mask -> a, b (workspace)
+ *   stage 2: contraction over k -> x (workspace)
+ *   stage 3: output LayerNorm + projection + output gate + mask -> out
+ * Running stages 1, 2, 3 in order equals tri_mul_forward. For inspection of the
+ * intermediates and for per-kernel timing. */
+int tri_mul_forward_stage(tri_mul_handle* h, int stage, const void* z, const void* pair_mask,
+                          void* out, int batch, int n, int direction, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* Releases the device weights. NULL is a no-op. Must not race a forward call. */
+void tri_mul_destroy(tri_mul_handle* h);
+
+/* Static text for an error code (never NULL). */
+const char* tri_mul_strerror(int code);
+
+/* Details of the last TRI_MUL_ERR_HIP on the calling thread (static text). */
+const char* tri_mul_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TRI_MUL_H */

@@ -100,8 +100,9 @@ def input_operands(z, mask, w, eps=EPS):
 
 def contract(a, b, direction):
     """Step 3 on [B, N, N, c] operands, one matmul per (batch, channel)."""
-    A = np.moveaxis(_f64(a), -1, 1)  # [B, c, N, N]
-    Bm = np.moveaxis(_f64(b), -1, 1)
+    # channel-major copies so that every per-channel product is a BLAS matmul
+    A = np.ascontiguousarray(np.moveaxis(_f64(a), -1, 1))  # [B, c, N, N]
+    Bm = np.ascontiguousarray(np.moveaxis(_f64(b), -1, 1))
     if direction == "outgoing":
         X = np.matmul(A, np.swapaxes(Bm, -1, -2))  # x_ij = sum_k a_ik b_jk
     elif direction == "incoming":

@@ -1,0 +1,308 @@
+// Host side of the C ABI declared in include/tri_mul.h: argument validation,
+// LayerNorm folding and weight packing, workspace layout, stage launches.
+
+#include "tri_mul.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "launch.h"
+
+struct tri_mul_handle {
+  int c_z, c, czp, cp, dtype, device;
+  bool bf16;
+  void* block;  // the one device allocation holding every packed weight
+  trimul::StageArgs w;  // weight pointers into `block` (activation fields unused)
+};
+
+namespace {
+
+thread_local char g_hip_err[256] = "no HIP error recorded";
+
+int hip_fail(hipError_t e, const char* what) {
+  snprintf(g_hip_err, sizeof(g_hip_err), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
+  return TRI_MUL_ERR_HIP;
+}
+
+uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u;
+  memcpy(&u, &f, 4);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+float bf16_to_f32(uint16_t h) {
+  uint32_t u = (uint32_t)h << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+// Folds y = W (gamma (.) xhat + beta) + bias into the stored matrix W' = W diag(gamma)
+// (rounded to the storage type, zero-padded from `cols` to `colsp`), s = row sums of
+// the stored W', t = W beta + bias. All sums in double.
+void fold(const float* W, const float* gamma, const float* beta, const float* bias, int rows,
+          int cols, int colsp, bool bf16, unsigned char* wdst, float* s, float* t) {
+  for (int r = 0; r < rows; ++r) {
+    double srow = 0.0, trow = bias ? (double)bias[r] : 0.0;
+    for (int k = 0; k < colsp; ++k) {
+      double v = 0.0;
+      if (k < cols) {
+        const double wk = W[(size_t)r * cols + k];
+        v = wk * (gamma ? (double)gamma[k] : 1.0);
+        if (beta) trow += wk * (double)beta[k];
+      }
+      const float vf = (float)v;
+      if (bf16) {
+        const uint16_t h = f32_to_bf16_rne(vf);
+        memcpy(wdst + ((size_t)r * colsp + k) * 2, &h, 2);
+        srow += bf16_to_f32(h);
+      } else {
+        memcpy(wdst + ((size_t)r * colsp + k) * 4, &vf, 4);
+        srow += vf;
+      }
+    }
+    s[r] = (float)srow;
+    t[r] = (float)trow;
+  }
+}
+
+bool overlaps(const void* p, size_t pn, const void* q, size_t qn) {
+  if (!p || !q || pn == 0 || qn == 0) return false;
+  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
+  return a < b + qn && b < a + pn;
+}
+
+struct Layout {
+  size_t a, b, x, total;
+  int np, esz;
+};
+
+Layout layout_of(const tri_mul_handle* h, int batch, int n) {
+  Layout L;
+  L.np = trimul::round_up(n, trimul::N_PAD);
+  L.esz = h->bf16 ? 2 : 4;
+  const size_t one = align256((size_t)batch * h->c * L.np * L.np * L.esz);
+  L.a = 0;
+  L.b = one;
+  L.x = 2 * one;
+  L.total = 3 * one;
+  return L;
+}
+
+int check_device(int* dev_out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDeviceProp_t prop;
+  e = hipGetDeviceProperties(&prop, dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
+  *dev_out = dev;
+  return TRI_MUL_OK;
+}
+
+int validate_call(const tri_mul_handle* h, int stage, const void* z, const void* mask,
+                  const void* out, int batch, int n, int direction, const void* ws,
+                  size_t ws_bytes) {
+  if (!h) return TRI_MUL_ERR_INVALID_ARG;
+  if (stage < 0 || stage > 3) return TRI_MUL_ERR_INVALID_ARG;
+  if (batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N) return TRI_MUL_ERR_INVALID_ARG;
+  if (direction != TRI_MUL_OUTGOING && direction != TRI_MUL_INCOMING) return TRI_MUL_ERR_INVALID_ARG;
+  if (!z || !out || !ws) return TRI_MUL_ERR_INVALID_ARG;
+  const Layout L = layout_of(h, batch, n);
+  const size_t t1d = (size_t)L.np / trimul::N_PAD;
+  if (t1d * t1d * (size_t)batch * h->c > 0x7fffffffu) return TRI_MUL_ERR_INVALID_ARG;
+  if (((uintptr_t)z | (uintptr_t)out | (uintptr_t)ws) & 15u) return TRI_MUL_ERR_ALIGNMENT;
+  if (mask && ((uintptr_t)mask & (uintptr_t)(L.esz - 1))) return TRI_MUL_ERR_ALIGNMENT;
+  if (ws_bytes < L.total) return TRI_MUL_ERR_WORKSPACE_TOO_SMALL;
+  const size_t pairs = (size_t)batch * n * n;
+  const size_t zb = pairs * h->c_z * L.esz, mb = pairs * L.esz;
+  if (overlaps(out, zb, z, zb) || overlaps(out, zb, mask, mb) || overlaps(out, zb, ws, L.total) ||
+      overlaps(ws, L.total, z, zb) || overlaps(ws, L.total, mask, mb))
+    return TRI_MUL_ERR_ALIAS;
+  return TRI_MUL_OK;
+}
+
+int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out, int batch, int n,
+        int direction, void* ws, size_t ws_bytes, void* stream) {
+  int rc = validate_call(h, stage, z, mask, out, batch, n, direction, ws, ws_bytes);
+  if (rc != TRI_MUL_OK) return rc;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != h->device) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
+  const Layout L = layout_of(h, batch, n);
+  trimul::StageArgs a = h->w;
+  a.z = z;
+  a.mask = mask;
+  a.out = out;
+  a.a = (unsigned char*)ws + L.a;
+  a.b = (unsigned char*)ws + L.b;
+  a.x = (unsigned char*)ws + L.x;
+  a.batch = batch;
+  a.n = n;
+  a.np = L.np;
+  a.incoming = direction == TRI_MUL_INCOMING;
+  hipStream_t st = (hipStream_t)stream;
+  for (int s = 1; s <= 3; ++s) {
+    if (stage != 0 && stage != s) continue;
+    e = trimul::launch_stage(s, h->bf16, a, st);
+    if (e != hipSuccess) return hip_fail(e, s == 1 ? "launch k1" : s == 2 ? "launch k2" : "launch k3");
+  }
+  return TRI_MUL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_handle** out) {
+  if (!out) return TRI_MUL_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!w || !w->w_a_gate || !w->w_a_proj || !w->w_b_gate || !w->w_b_proj || !w->w_out ||
+      !w->w_gate)
+    return TRI_MUL_ERR_INVALID_ARG;
+  if (c_z < 1 || c < 1) return TRI_MUL_ERR_INVALID_ARG;
+  if (dtype != TRI_MUL_FP32 && dtype != TRI_MUL_BF16) return TRI_MUL_ERR_UNSUPPORTED;
+  if (c_z % 16 || c % 16 || c_z > TRI_MUL_MAX_WIDTH || c > TRI_MUL_MAX_WIDTH)
+    return TRI_MUL_ERR_UNSUPPORTED;
+  int dev = -1;
+  int rc = check_device(&dev);
+  if (rc != TRI_MUL_OK) return rc;
+
+  const bool bf16 = dtype == TRI_MUL_BF16;
+  const int kg = trimul::k_group(bf16);
+  const int czp = trimul::round_up(c_z, kg), cp = trimul::round_up(c, kg);
+  const int esz = bf16 ? 2 : 4;
+  // block: w1 | wo | wg | s1 t1 | so to | sg tg
+  const size_t w1b = align256((size_t)4 * c * czp * esz);
+  const size_t wob = align256((size_t)c_z * cp * esz);
+  const size_t wgb = align256((size_t)c_z * czp * esz);
+  const size_t st1 = align256((size_t)8 * c * sizeof(float));
+  const size_t sto = align256((size_t)2 * c_z * sizeof(float));
+  const size_t total = w1b + wob + wgb + st1 + 2 * sto;
+  std::vector<unsigned char> host(total, 0);
+  unsigned char* hw1 = host.data();
+  unsigned char* hwo = hw1 + w1b;
+  unsigned char* hwg = hwo + wob;
+  float* hs1 = (float*)(hwg + wgb);
+  float* ht1 = hs1 + 4 * c;
+  float* hso = (float*)((unsigned char*)hs1 + st1);
+  float* hto = hso + c_z;
+  float* hsg = (float*)((unsigned char*)hso + sto);
+  float* htg = hsg + c_z;
+  const float* mats[4] = {w->w_a_gate, w->w_a_proj, w->w_b_gate, w->w_b_proj};
+  const float* biases[4] = {w->b_a_gate, w->b_a_proj, w->b_b_gate, w->b_b_proj};
+  for (int q = 0; q < 4; ++q)
+    fold(mats[q], w->ln_in_gamma, w->ln_in_beta, biases[q], c, c_z, czp, bf16,
+         hw1 + (size_t)q * c * czp * esz, hs1 + q * c, ht1 + q * c);
+  fold(w->w_out, w->ln_out_gamma, w->ln_out_beta, w->b_out, c_z, c, cp, bf16, hwo, hso, hto);
+  fold(w->w_gate, w->ln_in_gamma, w->ln_in_beta, w->b_gate, c_z, c_z, czp, bf16, hwg, hsg, htg);
+
+  tri_mul_handle* h = new (std::nothrow) tri_mul_handle();
+  if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
+  void* dptr = nullptr;
+  hipError_t e = hipMalloc(&dptr, total);
+  if (e != hipSuccess) {
+    delete h;
+    if (e == hipErrorOutOfMemory) return TRI_MUL_ERR_OUT_OF_MEMORY;
+    return hip_fail(e, "hipMalloc(weights)");
+  }
+  e = hipMemcpy(dptr, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(dptr);
+    delete h;
+    return hip_fail(e, "hipMemcpy(weights)");
+  }
+  unsigned char* d = (unsigned char*)dptr;
+  h->c_z = c_z;
+  h->c = c;
+  h->czp = czp;
+  h->cp = cp;
+  h->dtype = dtype;
+  h->device = dev;
+  h->bf16 = bf16;
+  h->block = dptr;
+  trimul::StageArgs& a = h->w;
+  memset(&a, 0, sizeof(a));
+  a.w1 = d;
+  a.wo = d + w1b;
+  a.wg = d + w1b + wob;
+  a.s1 = (const float*)(d + ((unsigned char*)hs1 - hw1));
+  a.t1 = (const float*)(d + ((unsigned char*)ht1 - hw1));
+  a.so = (const float*)(d + ((unsigned char*)hso - hw1));
+  a.to = (const float*)(d + ((unsigned char*)hto - hw1));
+  a.sg = (const float*)(d + ((unsigned char*)hsg - hw1));
+  a.tg = (const float*)(d + ((unsigned char*)htg - hw1));
+  a.cz = c_z;
+  a.czp = czp;
+  a.c = c;
+  a.cp = cp;
+  *out = h;
+  return TRI_MUL_OK;
+}
+
+int tri_mul_workspace_bytes(const tri_mul_handle* h, int batch, int n, size_t* bytes) {
+  if (!h || !bytes || batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N)
+    return TRI_MUL_ERR_INVALID_ARG;
+  *bytes = layout_of(h, batch, n).total;
+  return TRI_MUL_OK;
+}
+
+int tri_mul_workspace_layout(const tri_mul_handle* h, int batch, int n, tri_mul_layout* out) {
+  if (!h || !out || batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N)
+    return TRI_MUL_ERR_INVALID_ARG;
+  const Layout L = layout_of(h, batch, n);
+  out->a_offset = L.a;
+  out->b_offset = L.b;
+  out->x_offset = L.x;
+  out->total_bytes = L.total;
+  out->n_pad = L.np;
+  out->elem_bytes = L.esz;
+  return TRI_MUL_OK;
+}
+
+int tri_mul_forward(tri_mul_handle* h, const void* z, const void* pair_mask, void* out, int batch,
+                    int n, int direction, void* workspace, size_t workspace_bytes, void* stream) {
+  return run(h, 0, z, pair_mask, out, batch, n, direction, workspace, workspace_bytes, stream);
+}
+
+int tri_mul_forward_stage(tri_mul_handle* h, int stage, const void* z, const void* pair_mask,
+                          void* out, int batch, int n, int direction, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (stage < 1 || stage > 3) return TRI_MUL_ERR_INVALID_ARG;
+  return run(h, stage, z, pair_mask, out, batch, n, direction, workspace, workspace_bytes, stream);
+}
+
+void tri_mul_destroy(tri_mul_handle* h) {
+  if (!h) return;
+  if (h->block) (void)hipFree(h->block);
+  delete h;
+}
+
+const char* tri_mul_strerror(int code) {
+  switch (code) {
+    case TRI_MUL_OK: return "ok";
+    case TRI_MUL_ERR_INVALID_ARG: return "invalid argument (NULL pointer, size out of range or bad enum)";
+    case TRI_MUL_ERR_UNSUPPORTED: return "unsupported configuration (c_z and c must be multiples of 16, at most 1024; dtype fp32 or bf16)";
+    case TRI_MUL_ERR_UNSUPPORTED_DEVICE: return "unsupported device (needs gfx950, the device the handle was created on)";
+    case TRI_MUL_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
+    case TRI_MUL_ERR_ALIAS: return "output or workspace overlaps another buffer";
+    case TRI_MUL_ERR_WORKSPACE_TOO_SMALL: return "workspace smaller than tri_mul_workspace_bytes()";
+    case TRI_MUL_ERR_HIP: return "HIP runtime error (see tri_mul_last_hip_error)";
+    case TRI_MUL_ERR_OUT_OF_MEMORY: return "out of device memory";
+    default: return "unknown error code";
+  }
+}
+
+const char* tri_mul_last_hip_error(void) { return g_hip_err; }
+
+}  // extern "C"

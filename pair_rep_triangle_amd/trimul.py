@@ -1,0 +1,199 @@
+"""Python binding of libtrimul.so (ctypes): argument marshalling only.
+
+Every step of the operator runs in the HIP kernels behind the C ABI
+(include/tri_mul.h); PyTorch supplies device memory and the stream. There is
+no other execution path: if the library is missing or the call fails, this
+module raises.
+"""
+
+import ctypes
+import os
+
+import numpy as np
+
+from .inputs import WEIGHT_FIELDS
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtrimul.so")
+
+TRI_MUL_FP32, TRI_MUL_BF16 = 0, 1
+DIRECTIONS = {"outgoing": 0, "incoming": 1}
+DTYPES = {"fp32": TRI_MUL_FP32, "bf16": TRI_MUL_BF16}
+ERRORS = {
+    0: "OK", -1: "INVALID_ARG", -2: "UNSUPPORTED", -3: "UNSUPPORTED_DEVICE", -4: "ALIGNMENT",
+    -5: "ALIAS", -6: "WORKSPACE_TOO_SMALL", -7: "HIP", -8: "OUT_OF_MEMORY",
+}
+EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
+           "tri_mul_forward", "tri_mul_forward_stage", "tri_mul_destroy", "tri_mul_strerror",
+           "tri_mul_last_hip_error")
+
+
+class TriMulError(RuntimeError):
+    def __init__(self, code, what, detail=""):
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+        super().__init__(f"{what}: TRI_MUL_ERR_{self.name} ({code}) {detail}".rstrip())
+
+
+class Weights(ctypes.Structure):
+    _fields_ = [(name, ctypes.POINTER(ctypes.c_float)) for name in WEIGHT_FIELDS]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("a_offset", ctypes.c_size_t), ("b_offset", ctypes.c_size_t),
+                ("x_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
+                ("n_pad", ctypes.c_int), ("elem_bytes", ctypes.c_int)]
+
+
+_lib = None
+
+
+def load_library(path=LIB_PATH):
+    """Load libtrimul.so once. Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it first "
+                           "(python -m pair_rep_triangle_amd.build)")
+    lib = ctypes.CDLL(path)
+    vp, sz, i = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int
+    lib.tri_mul_create.argtypes = [ctypes.POINTER(Weights), i, i, i, ctypes.POINTER(vp)]
+    lib.tri_mul_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.tri_mul_workspace_layout.argtypes = [vp, i, i, ctypes.POINTER(Layout)]
+    lib.tri_mul_forward.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+    lib.tri_mul_forward_stage.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, sz, vp]
+    lib.tri_mul_destroy.argtypes = [vp]
+    lib.tri_mul_destroy.restype = None
+    lib.tri_mul_strerror.argtypes = [i]
+    lib.tri_mul_strerror.restype = ctypes.c_char_p
+    lib.tri_mul_last_hip_error.argtypes = []
+    lib.tri_mul_last_hip_error.restype = ctypes.c_char_p
+    for name in ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
+                 "tri_mul_forward", "tri_mul_forward_stage"):
+        getattr(lib, name).restype = i
+    _lib = lib
+    return lib
+
+
+def _check(rc, what):
+    if rc != 0:
+        detail = ""
+        if rc == -7:
+            detail = "- " + load_library().tri_mul_last_hip_error().decode()
+        raise TriMulError(rc, what, detail)
+
+
+def _host_f32(v):
+    if hasattr(v, "detach"):
+        v = v.detach().cpu().numpy()
+    return np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+
+
+class TriMul:
+    """One triangle multiplicative update module (one weight set, one dtype).
+
+    weights: mapping with the tri_mul_weights field names, fp32 host arrays in
+    nn.Linear orientation (missing gamma -> ones, missing beta / bias -> zeros).
+    """
+
+    def __init__(self, weights, c_z, c, dtype="bf16"):
+        self.lib = load_library()
+        self.c_z, self.c, self.dtype = int(c_z), int(c), dtype
+        if dtype not in DTYPES:
+            raise ValueError(f"dtype must be one of {sorted(DTYPES)}")
+        self._keep = {}
+        ws = Weights()
+        for name in WEIGHT_FIELDS:
+            v = weights.get(name) if hasattr(weights, "get") else None
+            if v is None:
+                continue
+            arr = _host_f32(v)
+            self._keep[name] = arr
+            setattr(ws, name, arr.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        h = ctypes.c_void_p()
+        _check(self.lib.tri_mul_create(ctypes.byref(ws), self.c_z, self.c, DTYPES[dtype],
+                                       ctypes.byref(h)), "tri_mul_create")
+        self._h = h
+        self._keep.clear()
+
+    # -- sizes -------------------------------------------------------------------------
+    def workspace_bytes(self, batch, n):
+        out = ctypes.c_size_t()
+        _check(self.lib.tri_mul_workspace_bytes(self._h, batch, n, ctypes.byref(out)),
+               "tri_mul_workspace_bytes")
+        return out.value
+
+    def layout(self, batch, n):
+        lay = Layout()
+        _check(self.lib.tri_mul_workspace_layout(self._h, batch, n, ctypes.byref(lay)),
+               "tri_mul_workspace_layout")
+        return lay
+
+    def torch_dtype(self):
+        import torch
+        return torch.bfloat16 if self.dtype == "bf16" else torch.float32
+
+    def new_workspace(self, batch, n, device="cuda"):
+        import torch
+        return torch.empty(self.workspace_bytes(batch, n), dtype=torch.uint8, device=device)
+
+    def workspace_views(self, ws, batch, n):
+        """(a, b, x) views [batch, c, n_pad, n_pad] into a workspace tensor."""
+        lay = self.layout(batch, n)
+        dt = self.torch_dtype()
+        numel = batch * self.c * lay.n_pad * lay.n_pad
+        views = []
+        for off in (lay.a_offset, lay.b_offset, lay.x_offset):
+            views.append(ws[off:off + numel * lay.elem_bytes].view(dt)
+                         .view(batch, self.c, lay.n_pad, lay.n_pad))
+        return tuple(views)
+
+    # -- calls -------------------------------------------------------------------------
+    def _args(self, z, mask, out, workspace, direction, stream):
+        import torch
+        if z.dim() != 4 or z.shape[1] != z.shape[2] or z.shape[3] != self.c_z:
+            raise ValueError(f"z must be [B, N, N, {self.c_z}], got {tuple(z.shape)}")
+        if z.dtype != self.torch_dtype() or not z.is_cuda or not z.is_contiguous():
+            raise ValueError("z must be a contiguous CUDA tensor of the handle's dtype")
+        batch, n = int(z.shape[0]), int(z.shape[1])
+        if mask is not None:
+            if tuple(mask.shape) != (batch, n, n) or mask.dtype != z.dtype or not mask.is_contiguous():
+                raise ValueError("mask must be a contiguous [B, N, N] tensor of z's dtype")
+        if out is None:
+            out = torch.empty_like(z)
+        elif out.shape != z.shape or out.dtype != z.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor shaped like z")
+        if workspace is None:
+            workspace = self.new_workspace(batch, n, device=z.device)
+        if direction not in DIRECTIONS:
+            raise ValueError("direction must be 'outgoing' or 'incoming'")
+        if stream is None:
+            stream = torch.cuda.current_stream(z.device).cuda_stream
+        return (z.data_ptr(), None if mask is None else mask.data_ptr(), out.data_ptr(),
+                batch, n, DIRECTIONS[direction], workspace.data_ptr(),
+                workspace.numel() * workspace.element_size(), stream), out, workspace
+
+    def forward(self, z, mask=None, out=None, direction="outgoing", workspace=None, stream=None):
+        args, out, _ = self._args(z, mask, out, workspace, direction, stream)
+        _check(self.lib.tri_mul_forward(self._h, *args), "tri_mul_forward")
+        return out
+
+    __call__ = forward
+
+    def stage(self, stage, z, mask=None, out=None, direction="outgoing", workspace=None,
+              stream=None):
+        args, out, workspace = self._args(z, mask, out, workspace, direction, stream)
+        _check(self.lib.tri_mul_forward_stage(self._h, int(stage), *args), "tri_mul_forward_stage")
+        return out, workspace
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self.lib.tri_mul_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -1,0 +1,79 @@
+"""Helpers shared by the GPU tests: move a seeded case to the device, run the
+HIP path through the C ABI, and compare with the fp64 oracle."""
+
+import sys
+
+import numpy as np
+import torch
+
+from oracle import tri_mul_ref, tri_mul_ref_pairs, tri_mul_intermediates
+from pair_rep_triangle_amd.trimul import TriMul
+
+TOL = {"fp32": 1e-4, "bf16": 2e-2}  # max |gpu - ref| / max |ref|
+
+
+def note(msg):
+    """Print (and flush) what the next GPU step is, so a failing run names its case."""
+    print(f"[gpu-case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def torch_dtype(dtype):
+    return torch.bfloat16 if dtype == "bf16" else torch.float32
+
+
+def to_device(d, dtype):
+    """z, mask as device tensors in the storage dtype, plus the exact values the
+    device holds (as float64 NumPy) for the oracle."""
+    dt = torch_dtype(dtype)
+    z = torch.from_numpy(d["z"]).to(dt)
+    m = torch.from_numpy(d["mask"]).to(dt)
+    z_host = z.to(torch.float64).numpy()
+    m_host = m.to(torch.float64).numpy()
+    return z.cuda(), m.cuda(), z_host, m_host
+
+
+def rel_err(got, want):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    scale = np.abs(want).max()
+    return float(np.abs(got - want).max() / (scale if scale > 0 else 1.0))
+
+
+def run_full(d, dtype, direction, use_mask=True, module=None):
+    z, m, z_host, m_host = to_device(d, dtype)
+    c_z, c = d["z"].shape[-1], d["weights"]["w_a_gate"].shape[0]
+    mod = module or TriMul(d["weights"], c_z, c, dtype)
+    out = mod.forward(z, m if use_mask else None, direction=direction)
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy()
+    return got, z_host, (m_host if use_mask else None), mod
+
+
+def check_full(d, dtype, direction, use_mask=True, tol=None):
+    got, z_host, m_host, _ = run_full(d, dtype, direction, use_mask)
+    want = tri_mul_ref(z_host, m_host, d["weights"], direction)
+    err = rel_err(got, want)
+    assert np.isfinite(got).all(), "non-finite output"
+    assert err <= (tol or TOL[dtype]), f"rel err {err:.3e} > {tol or TOL[dtype]:.1e}"
+    return err, got, want
+
+
+def sample_pairs(rng, batch, n, count, valid=None):
+    v = n if valid is None else valid
+    bi = rng.integers(0, batch, count)
+    ii = rng.integers(0, n, count)
+    jj = rng.integers(0, n, count)
+    # always include the corners and, when padded, the first padded row / column
+    extra = [(0, 0, 0), (batch - 1, n - 1, n - 1), (0, 0, n - 1), (0, n - 1, 0),
+             (0, v - 1, v - 1)]
+    if v < n:
+        extra += [(0, v, 0), (0, 0, v), (0, v - 1, v)]
+    bi = np.concatenate([bi, [e[0] for e in extra]])
+    ii = np.concatenate([ii, [e[1] for e in extra]])
+    jj = np.concatenate([jj, [e[2] for e in extra]])
+    return bi, ii, jj
+
+
+__all__ = ["TOL", "note", "to_device", "rel_err", "run_full", "check_full", "sample_pairs",
+           "tri_mul_ref", "tri_mul_ref_pairs", "tri_mul_intermediates", "TriMul", "torch_dtype"]

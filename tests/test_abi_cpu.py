@@ -1,0 +1,88 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+symbol include/tri_mul.h declares, and rejects bad create arguments before any
+HIP call."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from pair_rep_triangle_amd import trimul as tm
+from pair_rep_triangle_amd.inputs import make_weights
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    with open(os.path.join(ROOT, "include", "tri_mul.h")) as f:
+        src = f.read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(tri_mul_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return tm.load_library()
+
+
+def test_header_declares_the_entry_points():
+    assert _declared_functions() == sorted(tm.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in _declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_strerror_covers_every_code(lib):
+    for code in tm.ERRORS:
+        msg = lib.tri_mul_strerror(code).decode()
+        assert msg and msg != "unknown error code"
+    assert lib.tri_mul_strerror(12345).decode() == "unknown error code"
+
+
+def _weights_struct(w):
+    keep = {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in w.items()}
+    s = tm.Weights()
+    for k, v in keep.items():
+        setattr(s, k, v.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return s, keep
+
+
+@pytest.mark.parametrize("c_z,c,dtype,code", [
+    (24, 16, tm.TRI_MUL_BF16, -2), (16, 40, tm.TRI_MUL_BF16, -2), (2048, 16, tm.TRI_MUL_FP32, -2),
+    (16, 16, 7, -2), (0, 16, tm.TRI_MUL_FP32, -1), (16, -16, tm.TRI_MUL_FP32, -1),
+])
+def test_create_rejects_bad_shapes_before_touching_the_device(lib, c_z, c, dtype, code):
+    w = make_weights(np.random.default_rng(0), max(c_z, 1), max(c, 1))
+    s, keep = _weights_struct(w)
+    h = ctypes.c_void_p(1)
+    assert lib.tri_mul_create(ctypes.byref(s), c_z, c, dtype, ctypes.byref(h)) == code
+    assert h.value is None
+
+
+def test_create_requires_weight_matrices(lib):
+    w = make_weights(np.random.default_rng(0), 16, 16)
+    del w["w_gate"]
+    s, keep = _weights_struct(w)
+    h = ctypes.c_void_p()
+    assert lib.tri_mul_create(ctypes.byref(s), 16, 16, tm.TRI_MUL_BF16, ctypes.byref(h)) == -1
+    assert lib.tri_mul_create(None, 16, 16, tm.TRI_MUL_BF16, ctypes.byref(h)) == -1
+    assert lib.tri_mul_create(ctypes.byref(s), 16, 16, tm.TRI_MUL_BF16, None) == -1
+
+
+def test_null_handle_is_rejected(lib):
+    n = ctypes.c_size_t()
+    assert lib.tri_mul_workspace_bytes(None, 1, 8, ctypes.byref(n)) == -1
+    assert lib.tri_mul_workspace_layout(None, 1, 8, None) == -1
+    assert lib.tri_mul_forward(None, 16, 16, 32, 1, 8, 0, 48, 1 << 20, None) == -1
+    assert lib.tri_mul_forward_stage(None, 1, 16, 16, 32, 1, 8, 0, 48, 1 << 20, None) == -1
+    lib.tri_mul_destroy(None)  # no-op
+
+
+def test_binding_raises_with_a_named_error():
+    with pytest.raises(tm.TriMulError) as ei:
+        tm.TriMul(make_weights(np.random.default_rng(0), 16, 16), 20, 16, "bf16")
+    assert ei.value.name == "UNSUPPORTED"

@@ -1,0 +1,236 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerance (max |gpu - ref| / max |ref|): 1e-4 for fp32 storage, 2e-2 for bf16
+storage with fp32 accumulation. Full-output comparisons at sizes the oracle
+finishes in seconds; sampled pairs at the large workloads, run in the same
+launch configuration the benchmark times."""
+
+import numpy as np
+import pytest
+import torch
+
+from pair_rep_triangle_amd.inputs import WORKLOADS, make_random, make_workload
+from tests.gpu_util import (TOL, TriMul, check_full, note, rel_err, run_full, sample_pairs,
+                            to_device, tri_mul_intermediates, tri_mul_ref, tri_mul_ref_pairs)
+
+pytestmark = pytest.mark.gpu
+DIRS = ("outgoing", "incoming")
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a visible GPU"
+    yield
+    torch.cuda.synchronize()
+
+
+# --- the five workloads ---------------------------------------------------------------------
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("name", ["n32_cz16_c16_fp32", "n256_cz128_c128_bf16",
+                                  "n512_cz128_c128_bf16_masked"])
+def test_workload_full_output(name, direction):
+    note(f"workload {name} {direction} full")
+    d = make_workload(name, seed=0)
+    err, _, _ = check_full(d, WORKLOADS[name]["dtype"], direction)
+    print(f"{name} {direction}: rel err {err:.3e}")
+
+
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("name", ["n768_cz384_c128_b2_bf16", "n2048_cz128_c128_bf16_chains"])
+def test_workload_sampled(name, direction):
+    note(f"workload {name} {direction} sampled")
+    d = make_workload(name, seed=0)
+    spec = WORKLOADS[name]
+    dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+    z = torch.from_numpy(d["z"]).to(dt)
+    m = torch.from_numpy(d["mask"]).to(dt)
+    mod = TriMul(d["weights"], spec["c_z"], spec["c"], spec["dtype"])
+    out = mod.forward(z.cuda(), m.cuda(), direction=direction)
+    rng = np.random.default_rng(7)
+    bi, ii, jj = sample_pairs(rng, spec["batch"], spec["n"], 48, d["meta"].get("valid_length"))
+    idx = [torch.as_tensor(v, device=out.device) for v in (bi, ii, jj)]
+    got = out[idx[0], idx[1], idx[2]].double().cpu().numpy()
+    finite = bool(torch.isfinite(out).all().item())
+    torch.cuda.synchronize()
+    del out
+    want = tri_mul_ref_pairs(z.double().numpy(), m.double().numpy(), d["weights"], direction,
+                             bi, ii, jj)
+    err = rel_err(got, want)
+    print(f"{name} {direction}: sampled rel err {err:.3e}")
+    assert finite
+    assert err <= TOL[spec["dtype"]]
+
+
+def test_headline_padding_is_zero():
+    name = "n512_cz128_c128_bf16_masked"
+    d = make_workload(name, seed=0)
+    L = d["meta"]["valid_length"]
+    for direction in DIRS:
+        note(f"headline padding {direction}")
+        got, _, _, _ = run_full(d, "bf16", direction)
+        assert np.all(got[:, L:, :, :] == 0) and np.all(got[:, :, L:, :] == 0)
+
+
+# --- ragged sizes, widths, masks, batches -----------------------------------------------------
+
+RAGGED = [
+    # batch, n, c_z, c, mask
+    (1, 1, 16, 16, "ones"), (2, 7, 16, 32, "random_pairs"), (1, 33, 32, 16, "block"),
+    (2, 100, 48, 32, "random_residues"), (1, 130, 64, 48, "random_pairs"),
+    (1, 129, 128, 128, "block"), (3, 64, 32, 64, "ones"),
+]
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("batch,n,c_z,c,mask", RAGGED)
+def test_ragged_full_output(batch, n, c_z, c, mask, direction, dtype):
+    note(f"ragged B={batch} n={n} cz={c_z} c={c} {mask} {direction} {dtype}")
+    d = make_random(batch, n, c_z, c, seed=n + c_z, mask=mask, random_affine=True)
+    check_full(d, dtype, direction)
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_null_mask_means_all_ones(dtype):
+    d = make_random(1, 40, 32, 32, seed=5, mask="ones")
+    note(f"null mask {dtype}")
+    got_null, z_host, _, mod = run_full(d, dtype, "incoming", use_mask=False)
+    got_ones, _, _, _ = run_full(d, dtype, "incoming", use_mask=True, module=mod)
+    assert np.array_equal(got_null, got_ones)
+
+
+@pytest.mark.parametrize("shift", [3.0, -5.0])
+def test_nonzero_mean_input_folded_layernorm(shift):
+    """The kernels apply LayerNorm after the projection (folded weights); inputs
+    with a large common offset must stay within tolerance."""
+    d = make_random(1, 48, 64, 32, seed=9, mask="random_pairs", z_shift=shift)
+    note(f"nonzero mean {shift}")
+    for dtype in ("fp32", "bf16"):
+        check_full(d, dtype, "outgoing")
+
+
+# --- intermediates through the documented workspace layout ----------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("direction", DIRS)
+def test_intermediates_in_workspace(direction, dtype):
+    batch, n, c_z, c = 2, 37, 32, 48
+    d = make_random(batch, n, c_z, c, seed=3, mask="random_pairs")
+    z, m, z_host, m_host = to_device(d, dtype)
+    note(f"intermediates {direction} {dtype}")
+    mod = TriMul(d["weights"], c_z, c, dtype)
+    ws = mod.new_workspace(batch, n)
+    out = mod.forward(z, m, direction=direction, workspace=ws)
+    torch.cuda.synchronize()
+    A, Bm, X = (v.to(torch.float64).cpu().numpy() for v in mod.workspace_views(ws, batch, n))
+    it = tri_mul_intermediates(z_host, m_host, d["weights"], direction)
+    a_ref = np.moveaxis(it["a"], -1, 1)  # [B, c, N, N]
+    b_ref = np.moveaxis(it["b"], -1, 1)
+    if direction == "incoming":
+        a_ref, b_ref = np.swapaxes(a_ref, -1, -2), np.swapaxes(b_ref, -1, -2)
+    tol = TOL[dtype]
+    assert rel_err(A[:, :, :n, :n], a_ref) <= tol
+    assert rel_err(Bm[:, :, :n, :n], b_ref) <= tol
+    assert np.all(A[:, :, n:, :] == 0) and np.all(A[:, :, :, n:] == 0)
+    assert np.all(Bm[:, :, n:, :] == 0) and np.all(Bm[:, :, :, n:] == 0)
+    assert rel_err(X[:, :, :n, :n], np.moveaxis(it["x"], -1, 1)) <= tol
+    assert rel_err(out.to(torch.float64).cpu().numpy(), it["out"]) <= tol
+
+
+def test_stages_in_order_equal_forward():
+    d = make_random(1, 70, 32, 32, seed=4, mask="block")
+    z, m, _, _ = to_device(d, "bf16")
+    note("stages vs forward")
+    mod = TriMul(d["weights"], 32, 32, "bf16")
+    ws = mod.new_workspace(1, 70)
+    full = mod.forward(z, m, direction="incoming", workspace=ws).clone()
+    out = torch.empty_like(z)
+    for s in (1, 2, 3):
+        mod.stage(s, z, m, out=out, direction="incoming", workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(full, out)
+
+
+# --- identities on the GPU ----------------------------------------------------------------------
+
+def _swap_ab(w):
+    s = dict(w)
+    for part in ("gate", "proj"):
+        s[f"w_a_{part}"], s[f"w_b_{part}"] = w[f"w_b_{part}"], w[f"w_a_{part}"]
+        s[f"b_a_{part}"], s[f"b_b_{part}"] = w[f"b_b_{part}"], w[f"b_a_{part}"]
+    return s
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_transpose_identity_two_handles(dtype):
+    """incoming(z, m; W_a, W_b) == outgoing(z^T, m^T; W_b, W_a)^T."""
+    d = make_random(1, 90, 32, 32, seed=6, mask="random_pairs")
+    z, m, _, _ = to_device(d, dtype)
+    note(f"transpose identity {dtype}")
+    inc = TriMul(d["weights"], 32, 32, dtype).forward(z, m, direction="incoming")
+    zt = z.transpose(1, 2).contiguous()
+    mt = m.transpose(1, 2).contiguous()
+    out_t = TriMul(_swap_ab(d["weights"]), 32, 32, dtype).forward(zt, mt, direction="outgoing")
+    torch.cuda.synchronize()
+    err = rel_err(inc.double().cpu().numpy(), out_t.transpose(1, 2).double().cpu().numpy())
+    assert err <= TOL[dtype] / 4
+
+
+def test_crop_invariance_on_gpu():
+    n, L = 150, 97
+    d = make_random(1, n, 32, 32, seed=8, mask="block", valid=[L])
+    z, m, _, _ = to_device(d, "bf16")
+    note("crop invariance")
+    mod = TriMul(d["weights"], 32, 32, "bf16")
+    for direction in DIRS:
+        full = mod.forward(z, m, direction=direction)
+        crop = mod.forward(z[:, :L, :L].contiguous(), None, direction=direction)
+        torch.cuda.synchronize()
+        err = rel_err(full[:, :L, :L].double().cpu().numpy(), crop.double().cpu().numpy())
+        assert err <= 1e-2
+        assert torch.all(full[:, L:] == 0) and torch.all(full[:, :, L:] == 0)
+
+
+def test_deterministic_and_stream_safe():
+    d = make_workload("n256_cz128_c128_bf16", seed=0)
+    z, m, _, _ = to_device(d, "bf16")
+    note("determinism / side stream")
+    mod = TriMul(d["weights"], 128, 128, "bf16")
+    first = mod.forward(z, m, direction="outgoing")
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        second = mod.forward(z, m, direction="outgoing")
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert torch.equal(first, second)
+
+
+# --- argument validation on a real handle ------------------------------------------------------
+
+def test_forward_rejects_bad_calls():
+    from pair_rep_triangle_amd.trimul import TriMulError
+    d = make_random(1, 24, 16, 16, seed=1)
+    z, m, _, _ = to_device(d, "bf16")
+    note("validation")
+    mod = TriMul(d["weights"], 16, 16, "bf16")
+    lib, h = mod.lib, mod._h
+    ws = mod.new_workspace(1, 24)
+    wsb = ws.numel()
+    out = torch.empty_like(z)
+    st = torch.cuda.current_stream().cuda_stream
+    zp, mp, op, wp = z.data_ptr(), m.data_ptr(), out.data_ptr(), ws.data_ptr()
+    assert lib.tri_mul_forward(h, zp, mp, op, 1, 24, 0, wp, wsb, st) == 0
+    assert lib.tri_mul_forward(h, zp, mp, op, 1, 24, 2, wp, wsb, st) == -1   # direction
+    assert lib.tri_mul_forward(h, zp, mp, op, 0, 24, 0, wp, wsb, st) == -1   # batch
+    assert lib.tri_mul_forward(h, zp, mp, op, 1, 0, 0, wp, wsb, st) == -1    # n
+    assert lib.tri_mul_forward(h, None, mp, op, 1, 24, 0, wp, wsb, st) == -1
+    assert lib.tri_mul_forward(h, zp + 2, mp, op, 1, 24, 0, wp, wsb, st) == -4
+    assert lib.tri_mul_forward(h, zp, mp, op, 1, 24, 0, wp, wsb - 16, st) == -6
+    assert lib.tri_mul_forward(h, zp, mp, zp, 1, 24, 0, wp, wsb, st) == -5   # out == z
+    assert lib.tri_mul_forward(h, zp, mp, op, 1, 24, 0, op, wsb, st) == -5   # ws over out
+    assert lib.tri_mul_forward_stage(h, 4, zp, mp, op, 1, 24, 0, wp, wsb, st) == -1
+    with pytest.raises(TriMulError):
+        mod.forward(z, m, direction="incoming", workspace=ws[:16])
+    torch.cuda.synchronize()
