@@ -36,6 +36,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time whole steps only (no events between the kernels)")
+    p.add_argument("--copy-calibration-mb", type=int, default=0,
+                   help="also run a plain device-to-device copy of this many MiB three times "
+                        "(reference kernel for scaling HBM byte counters)")
     return p.parse_args()
 
 
@@ -98,6 +101,15 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
+
+    if args.copy_calibration_mb:
+        src = torch.empty(args.copy_calibration_mb << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        src.fill_(1)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     use_ev = not args.no_kernel_events
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]

@@ -39,7 +39,7 @@ extern "C" {
 
 #define TRI_MUL_OK 0
 #define TRI_MUL_ERR_INVALID_ARG -1        /* NULL pointer, size out of range, bad enum   */
-#define TRI_MUL_ERR_UNSUPPORTED -2        /* c_z or c not a multiple of 16 / too large    */
+#define TRI_MUL_ERR_UNSUPPORTED -2        /* width not a multiple of 16 / too large, dtype */
 #define TRI_MUL_ERR_UNSUPPORTED_DEVICE -3 /* current device is not gfx950 / wrong device */
 #define TRI_MUL_ERR_ALIGNMENT -4          /* a device pointer not 16-byte aligned         */
 #define TRI_MUL_ERR_ALIAS -5              /* out or workspace overlaps another buffer     */
@@ -48,7 +48,9 @@ extern "C" {
 #define TRI_MUL_ERR_OUT_OF_MEMORY -8      /* tri_mul_create could not allocate weights    */
 
 #define TRI_MUL_MAX_N 32768               /* residues per side                            */
-#define TRI_MUL_MAX_WIDTH 1024            /* largest c_z and c                            */
+#define TRI_MUL_MAX_WIDTH 512             /* largest c_z and c, bf16                      */
+#define TRI_MUL_MAX_WIDTH_FP32_CZ 256     /* largest c_z, fp32                            */
+#define TRI_MUL_MAX_WIDTH_FP32_C 128      /* largest c, fp32                              */
 #define TRI_MUL_LN_EPS 1e-5f              /* epsilon of both LayerNorms                   */
 
 typedef enum { TRI_MUL_FP32 = 0, TRI_MUL_BF16 = 1 } tri_mul_dtype;
@@ -83,8 +85,8 @@ typedef struct tri_mul_layout {
   int elem_bytes;                      /* 2 (bf16) or 4 (fp32)          */
 } tri_mul_layout;
 
-/* Build a handle: checks c_z, c (multiples of 16, at most TRI_MUL_MAX_WIDTH)
- * and dtype, checks that the current device is gfx950, folds both LayerNorm
+/* Build a handle: checks c_z, c (multiples of 16; at most TRI_MUL_MAX_WIDTH for
+ * bf16, TRI_MUL_MAX_WIDTH_FP32_CZ / _C for fp32) and dtype, checks that the current device is gfx950, folds both LayerNorm
  * affines into the projection weights (in double precision), converts them to
  * `dtype` and copies them to the current device. The only call that allocates.
  * On error *out is set to NULL. */

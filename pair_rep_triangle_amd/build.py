@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtrimul.so")
-SOURCES = ("kernels.hip", "tri_mul.cpp")
+SOURCES = ("k1_input_gate.hip", "k2_contract.hip", "k3_output_gate.hip", "tri_mul.cpp")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -41,11 +41,12 @@ def build(verbose=True):
     """Compile every source and link libtrimul.so (always recompiles)."""
     objdir = os.path.join(PKG, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
-        obj = os.path.join(objdir, src + ".o")
-        _run([HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj])
-        objs.append(obj)
+    from concurrent.futures import ThreadPoolExecutor
+    objs = [os.path.join(objdir, src + ".o") for src in SOURCES]
+    jobs = [[HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+            for src, obj in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as ex:
+        list(ex.map(_run, jobs))
     tmp = LIB + ".tmp"
     _run([HIPCC, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs])
     os.replace(tmp, LIB)

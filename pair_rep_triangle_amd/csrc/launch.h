@@ -3,12 +3,14 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include <atomic>
+
 #define TRI_MUL_LN_EPS_F 1e-5f
 
 namespace trimul {
 
-// Everything one stage launch needs. Pointers are device memory; the element
-// type (bf16 or fp32) is chosen by launch_stage's `bf16_storage`.
+// Everything one stage launch needs. Pointers are device memory; the element type
+// (bf16 or fp32) is chosen by the launcher's `bf16_storage`.
 struct StageArgs {
   const void* z;     // [batch][n][n][cz]
   const void* mask;  // [batch][n][n] or nullptr (all ones)
@@ -16,24 +18,68 @@ struct StageArgs {
   void* a;           // [batch][c][np][np]
   void* b;           // [batch][c][np][np]
   void* x;           // [batch][c][np][np]
-  const void* w1;    // [4][c][czp]  a_gate, a_proj, b_gate, b_proj with gamma_in folded
-  const float* s1;   // [4][c]       row sums of the stored w1
-  const float* t1;   // [4][c]       W beta_in + bias
-  const void* wo;    // [cz][cp]     output projection with gamma_out folded
-  const float* so;   // [cz]
-  const float* to;   // [cz]
-  const void* wg;    // [cz][czp]    output gate with gamma_in folded
-  const float* sg;   // [cz]
-  const float* tg;   // [cz]
-  int batch, n, np, cz, czp, c, cp, incoming;
+  const void* w1;    // [4][c][czp]  a_gate, a_proj, b_gate, b_proj: W diag(gamma_in);
+                     //              gate rows times -log2(e)
+  const float* t1;   // [4][c]       W beta_in + bias (gate rows times -log2(e))
+  const void* wo;    // [cz][cp]     W_o diag(gamma_out)
+  const float* to;   // [cz]         W_o beta_out + b_o
+  const void* wg;    // [cz][czp]    W_g diag(gamma_in) times -log2(e)
+  const float* tg;   // [cz]         (W_g beta_in + b_g) times -log2(e)
+  const void* one;   // one element of value 1 in the storage type (stands in for no mask)
+  int batch, n, np, cz, czp, c, cp, incoming, num_cus;
 };
 
-// Padded widths: the k extent of every MFMA chunk group (32 for bf16, 16 for fp32).
+// k extent of one 16x16 MFMA chunk group: 32 (bf16) or 16 (fp32).
 inline int k_group(bool bf16_storage) { return bf16_storage ? 32 : 16; }
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
-constexpr int N_PAD = 128;  // a, b, x side padding (the contraction tile)
+constexpr int N_PAD = 128;  // side padding of a, b, x (the contraction tile)
 
-hipError_t launch_stage(int stage, bool bf16_storage, const StageArgs& a, hipStream_t st);
-size_t stage_lds_bytes(int stage, bool bf16_storage, int czp, int cp);
+// The projection kernels keep their weights in registers, sized at compile time by the
+// number of chunk groups along k. The output kernel is compiled for these (KX, KZ) pairs
+// (KX for c, KZ for c_z); the input kernel for every KZ that appears. A handle pads c and
+// c_z with zeros up to the cheapest pair that covers both.
+#define TRIMUL_K3_VARIANTS(X) \
+  X(1, 1) X(2, 2) X(4, 4) X(8, 8) X(12, 12) X(16, 16) X(4, 12) X(4, 16) X(8, 12) X(8, 16) \
+  X(12, 16) X(2, 4) X(4, 8) X(4, 2) X(8, 4)
+inline bool padded_ksteps(int c, int cz, bool bf16_storage, int* kx, int* kz) {
+  const int kg = k_group(bf16_storage);
+  const int kx0 = (c + kg - 1) / kg, kz0 = (cz + kg - 1) / kg;
+  int best = -1;
+#define TRIMUL_PICK(X_, Z_) \
+  if (X_ >= kx0 && Z_ >= kz0 && (best < 0 || X_ + Z_ < best)) { best = X_ + Z_; *kx = X_; *kz = Z_; }
+  TRIMUL_K3_VARIANTS(TRIMUL_PICK)
+#undef TRIMUL_PICK
+  return best > 0;
+}
+
+// Raises a kernel's dynamic-LDS limit when a launch needs more than was granted so far.
+inline hipError_t ensure_dynamic_lds(const void* fn, std::atomic<int>& granted, size_t need) {
+  if ((int)need <= granted.load(std::memory_order_relaxed)) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)need);
+  if (e == hipSuccess) {
+    int cur = granted.load();
+    while ((int)need > cur && !granted.compare_exchange_weak(cur, (int)need)) {
+    }
+  }
+  return e;
+}
+
+// Resident workgroups per CU for a persistent kernel (queried once per instantiation and
+// LDS size; at least 1).
+inline int resident_blocks(const void* fn, int threads, size_t lds, std::atomic<int>& cache,
+                           std::atomic<size_t>& cache_lds) {
+  int v = cache.load(std::memory_order_relaxed);
+  if (v > 0 && cache_lds.load(std::memory_order_relaxed) == lds) return v;
+  int nb = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, threads, lds) != hipSuccess || nb < 1)
+    nb = 1;
+  cache_lds.store(lds);
+  cache.store(nb);
+  return nb;
+}
+
+hipError_t launch_k1(bool bf16_storage, const StageArgs& a, hipStream_t st);
+hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st);
+hipError_t launch_k3(bool bf16_storage, const StageArgs& a, hipStream_t st);
 
 }  // namespace trimul

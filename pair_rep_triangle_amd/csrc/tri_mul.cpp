@@ -14,7 +14,7 @@
 #include "launch.h"
 
 struct tri_mul_handle {
-  int c_z, c, czp, cp, dtype, device;
+  int c_z, c, czp, cp, dtype, device, num_cus;
   bool bf16;
   void* block;  // the one device allocation holding every packed weight
   trimul::StageArgs w;  // weight pointers into `block` (activation fields unused)
@@ -36,41 +36,32 @@ uint16_t f32_to_bf16_rne(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
 }
-float bf16_to_f32(uint16_t h) {
-  uint32_t u = (uint32_t)h << 16;
-  float f;
-  memcpy(&f, &u, 4);
-  return f;
-}
 
 size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-// Folds y = W (gamma (.) xhat + beta) + bias into the stored matrix W' = W diag(gamma)
-// (rounded to the storage type, zero-padded from `cols` to `colsp`), s = row sums of
-// the stored W', t = W beta + bias. All sums in double.
+// Folds y = scale * (W (gamma (.) xhat + beta) + bias) into the stored matrix
+// W' = scale * W diag(gamma) (rounded to the storage type, zero-padded from `cols` to
+// `colsp`) and the accumulator start t = scale * (W beta + bias). Sums in double.
 void fold(const float* W, const float* gamma, const float* beta, const float* bias, int rows,
-          int cols, int colsp, bool bf16, unsigned char* wdst, float* s, float* t) {
+          int cols, int colsp, bool bf16, double scale, unsigned char* wdst, float* t) {
   for (int r = 0; r < rows; ++r) {
-    double srow = 0.0, trow = bias ? (double)bias[r] : 0.0;
+    double trow = bias ? (double)bias[r] : 0.0;
     for (int k = 0; k < colsp; ++k) {
       double v = 0.0;
       if (k < cols) {
         const double wk = W[(size_t)r * cols + k];
-        v = wk * (gamma ? (double)gamma[k] : 1.0);
+        v = scale * wk * (gamma ? (double)gamma[k] : 1.0);
         if (beta) trow += wk * (double)beta[k];
       }
       const float vf = (float)v;
       if (bf16) {
         const uint16_t h = f32_to_bf16_rne(vf);
         memcpy(wdst + ((size_t)r * colsp + k) * 2, &h, 2);
-        srow += bf16_to_f32(h);
       } else {
         memcpy(wdst + ((size_t)r * colsp + k) * 4, &vf, 4);
-        srow += vf;
       }
     }
-    s[r] = (float)srow;
-    t[r] = (float)trow;
+    t[r] = (float)(scale * trow);
   }
 }
 
@@ -97,7 +88,7 @@ Layout layout_of(const tri_mul_handle* h, int batch, int n) {
   return L;
 }
 
-int check_device(int* dev_out) {
+int check_device(int* dev_out, int* cus_out) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
@@ -106,6 +97,7 @@ int check_device(int* dev_out) {
   if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
   if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
   *dev_out = dev;
+  *cus_out = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
   return TRI_MUL_OK;
 }
 
@@ -151,11 +143,19 @@ int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out
   a.n = n;
   a.np = L.np;
   a.incoming = direction == TRI_MUL_INCOMING;
+  a.num_cus = h->num_cus;
   hipStream_t st = (hipStream_t)stream;
-  for (int s = 1; s <= 3; ++s) {
-    if (stage != 0 && stage != s) continue;
-    e = trimul::launch_stage(s, h->bf16, a, st);
-    if (e != hipSuccess) return hip_fail(e, s == 1 ? "launch k1" : s == 2 ? "launch k2" : "launch k3");
+  if (stage == 0 || stage == 1) {
+    e = trimul::launch_k1(h->bf16, a, st);
+    if (e != hipSuccess) return hip_fail(e, "launch k1_input_gate");
+  }
+  if (stage == 0 || stage == 2) {
+    e = trimul::launch_k2(h->bf16, a, st);
+    if (e != hipSuccess) return hip_fail(e, "launch k2_contract");
+  }
+  if (stage == 0 || stage == 3) {
+    e = trimul::launch_k3(h->bf16, a, st);
+    if (e != hipSuccess) return hip_fail(e, "launch k3_output_gate");
   }
   return TRI_MUL_OK;
 }
@@ -172,40 +172,51 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
     return TRI_MUL_ERR_INVALID_ARG;
   if (c_z < 1 || c < 1) return TRI_MUL_ERR_INVALID_ARG;
   if (dtype != TRI_MUL_FP32 && dtype != TRI_MUL_BF16) return TRI_MUL_ERR_UNSUPPORTED;
-  if (c_z % 16 || c % 16 || c_z > TRI_MUL_MAX_WIDTH || c > TRI_MUL_MAX_WIDTH)
+  const bool bf16 = dtype == TRI_MUL_BF16;
+  if (c_z % 16 || c % 16) return TRI_MUL_ERR_UNSUPPORTED;
+  if (bf16 ? (c_z > TRI_MUL_MAX_WIDTH || c > TRI_MUL_MAX_WIDTH)
+           : (c_z > TRI_MUL_MAX_WIDTH_FP32_CZ || c > TRI_MUL_MAX_WIDTH_FP32_C))
     return TRI_MUL_ERR_UNSUPPORTED;
-  int dev = -1;
-  int rc = check_device(&dev);
+  int dev = -1, cus = 0;
+  int rc = check_device(&dev, &cus);
   if (rc != TRI_MUL_OK) return rc;
 
-  const bool bf16 = dtype == TRI_MUL_BF16;
   const int kg = trimul::k_group(bf16);
-  const int czp = trimul::round_up(c_z, kg), cp = trimul::round_up(c, kg);
+  int kx = 0, kz = 0;
+  if (!trimul::padded_ksteps(c, c_z, bf16, &kx, &kz)) return TRI_MUL_ERR_UNSUPPORTED;
+  const int czp = kg * kz, cp = kg * kx;
   const int esz = bf16 ? 2 : 4;
-  // block: w1 | wo | wg | s1 t1 | so to | sg tg
+  const double ng = -1.4426950408889634;  // -log2(e): gate rows feed exp2 directly
+  // block: w1 | wo | wg | t1 | to | tg
   const size_t w1b = align256((size_t)4 * c * czp * esz);
   const size_t wob = align256((size_t)c_z * cp * esz);
   const size_t wgb = align256((size_t)c_z * czp * esz);
-  const size_t st1 = align256((size_t)8 * c * sizeof(float));
-  const size_t sto = align256((size_t)2 * c_z * sizeof(float));
-  const size_t total = w1b + wob + wgb + st1 + 2 * sto;
+  const size_t t1b = align256((size_t)4 * c * sizeof(float));
+  const size_t tob = align256((size_t)c_z * sizeof(float));
+  const size_t oneb = 256;
+  const size_t total = w1b + wob + wgb + t1b + 2 * tob + oneb;
   std::vector<unsigned char> host(total, 0);
   unsigned char* hw1 = host.data();
   unsigned char* hwo = hw1 + w1b;
   unsigned char* hwg = hwo + wob;
-  float* hs1 = (float*)(hwg + wgb);
-  float* ht1 = hs1 + 4 * c;
-  float* hso = (float*)((unsigned char*)hs1 + st1);
-  float* hto = hso + c_z;
-  float* hsg = (float*)((unsigned char*)hso + sto);
-  float* htg = hsg + c_z;
+  float* ht1 = (float*)(hwg + wgb);
+  float* hto = (float*)((unsigned char*)ht1 + t1b);
+  float* htg = (float*)((unsigned char*)hto + tob);
+  unsigned char* hone = (unsigned char*)htg + tob;
+  if (bf16) {
+    const uint16_t one = 0x3f80;  // 1.0 in bf16
+    memcpy(hone, &one, 2);
+  } else {
+    const float one = 1.0f;
+    memcpy(hone, &one, 4);
+  }
   const float* mats[4] = {w->w_a_gate, w->w_a_proj, w->w_b_gate, w->w_b_proj};
   const float* biases[4] = {w->b_a_gate, w->b_a_proj, w->b_b_gate, w->b_b_proj};
   for (int q = 0; q < 4; ++q)
     fold(mats[q], w->ln_in_gamma, w->ln_in_beta, biases[q], c, c_z, czp, bf16,
-         hw1 + (size_t)q * c * czp * esz, hs1 + q * c, ht1 + q * c);
-  fold(w->w_out, w->ln_out_gamma, w->ln_out_beta, w->b_out, c_z, c, cp, bf16, hwo, hso, hto);
-  fold(w->w_gate, w->ln_in_gamma, w->ln_in_beta, w->b_gate, c_z, c_z, czp, bf16, hwg, hsg, htg);
+         (q % 2 == 0) ? ng : 1.0, hw1 + (size_t)q * c * czp * esz, ht1 + q * c);
+  fold(w->w_out, w->ln_out_gamma, w->ln_out_beta, w->b_out, c_z, c, cp, bf16, 1.0, hwo, hto);
+  fold(w->w_gate, w->ln_in_gamma, w->ln_in_beta, w->b_gate, c_z, c_z, czp, bf16, ng, hwg, htg);
 
   tri_mul_handle* h = new (std::nothrow) tri_mul_handle();
   if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
@@ -229,6 +240,7 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   h->cp = cp;
   h->dtype = dtype;
   h->device = dev;
+  h->num_cus = cus;
   h->bf16 = bf16;
   h->block = dptr;
   trimul::StageArgs& a = h->w;
@@ -236,12 +248,10 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   a.w1 = d;
   a.wo = d + w1b;
   a.wg = d + w1b + wob;
-  a.s1 = (const float*)(d + ((unsigned char*)hs1 - hw1));
   a.t1 = (const float*)(d + ((unsigned char*)ht1 - hw1));
-  a.so = (const float*)(d + ((unsigned char*)hso - hw1));
   a.to = (const float*)(d + ((unsigned char*)hto - hw1));
-  a.sg = (const float*)(d + ((unsigned char*)hsg - hw1));
   a.tg = (const float*)(d + ((unsigned char*)htg - hw1));
+  a.one = d + (hone - hw1);
   a.cz = c_z;
   a.czp = czp;
   a.c = c;
@@ -292,7 +302,7 @@ const char* tri_mul_strerror(int code) {
   switch (code) {
     case TRI_MUL_OK: return "ok";
     case TRI_MUL_ERR_INVALID_ARG: return "invalid argument (NULL pointer, size out of range or bad enum)";
-    case TRI_MUL_ERR_UNSUPPORTED: return "unsupported configuration (c_z and c must be multiples of 16, at most 1024; dtype fp32 or bf16)";
+    case TRI_MUL_ERR_UNSUPPORTED: return "unsupported configuration (c_z and c multiples of 16; at most 512 for bf16, c_z 256 / c 128 for fp32; dtype fp32 or bf16)";
     case TRI_MUL_ERR_UNSUPPORTED_DEVICE: return "unsupported device (needs gfx950, the device the handle was created on)";
     case TRI_MUL_ERR_ALIGNMENT: return "device pointer not 16-byte aligned";
     case TRI_MUL_ERR_ALIAS: return "output or workspace overlaps another buffer";

@@ -52,7 +52,8 @@ def _weights_struct(w):
 
 
 @pytest.mark.parametrize("c_z,c,dtype,code", [
-    (24, 16, tm.TRI_MUL_BF16, -2), (16, 40, tm.TRI_MUL_BF16, -2), (2048, 16, tm.TRI_MUL_FP32, -2),
+    (24, 16, tm.TRI_MUL_BF16, -2), (16, 40, tm.TRI_MUL_BF16, -2), (528, 16, tm.TRI_MUL_BF16, -2),
+    (16, 528, tm.TRI_MUL_BF16, -2), (272, 16, tm.TRI_MUL_FP32, -2), (16, 144, tm.TRI_MUL_FP32, -2),
     (16, 16, 7, -2), (0, 16, tm.TRI_MUL_FP32, -1), (16, -16, tm.TRI_MUL_FP32, -1),
 ])
 def test_create_rejects_bad_shapes_before_touching_the_device(lib, c_z, c, dtype, code):
