@@ -27,6 +27,13 @@ __device__ __forceinline__ float to_f32(float v) { return v; }
 __device__ __forceinline__ chunk_t ld16(const void* p) { return *(const chunk_t*)p; }
 __device__ __forceinline__ void st16(void* p, chunk_t v) { *(chunk_t*)p = v; }
 __device__ __forceinline__ f32x4 ld16f(const float* p) { return *(const f32x4*)p; }
+// 16 bytes from an LDS address that is only 8-byte aligned (bf16 staging rows); fp32
+// staging rows are 16-byte aligned.
+__device__ __forceinline__ chunk_t ld16_lds8(const bf16* p) {
+  const half_t lo = *(const half_t*)p, hi = *(const half_t*)(p + 4);
+  return chunk_t{lo[0], lo[1], hi[0], hi[1]};
+}
+__device__ __forceinline__ chunk_t ld16_lds8(const float* p) { return ld16(p); }
 
 // chunk <-> floats
 __device__ __forceinline__ void unpack(chunk_t c, float* f, bf16) {
@@ -91,15 +98,27 @@ __device__ __forceinline__ f32x16 mma32(f32x16 acc, chunk_t a, chunk_t b, float)
   return acc;
 }
 
-// Sum over the 8 consecutive lanes 8q .. 8q+7 (two quad permutes, then the half-row mirror),
-// every lane of the group receives the total.
+// Sum over the G consecutive lanes G*q .. G*q+G-1 (G = 4 or 8; quad permutes, then the
+// half-row mirror for 8); every lane of the group receives the total.
 #define TRIMUL_DPP(v, ctrl) \
   __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true))
-__device__ __forceinline__ float sum8(float v) {
-  v += TRIMUL_DPP(v, 0xB1);   // quad_perm [1,0,3,2]
-  v += TRIMUL_DPP(v, 0x4E);   // quad_perm [2,3,0,1]
-  v += TRIMUL_DPP(v, 0x141);  // row_half_mirror
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 4 || G == 8, "group of 4 or 8 lanes");
+  v += TRIMUL_DPP(v, 0xB1);  // quad_perm [1,0,3,2]
+  v += TRIMUL_DPP(v, 0x4E);  // quad_perm [2,3,0,1]
+  if (G == 8) v += TRIMUL_DPP(v, 0x141);  // row_half_mirror
   return v;
+}
+
+// Orders this wave's earlier LDS writes before its later LDS reads of other lanes' data
+// (LDS operations of one wave are executed in issue order; the fences stop the compiler
+// from moving accesses across this point and wait for the writes to complete).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // out = p * m * sigmoid(g) with the gate pre-activation given as g2 = -g * log2(e)
@@ -108,44 +127,71 @@ __device__ __forceinline__ float gate_mul(float p_times_m, float g2) {
   return p_times_m * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g2));
 }
 
-// LayerNorm of one row held by the 8 lanes of a pair: lane `part` holds chunks part,
-// part+8, ... of the row in v[0..NCH); chunk indices >= nreal are padding (zero, and not
-// counted). Normalises v in place to (x - mean) * rstd over the `width` real values
-// (two passes in fp32); padding chunks stay zero.
-template <class T, int NCH>
-__device__ __forceinline__ void normalize_row(chunk_t (&v)[NCH], int part, int nreal, int width) {
-  constexpr int E = Traits<T>::E;
-  float s = 0.f;
+// LayerNorm of one row held by the G consecutive lanes of a pair: lane `part` holds
+// chunks part, part+G, ... of the row in v[0..NCH); chunk indices >= nreal are padding
+// (zero, and not counted). Normalises v in place to (x - mean) * rstd over the `width`
+// real values; padding chunks stay zero. The bf16 version takes sum and sum of squares in
+// one fp32 pass; the fp32 version uses two passes.
+template <int NCH, int G>
+__device__ __forceinline__ void normalize_row_stats(const chunk_t (&v)[NCH], int part, int nreal,
+                                                    int width, float& mean, float& rstd, bf16) {
+  // bf16 -> fp32 by shifting (the packed bf16 dot-product route is not used: this
+  // compiler feeds every unrolled v_dot2c_f32_bf16 the same source register)
+  float s = 0.f, q = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    float f[E];
-    unpack(v[i], f, T());
+    float f[8];
+    unpack(v[i], f, bf16());
 #pragma unroll
-    for (int e = 0; e < E; ++e) s += f[e];
+    for (int e = 0; e < 8; ++e) {
+      s += f[e];
+      q = fmaf(f[e], f[e], q);
+    }
   }
+  (void)part;
+  (void)nreal;
   const float inv_w = 1.0f / (float)width;
-  const float mean = sum8(s) * inv_w;
+  mean = group_sum<G>(s) * inv_w;
+  const float var = group_sum<G>(q) * inv_w - mean * mean;
+  rstd = rsqrtf(fmaxf(var, 0.f) + TRI_MUL_LN_EPS_F);
+}
+template <int NCH, int G>
+__device__ __forceinline__ void normalize_row_stats(const chunk_t (&v)[NCH], int part, int nreal,
+                                                    int width, float& mean, float& rstd, float) {
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < NCH; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += __uint_as_float(v[i][e]);
+  const float inv_w = 1.0f / (float)width;
+  mean = group_sum<G>(s) * inv_w;
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    if (part + 8 * i < nreal) {
-      float f[E];
-      unpack(v[i], f, T());
+    if (part + G * i < nreal) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const float d = f[e] - mean;
+      for (int e = 0; e < 4; ++e) {
+        const float d = __uint_as_float(v[i][e]) - mean;
         q += d * d;
       }
     }
   }
-  const float rstd = rsqrtf(sum8(q) * inv_w + TRI_MUL_LN_EPS_F);
+  rstd = rsqrtf(group_sum<G>(q) * inv_w + TRI_MUL_LN_EPS_F);
+}
+
+template <class T, int NCH, int G>
+__device__ __forceinline__ void normalize_row(chunk_t (&v)[NCH], int part, int nreal, int width) {
+  constexpr int E = Traits<T>::E;
+  float mean, rstd;
+  normalize_row_stats<NCH, G>(v, part, nreal, width, mean, rstd, T());
+  const float shift = -mean * rstd;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    if (part + 8 * i < nreal) {
+    if (part + G * i < nreal) {
       float f[E];
       unpack(v[i], f, T());
 #pragma unroll
-      for (int e = 0; e < E; ++e) f[e] = (f[e] - mean) * rstd;
+      for (int e = 0; e < E; ++e) f[e] = fmaf(f[e], rstd, shift);
       v[i] = pack(f, T());
     }
   }

@@ -5,16 +5,17 @@
 // gates" (x_x form sigma(x W_g^T + b_g) * (x W_p^T + b_p); the input gate absorbs the
 // pair mask and writes its output already laid out for the contraction).
 //
-// The k extent is a compile-time constant: the host pads c_z to exactly KMAX chunk groups.
 // Work split (persistent): a tile is TP = 64 consecutive storage columns of one storage
 // row r; for outgoing the z pairs are (r, s), for incoming (s, r), so both directions
 // store a[b][ch][r][s] contiguously along s. A workgroup of 8 waves loops over tiles.
 // Each wave owns UPW "units" (a unit = the gate and proj rows of 16 channels of a or b)
-// and keeps their weights in registers for the whole kernel; the tile's normalised z
-// (the MFMA A operand) is shared through LDS. The LayerNorm gamma is folded into the
-// weights and beta / the bias into the accumulator's initial value (host side); the gate
-// rows carry an extra -log2(e) so the epilogue is one exp2 and one reciprocal.
+// and keeps their weights in registers for the whole launch; the tile's normalised z
+// (the MFMA A operand) is shared through double-buffered LDS. The LayerNorm gamma is
+// folded into the weights and beta / the bias into the accumulator's initial value (host
+// side); the gate rows carry an extra -log2(e) so the gate is one exp2 and one reciprocal.
+// The k extent is a compile-time constant: the host pads c_z to exactly KMAX chunk groups.
 // The next tile's z is fetched into registers while the MFMAs of the current tile run.
+// Results are staged per wave in LDS and written as whole rows of TP contiguous pairs.
 
 #include "device_common.h"
 
@@ -23,58 +24,104 @@ namespace trimul {
 constexpr int K1_TP = 64;
 constexpr int K1_WAVES = 8;
 constexpr int K1_THREADS = 64 * K1_WAVES;
+constexpr int K1_TPP = K1_THREADS / K1_TP;  // threads per pair when staging a tile
 
 template <class T, int KMAX, int UPW>
-__global__ __launch_bounds__(K1_THREADS, 2) void k1_input_gate(
+__global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
     const T* __restrict__ z, const T* __restrict__ mask, T* __restrict__ a_out,
     T* __restrict__ b_out, const T* __restrict__ w1, const float* __restrict__ t1, int n, int np,
-    int cz, int czp, int c, int incoming, int mask_all, int total_tiles) {
+    int cz, int czp, int c, int incoming, int mask_all, int nbuf, int total_tiles) {
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int TP = K1_TP;
-  constexpr int NCH = (KMAX * KG / E + 7) / 8;  // z chunks per thread (8 threads per pair)
+  constexpr int TPP = K1_TPP;
+  constexpr int NCH = (KMAX * KG / E + TPP - 1) / TPP;  // z chunks per thread
+  // staging row (one channel, TP pairs): for bf16 an 8-byte-aligned stride of 34 dwords so
+  // the 8-byte writes of 16 consecutive rows hit distinct banks; fp32 rows stay 16-byte
+  // aligned (68 dwords).
+  constexpr int SROW = TP + 4;
+  constexpr int CPT = TP / E;       // 16-byte chunks per staged row
+  constexpr int NST = UPW * 16 * CPT / 64;  // 16-byte stores per lane per tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int zstride = czp + E;
-  // LDS: normalised z tiles [2][TP][zstride], masks [2][TP]
+  // LDS: normalised z tiles [nbuf][TP][zstride], masks [nbuf][TP], per-wave output
+  // staging [UPW*16 channels][SROW]. nbuf = 2 double-buffers the z tile; wide c_z that does
+  // not fit uses one buffer and an extra barrier per tile.
   T* const zbase = (T*)smem;
-  float* const mvbuf = (float*)(zbase + 2 * TP * zstride);
+  float* const mvbuf = (float*)(zbase + nbuf * TP * zstride);
   auto zbuf = [&](int b) { return zbase + b * TP * zstride; };
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  T* const stg = (T*)(mvbuf + nbuf * TP) + (size_t)wave * UPW * 16 * SROW;
   const int cblocks = c / 16, units = 2 * cblocks;
   const int ntx = np / TP;
+  const size_t plane = (size_t)np * np;  // one channel of a or b
 
   // ---- this wave's units: weights and biases into registers ----
   chunk_t wgt[UPW][2][KMAX];
-  float bias[UPW][2];
-  int uch[UPW], uq[UPW];
+  f32x4 bias[UPW][2];
+  int uq[UPW], ucb[UPW];
   bool uok[UPW];
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
     const int u = blockIdx.y * (K1_WAVES * UPW) + wave + K1_WAVES * j;
     uok[j] = u < units;
     uq[j] = uok[j] ? u / cblocks : 0;
-    uch[j] = uok[j] ? (u - uq[j] * cblocks) * 16 + (lane & 15) : 0;
+    ucb[j] = uok[j] ? (u - uq[j] * cblocks) * 16 : 0;
 #pragma unroll
     for (int gp = 0; gp < 2; ++gp) {
-      const size_t row = (size_t)(2 * uq[j] + gp) * c + uch[j];
-      bias[j][gp] = uok[j] ? t1[row] : 0.f;
+      const size_t row = (size_t)(2 * uq[j] + gp) * c + ucb[j] + (lane & 15);
+      const float bv = uok[j] ? t1[row] : 0.f;
+      bias[j][gp] = f32x4{bv, bv, bv, bv};
 #pragma unroll
       for (int ks = 0; ks < KMAX; ++ks)
         wgt[j][gp][ks] = uok[j] ? ld16(w1 + row * czp + ks * KG + (lane >> 4) * E)
                                 : chunk_t{0u, 0u, 0u, 0u};
     }
   }
+  // per-lane offsets of the staged rows this lane stores (k-th store: row, chunk)
+  size_t soff[NST];
+#pragma unroll
+  for (int k = 0; k < NST; ++k) {
+    const int idx = k * 64 + lane, row = idx / CPT, cc = idx - row * CPT;
+    soff[k] = (size_t)(ucb[row >> 4] + (row & 15)) * plane + cc * E;
+  }
 
-  // ---- tile staging: thread (t, part) handles chunks part, part+8, ... of pair t ----
-  const int t = tid >> 3, part = tid & 7;
+  // ---- tile staging: thread (t, part) handles chunks part, part+TPP, ... of pair t ----
+  const int t = tid / TPP, part = tid % TPP;
   const int czc = cz / E, cpr = czp / E;
-  auto tile_coords = [&](int tile, int& bb, int& r, int& s0) {
-    bb = tile / (np * ntx);
-    const int rem = tile - bb * np * ntx;
-    r = rem / ntx;
-    s0 = (rem - r * ntx) * TP;
+  // pair t of a tile sits t pairs (outgoing) or t rows (incoming) after the tile's first pair
+  const size_t tstep = incoming ? (size_t)n : 1;
+
+  // Tiles are visited as tile = blockIdx.x + k * gridDim.x with tile = (bb*np + r)*ntx + sx;
+  // the coordinates advance incrementally (no divisions in the loop).
+  struct Coord {
+    int bb, r, sx;
   };
+  auto decompose = [&](int tile) {
+    Coord q;
+    q.bb = tile / (np * ntx);
+    const int rem = tile - q.bb * np * ntx;
+    q.r = rem / ntx;
+    q.sx = rem - q.r * ntx;
+    return q;
+  };
+  const Coord step = decompose(gridDim.x);
+  auto advance = [&](Coord q) {
+    q.sx += step.sx;
+    q.r += step.r;
+    q.bb += step.bb;
+    if (q.sx >= ntx) {
+      q.sx -= ntx;
+      ++q.r;
+    }
+    if (q.r >= np) {
+      q.r -= np;
+      ++q.bb;
+    }
+    return q;
+  };
+
   // The next tile is fetched into registers with unconditional loads from clamped,
   // in-bounds addresses (no branches), and every select that depends on the loaded data
   // happens in stage(), after the current tile's MFMAs: the loads stay in flight meanwhile.
@@ -84,17 +131,19 @@ __global__ __launch_bounds__(K1_THREADS, 2) void k1_input_gate(
     T m;
     bool valid;
   };
-  auto fetch = [&](int tile, Pre& f) {
-    int bb, r, s0;
-    tile_coords(tile, bb, r, s0);
-    const int s = s0 + t;
-    const int p = incoming ? s : r, q = incoming ? r : s;
-    f.valid = p < n && q < n;
-    const size_t pair = f.valid ? ((size_t)bb * n + p) * n + q : 0;
+  auto fetch = [&](Coord q, Pre& f) {
+    const int s0 = q.sx * TP;
+    const bool tile_ok = q.r < n && s0 < n;  // uniform
+    f.valid = tile_ok && s0 + t < n;
+    // first pair of the tile: (r, s0) outgoing, (s0, r) incoming
+    const size_t p0 = tile_ok ? (incoming ? ((size_t)q.bb * n + s0) * n + q.r
+                                          : ((size_t)q.bb * n + q.r) * n + s0)
+                              : 0;
+    const size_t pair = p0 + (f.valid ? t * tstep : 0);
     const T* src = z + pair * cz;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = part + 8 * i;
+      const int ch = part + TPP * i;
       f.v[i] = ld16(src + (ch < czc ? ch : 0) * E);
     }
     f.m = mask[mask_all ? 0 : pair];
@@ -102,46 +151,57 @@ __global__ __launch_bounds__(K1_THREADS, 2) void k1_input_gate(
   auto stage = [&](int buf, Pre& f) {
 #pragma unroll
     for (int i = 0; i < NCH; ++i)
-      if (!(f.valid && part + 8 * i < czc)) f.v[i] = chunk_t{0u, 0u, 0u, 0u};
-    normalize_row<T, NCH>(f.v, part, czc, cz);
+      if (!(f.valid && part + TPP * i < czc)) f.v[i] = chunk_t{0u, 0u, 0u, 0u};
+    normalize_row<T, NCH, TPP>(f.v, part, czc, cz);
     T* row = zbuf(buf) + t * zstride;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
-      const int ch = part + 8 * i;
+      const int ch = part + TPP * i;
       if (ch < cpr) st16(row + ch * E, f.v[i]);
     }
     if (part == 0) mvbuf[buf * TP + t] = f.valid ? to_f32(f.m) : 0.f;
   };
 
   int tile = blockIdx.x;  // the grid never exceeds the tile count
+  Coord cur_c = decompose(tile);
   {
     Pre f;
-    fetch(tile, f);
+    fetch(cur_c, f);
     stage(0, f);
   }
   __syncthreads();
 
   for (int it = 0; tile < total_tiles; tile += gridDim.x, ++it) {
-    const int cur = it & 1;
-    const int next = tile + gridDim.x;
+    const int cur = nbuf == 2 ? (it & 1) : 0;
+    const bool has_next = tile + (int)gridDim.x < total_tiles;
+    const Coord next_c = has_next ? advance(cur_c) : cur_c;
     Pre pre;
-    fetch(next < total_tiles ? next : tile, pre);  // the last iteration refetches, unused
+    fetch(next_c, pre);  // the last iteration refetches the current tile, unused
 
-    int bb, r, s0;
-    tile_coords(tile, bb, r, s0);
     const T* zs = zbuf(cur);
     const float* mv = mvbuf + cur * TP;
 #pragma unroll
     for (int rt = 0; rt < TP / 16; ++rt) {
-      f32x4 acc[UPW][2];
+      // accumulator register rr <-> pair rt*16 + 4*(lane/16) + rr, channel lane%16 of unit
+      const int p0 = rt * 16 + 4 * (lane >> 4);
+      T* const srow = stg + (lane & 15) * SROW + p0;
+      if (__all(mv[rt * 16 + (lane & 15)] == 0.f)) {  // fully padded: zero, no MFMA
 #pragma unroll
-      for (int j = 0; j < UPW; ++j)
-#pragma unroll
-        for (int gp = 0; gp < 2; ++gp)
-          acc[j][gp] = f32x4{bias[j][gp], bias[j][gp], bias[j][gp], bias[j][gp]};
+        for (int j = 0; j < UPW; ++j) store4(srow + j * 16 * SROW, 0.f, 0.f, 0.f, 0.f);
+        continue;
+      }
       const T* arow = zs + (rt * 16 + (lane & 15)) * zstride + (lane >> 4) * E;
+      f32x4 acc[UPW][2];
+      {
+        const chunk_t af = ld16(arow);
 #pragma unroll
-      for (int ks = 0; ks < KMAX; ++ks) {
+        for (int j = 0; j < UPW; ++j) {
+          acc[j][0] = mma16(bias[j][0], af, wgt[j][0][0], T());
+          acc[j][1] = mma16(bias[j][1], af, wgt[j][1][0], T());
+        }
+      }
+#pragma unroll
+      for (int ks = 1; ks < KMAX; ++ks) {
         const chunk_t af = ld16(arow + ks * KG);
 #pragma unroll
         for (int j = 0; j < UPW; ++j) {
@@ -149,21 +209,30 @@ __global__ __launch_bounds__(K1_THREADS, 2) void k1_input_gate(
           acc[j][1] = mma16(acc[j][1], af, wgt[j][1][ks], T());
         }
       }
-      // accumulator register rr <-> pair rt*16 + 4*(lane/16) + rr, channel uch
-      const int p0 = rt * 16 + 4 * (lane >> 4);
       const f32x4 m4 = ld16f(mv + p0);
 #pragma unroll
-      for (int j = 0; j < UPW; ++j) {
-        if (!uok[j]) continue;
-        float o[4];
+      for (int j = 0; j < UPW; ++j)
+        store4(srow + j * 16 * SROW, gate_mul(acc[j][1][0] * m4[0], acc[j][0][0]),
+               gate_mul(acc[j][1][1] * m4[1], acc[j][0][1]),
+               gate_mul(acc[j][1][2] * m4[2], acc[j][0][2]),
+               gate_mul(acc[j][1][3] * m4[3], acc[j][0][3]));
+    }
+    // staging -> global: UPW*16 channel rows of TP contiguous elements (full cache lines)
+    wave_lds_sync();
+    const size_t tbase = (size_t)cur_c.bb * c * plane + (size_t)cur_c.r * np + cur_c.sx * TP;
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) o[rr] = gate_mul(acc[j][1][rr] * m4[rr], acc[j][0][rr]);
-        T* dst = (uq[j] ? b_out : a_out) + (((size_t)bb * c + uch[j]) * np + r) * np + s0 + p0;
-        store4(dst, o[0], o[1], o[2], o[3]);
+    for (int k = 0; k < NST; ++k) {
+      const int idx = k * 64 + lane, row = idx / CPT, cc = idx - row * CPT;
+      const int j = (k * 64) / CPT / 16;  // the same unit for the whole store
+      if (uok[j]) {
+        T* dst = (uq[j] ? b_out : a_out) + tbase + soff[k];
+        st16(dst, ld16_lds8(stg + row * SROW + cc * E));
       }
     }
-    stage(cur ^ 1, pre);
+    if (nbuf == 1) __syncthreads();  // every wave is done reading the single z buffer
+    stage(nbuf == 2 ? cur ^ 1 : 0, pre);
     __syncthreads();
+    cur_c = next_c;
   }
 }
 
@@ -172,7 +241,12 @@ __global__ __launch_bounds__(K1_THREADS, 2) void k1_input_gate(
 template <class T, int KMAX, int UPW>
 static hipError_t launch_k1_t(const StageArgs& a, hipStream_t st) {
   constexpr int E = Traits<T>::E;
-  const size_t lds = 2 * (size_t)K1_TP * (a.czp + E) * sizeof(T) + 2 * K1_TP * sizeof(float);
+  auto lds_for = [&](int nb) {
+    return nb * ((size_t)K1_TP * (a.czp + E) * sizeof(T) + K1_TP * sizeof(float)) +
+           (size_t)K1_WAVES * UPW * 16 * (K1_TP + 4) * sizeof(T);
+  };
+  const int nbuf = lds_for(2) <= LDS_PER_CU ? 2 : 1;
+  const size_t lds = lds_for(nbuf);
   auto fn = k1_input_gate<T, KMAX, UPW>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
@@ -188,10 +262,12 @@ static hipError_t launch_k1_t(const StageArgs& a, hipStream_t st) {
   const int mask_all = a.mask == nullptr;
   hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K1_THREADS), lds, st, (const T*)a.z,
                      (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b, (const T*)a.w1, a.t1,
-                     a.n, a.np, a.cz, a.czp, a.c, a.incoming, mask_all, total);
+                     a.n, a.np, a.cz, a.czp, a.c, a.incoming, mask_all, nbuf, total);
   return hipGetLastError();
 }
 
+// Units per wave: as many as the register budget allows for the k extent (the weights of
+// one unit take 8 * KMAX registers).
 template <class T>
 static hipError_t launch_k1_dispatch(const StageArgs& a, hipStream_t st) {
   switch (a.czp / Traits<T>::KG) {

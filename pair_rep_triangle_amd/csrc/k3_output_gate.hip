@@ -10,9 +10,9 @@
 // chunk groups.
 // Work split (persistent): a tile is TP = 64 consecutive pairs (i, j0 .. j0+63) of one row
 // i. Per tile the workgroup stages x (read channel-major, transposed on the way in
-// through registers) and z in LDS and normalises both rows in place; then each of the 8
-// waves computes UPW=1 unit = 16 output channels for the 64 pairs with the weights of its
-// unit held in registers (W_o as A operand against xhat, W_g against zhat). Biases and
+// through registers) and z in LDS and normalises both rows in place; then each of the 4
+// waves computes UPW=2 units of 16 output channels for the 64 pairs with the weights of its
+// units held in registers (W_o as A operand against xhat, W_g against zhat). Biases and
 // beta terms start the accumulators; the gate rows carry -log2(e) (host side). The next
 // tile's x and z are fetched into registers while the current tile's MFMAs run.
 
@@ -21,26 +21,33 @@
 namespace trimul {
 
 constexpr int K3_TP = 64;
-constexpr int K3_WAVES = 8;
+constexpr int K3_WAVES = 4;
 constexpr int K3_THREADS = 64 * K3_WAVES;
+constexpr int K3_TPP = K3_THREADS / K3_TP;  // threads per pair when staging a tile
+constexpr int K3_UPW = 2;                   // 16-channel output units per wave
+constexpr size_t K3_LDS_BUDGET = 80 * 1024;  // double-buffer only while two workgroups fit a CU
 
-template <class T, int KXM, int KZM>
-__global__ __launch_bounds__(K3_THREADS, 2) void k3_output_gate(
+template <class T, int KXM, int KZM, int XB>
+__global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
     const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ mask,
     T* __restrict__ out, const T* __restrict__ wo, const float* __restrict__ to,
     const T* __restrict__ wg, const float* __restrict__ tg, int n, int np, int cz, int czp, int c,
-    int cp, int mask_all, int total_tiles) {
+    int cp, int mask_all, int nbuf, int total_tiles) {
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int TP = K3_TP;
   constexpr int KMAX = KXM > KZM ? KXM : KZM;
-  constexpr int NCH = (KMAX * KG / E + 7) / 8;  // chunks per thread of one LDS row
+  constexpr int TPP = K3_TPP;
+  constexpr int UPW = K3_UPW;
+  constexpr int NCH = (KMAX * KG / E + TPP - 1) / TPP;  // chunks per thread of one LDS row
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int xstride = cp + E, zstride = czp + E;
-  // LDS: x tiles [2][TP][xstride], z tiles [2][TP][zstride], masks [2][TP]
+  // LDS: x tiles [nbuf][TP][xstride], z tiles [nbuf][TP][zstride], masks [nbuf][TP].
+  // nbuf = 2 double-buffers the staging; wide widths that do not fit use one buffer and an
+  // extra barrier per tile.
   T* const xbase = (T*)smem;
-  T* const zbase = xbase + 2 * TP * xstride;
-  float* const mvbuf = (float*)(zbase + 2 * TP * zstride);
+  T* const zbase = xbase + nbuf * TP * xstride;
+  float* const mvbuf = (float*)(zbase + nbuf * TP * zstride);
   auto xbuf = [&](int b) { return xbase + b * TP * xstride; };
   auto zbuf = [&](int b) { return zbase + b * TP * zstride; };
 
@@ -48,33 +55,37 @@ __global__ __launch_bounds__(K3_THREADS, 2) void k3_output_gate(
   const int units = cz / 16;
   const int ntx = (n + TP - 1) / TP;
 
-  // ---- this wave's unit: 16 output channels, weights in registers ----
-  const int u = blockIdx.y * K3_WAVES + wave;
-  const bool uok = u < units;
-  const int orow = uok ? u * 16 + (lane & 15) : 0;  // A-operand row this lane hands in
-  chunk_t wor[KXM], wgr[KZM];
+  // ---- this wave's units: 16 output channels each, weights in registers ----
+  chunk_t wor[UPW][KXM], wgr[UPW][KZM];
+  f32x4 bo[UPW], bg[UPW];
+  bool uok[UPW];
+  int oc0[UPW];  // accumulator register rr <-> output channel oc0 + rr
 #pragma unroll
-  for (int ks = 0; ks < KXM; ++ks)
-    wor[ks] = uok ? ld16(wo + (size_t)orow * cp + ks * KG + (lane >> 4) * E)
-                  : chunk_t{0u, 0u, 0u, 0u};
+  for (int jj = 0; jj < UPW; ++jj) {
+    const int u = blockIdx.y * (K3_WAVES * UPW) + wave + K3_WAVES * jj;
+    uok[jj] = u < units;
+    const int orow = uok[jj] ? u * 16 + (lane & 15) : 0;  // A-operand row this lane hands in
 #pragma unroll
-  for (int ks = 0; ks < KZM; ++ks)
-    wgr[ks] = uok ? ld16(wg + (size_t)orow * czp + ks * KG + (lane >> 4) * E)
-                  : chunk_t{0u, 0u, 0u, 0u};
-  // accumulator register rr <-> output channel u*16 + 4*(lane/16) + rr
-  const int oc0 = uok ? u * 16 + 4 * (lane >> 4) : 0;
-  const f32x4 bo = uok ? ld16f(to + oc0) : f32x4{0.f, 0.f, 0.f, 0.f};
-  const f32x4 bg = uok ? ld16f(tg + oc0) : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int ks = 0; ks < KXM; ++ks)
+      wor[jj][ks] = uok[jj] ? ld16(wo + (size_t)orow * cp + ks * KG + (lane >> 4) * E)
+                            : chunk_t{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int ks = 0; ks < KZM; ++ks)
+      wgr[jj][ks] = uok[jj] ? ld16(wg + (size_t)orow * czp + ks * KG + (lane >> 4) * E)
+                            : chunk_t{0u, 0u, 0u, 0u};
+    oc0[jj] = uok[jj] ? u * 16 + 4 * (lane >> 4) : 0;
+    bo[jj] = uok[jj] ? ld16f(to + oc0[jj]) : f32x4{0.f, 0.f, 0.f, 0.f};
+    bg[jj] = uok[jj] ? ld16f(tg + oc0[jj]) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   // ---- staging maps ----
-  // x: thread b < (c/E)*(TP/E) moves an E x E block (E channels x E pairs) through
-  // registers; the channel block varies fastest across lanes so that the transposed LDS
-  // writes of neighbouring lanes land in different banks.
-  const int xblocks = (c / E) * (TP / E);
-  const bool xact = tid < xblocks;
-  const int xpb = tid / (c / E), xcb = tid - xpb * (c / E);
-  // z and the row normalisation: thread (t, part) owns chunks part, part+8, ... of pair t
-  const int t = tid >> 3, part = tid & 7;
+  // x: the (c/E)*(TP/E) blocks of E channels x E pairs are moved through registers, XB
+  // per thread (block tid + k*THREADS); the channel block varies fastest across lanes so
+  // that the transposed LDS writes of neighbouring lanes land in different banks.
+  const int cbn = c / E;
+  const int xblocks = cbn * (TP / E);
+  // z and the row normalisation: thread (t, part) owns chunks part, part+TPP, ... of pair t
+  const int t = tid / TPP, part = tid % TPP;
   const int czc = cz / E, ccz = czp / E, cxc = c / E, ccx = cp / E;
 
   auto tile_coords = [&](int tile, int& bb, int& i, int& j0) {
@@ -88,7 +99,7 @@ __global__ __launch_bounds__(K3_THREADS, 2) void k3_output_gate(
   // stage(), after the current tile's MFMAs, so the loads stay in flight meanwhile.
   // `mask_all` (no mask given) reads the one-valued element at mask[0].
   struct Pre {
-    chunk_t xv[E];
+    chunk_t xv[XB][E];
     chunk_t zv[NCH];
     T m;
     bool valid;
@@ -96,48 +107,56 @@ __global__ __launch_bounds__(K3_THREADS, 2) void k3_output_gate(
   auto fetch = [&](int tile, Pre& f) {
     int bb, i, j0;
     tile_coords(tile, bb, i, j0);
-    {
-      const int cb = xact ? xcb : 0, pb = xact ? xpb : 0;
+#pragma unroll
+    for (int k = 0; k < XB; ++k) {
+      const int blk = tid + k * K3_THREADS;
+      const int bl = blk < xblocks ? blk : 0;
+      const int pb = bl / cbn, cb = bl - pb * cbn;
       const T* src = x + (((size_t)bb * c + cb * E) * np + i) * np + j0 + pb * E;
 #pragma unroll
-      for (int e = 0; e < E; ++e) f.xv[e] = ld16(src + (size_t)e * np * np);
+      for (int e = 0; e < E; ++e) f.xv[k][e] = ld16(src + (size_t)e * np * np);
     }
     const int j = j0 + t;
     f.valid = j < n;
     const size_t pair = f.valid ? ((size_t)bb * n + i) * n + j : 0;
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int ch = part + 8 * q;
+      const int ch = part + TPP * q;
       f.zv[q] = ld16(z + pair * cz + (ch < czc ? ch : 0) * E);
     }
     f.m = mask[mask_all ? 0 : pair];
   };
   // writes the fetched tile into LDS buffer `buf`; z rows normalised on the way
   auto stage = [&](int buf, Pre& f) {
-    if (xact) {
-      T blk[E][E];
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const T* pv = (const T*)&f.xv[e];
+    for (int k = 0; k < XB; ++k) {
+      const int blk = tid + k * K3_THREADS;
+      if (blk < xblocks) {
+        const int pb = blk / cbn, cb = blk - pb * cbn;
+        T tb[E][E];
 #pragma unroll
-        for (int f = 0; f < E; ++f) blk[e][f] = pv[f];
-      }
+        for (int e = 0; e < E; ++e) {
+          const T* pv = (const T*)&f.xv[k][e];
 #pragma unroll
-      for (int f = 0; f < E; ++f) {
-        T col[E];
+          for (int ff = 0; ff < E; ++ff) tb[e][ff] = pv[ff];
+        }
 #pragma unroll
-        for (int e = 0; e < E; ++e) col[e] = blk[e][f];
-        st16(xbuf(buf) + (xpb * E + f) * xstride + xcb * E, __builtin_bit_cast(chunk_t, col));
+        for (int ff = 0; ff < E; ++ff) {
+          T col[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) col[e] = tb[e][ff];
+          st16(xbuf(buf) + (pb * E + ff) * xstride + cb * E, __builtin_bit_cast(chunk_t, col));
+        }
       }
     }
 #pragma unroll
     for (int q = 0; q < NCH; ++q)
-      if (!(f.valid && part + 8 * q < czc)) f.zv[q] = chunk_t{0u, 0u, 0u, 0u};
-    normalize_row<T, NCH>(f.zv, part, czc, cz);
+      if (!(f.valid && part + TPP * q < czc)) f.zv[q] = chunk_t{0u, 0u, 0u, 0u};
+    normalize_row<T, NCH, TPP>(f.zv, part, czc, cz);
     T* zrow = zbuf(buf) + t * zstride;
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int ch = part + 8 * q;
+      const int ch = part + TPP * q;
       if (ch < ccz) st16(zrow + ch * E, f.zv[q]);
     }
     if (part == 0) mvbuf[buf * TP + t] = f.valid ? to_f32(f.m) : 0.f;
@@ -148,13 +167,13 @@ __global__ __launch_bounds__(K3_THREADS, 2) void k3_output_gate(
     chunk_t v[NCH];
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int ch = part + 8 * q;
+      const int ch = part + TPP * q;
       v[q] = ch < cxc ? ld16(xrow + ch * E) : chunk_t{0u, 0u, 0u, 0u};
     }
-    normalize_row<T, NCH>(v, part, cxc, c);
+    normalize_row<T, NCH, TPP>(v, part, cxc, c);
 #pragma unroll
     for (int q = 0; q < NCH; ++q) {
-      const int ch = part + 8 * q;
+      const int ch = part + TPP * q;
       if (ch < ccx) st16(xrow + ch * E, v[q]);
     }
   };
@@ -170,7 +189,8 @@ __global__ __launch_bounds__(K3_THREADS, 2) void k3_output_gate(
   __syncthreads();
 
   for (int it = 0; tile < total_tiles; tile += gridDim.x, ++it) {
-    const int cur = it & 1;
+    const int cur = nbuf == 2 ? (it & 1) : 0;
+    const int nxt = nbuf == 2 ? (cur ^ 1) : 0;
     const int next = tile + gridDim.x;
     Pre pre;
     fetch(next < total_tiles ? next : tile, pre);  // the last iteration refetches, unused
@@ -182,42 +202,63 @@ __global__ __launch_bounds__(K3_THREADS, 2) void k3_output_gate(
     const float* mv = mvbuf + cur * TP;
 #pragma unroll
     for (int pt = 0; pt < TP / 16; ++pt) {
-      f32x4 ap = bo, ag = bg;
+      f32x4 ap[UPW], ag[UPW];
+#pragma unroll
+      for (int jj = 0; jj < UPW; ++jj) {
+        ap[jj] = bo[jj];
+        ag[jj] = bg[jj];
+      }
       const int pr = pt * 16 + (lane & 15);  // B-operand column = pair
       const T* xr = xs + pr * xstride + (lane >> 4) * E;
       const T* zr = zs + pr * zstride + (lane >> 4) * E;
 #pragma unroll
-      for (int ks = 0; ks < KXM; ++ks) ap = mma16(ap, wor[ks], ld16(xr + ks * KG), T());
+      for (int ks = 0; ks < KXM; ++ks) {
+        const chunk_t xf = ld16(xr + ks * KG);
 #pragma unroll
-      for (int ks = 0; ks < KZM; ++ks) ag = mma16(ag, wgr[ks], ld16(zr + ks * KG), T());
+        for (int jj = 0; jj < UPW; ++jj) ap[jj] = mma16(ap[jj], wor[jj][ks], xf, T());
+      }
+#pragma unroll
+      for (int ks = 0; ks < KZM; ++ks) {
+        const chunk_t zf = ld16(zr + ks * KG);
+#pragma unroll
+        for (int jj = 0; jj < UPW; ++jj) ag[jj] = mma16(ag[jj], wgr[jj][ks], zf, T());
+      }
       const int j = j0 + pr;
-      if (uok && j < n) {
-        const float m = mv[pr];
-        T* dst = out + (((size_t)bb * n + i) * n + j) * cz + oc0;
-        store4(dst, gate_mul(ap[0] * m, ag[0]), gate_mul(ap[1] * m, ag[1]),
-               gate_mul(ap[2] * m, ag[2]), gate_mul(ap[3] * m, ag[3]));
+      const float m = mv[pr];
+#pragma unroll
+      for (int jj = 0; jj < UPW; ++jj) {
+        if (uok[jj] && j < n) {
+          T* dst = out + (((size_t)bb * n + i) * n + j) * cz + oc0[jj];
+          store4(dst, gate_mul(ap[jj][0] * m, ag[jj][0]), gate_mul(ap[jj][1] * m, ag[jj][1]),
+                 gate_mul(ap[jj][2] * m, ag[jj][2]), gate_mul(ap[jj][3] * m, ag[jj][3]));
+        }
       }
     }
-    stage(cur ^ 1, pre);
+    if (nbuf == 1) __syncthreads();  // every wave is done reading the single buffer
+    stage(nxt, pre);
     __syncthreads();
-    norm_x(cur ^ 1);
+    norm_x(nxt);
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------------------
 
-template <class T, int KXM, int KZM>
+template <class T, int KXM, int KZM, int XB>
 static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
   constexpr int E = Traits<T>::E;
-  const size_t lds = 2 * (size_t)K3_TP * ((a.cp + E) + (a.czp + E)) * sizeof(T) +
-                     2 * K3_TP * sizeof(float);
-  auto fn = k3_output_gate<T, KXM, KZM>;
+  auto lds_for = [&](int nb) {
+    return (size_t)nb * K3_TP * ((a.cp + E) + (a.czp + E)) * sizeof(T) +
+           (size_t)nb * K3_TP * sizeof(float);
+  };
+  const int nbuf = lds_for(2) <= K3_LDS_BUDGET ? 2 : 1;
+  const size_t lds = lds_for(nbuf);
+  auto fn = k3_output_gate<T, KXM, KZM, XB>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
   if (e != hipSuccess) return e;
   const int units = a.cz / 16;
-  const int groups = (units + K3_WAVES - 1) / K3_WAVES;
+  const int groups = (units + K3_WAVES * K3_UPW - 1) / (K3_WAVES * K3_UPW);
   const int total = a.batch * a.n * ((a.n + K3_TP - 1) / K3_TP);
   static std::atomic<int> occ{0};
   static std::atomic<size_t> occ_lds{0};
@@ -228,7 +269,7 @@ static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
   hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K3_THREADS), lds, st, (const T*)a.x,
                      (const T*)a.z, (const T*)(mask_all ? a.one : a.mask), (T*)a.out,
                      (const T*)a.wo, a.to, (const T*)a.wg, a.tg, a.n, a.np, a.cz, a.czp, a.c, a.cp,
-                     mask_all, total);
+                     mask_all, nbuf, total);
   return hipGetLastError();
 }
 
@@ -236,9 +277,16 @@ static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
 // pads cp and czp to exactly one of them.
 template <class T>
 static hipError_t launch_k3_dispatch(const StageArgs& a, hipStream_t st) {
+  constexpr int E = Traits<T>::E;
   const int kx = a.cp / Traits<T>::KG, kz = a.czp / Traits<T>::KG;
-#define TRIMUL_CALL(X_, Z_) \
-  if (kx == X_ && kz == Z_) return launch_k3_t<T, X_, Z_>(a, st);
+  const int xblocks = (a.c / E) * (K3_TP / E);
+  const int xb = (xblocks + K3_THREADS - 1) / K3_THREADS;
+  // a second x block per thread is needed only for wide c (KX >= 8 after padding)
+#define TRIMUL_CALL(X_, Z_)                                      \
+  if (kx == X_ && kz == Z_) {                                    \
+    if (xb == 1) return launch_k3_t<T, X_, Z_, 1>(a, st);        \
+    if (X_ >= 8 && xb == 2) return launch_k3_t<T, X_, Z_, (X_ >= 8 ? 2 : 1)>(a, st); \
+  }
   TRIMUL_K3_VARIANTS(TRIMUL_CALL)
 #undef TRIMUL_CALL
   return hipErrorInvalidValue;

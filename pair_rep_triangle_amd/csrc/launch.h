@@ -33,6 +33,7 @@ struct StageArgs {
 inline int k_group(bool bf16_storage) { return bf16_storage ? 32 : 16; }
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
 constexpr int N_PAD = 128;  // side padding of a, b, x (the contraction tile)
+constexpr size_t LDS_PER_CU = 160 * 1024;  // gfx950 LDS per CU (the most one workgroup may use)
 
 // The projection kernels keep their weights in registers, sized at compile time by the
 // number of chunk groups along k. The output kernel is compiled for these (KX, KZ) pairs

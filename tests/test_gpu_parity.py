@@ -91,6 +91,23 @@ def test_ragged_full_output(batch, n, c_z, c, mask, direction, dtype):
     check_full(d, dtype, direction)
 
 
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("batch,n,c_z,c,mask", [
+    (1, 70, 64, 512, "random_pairs"), (1, 50, 384, 256, "block"), (2, 33, 512, 384, "ones"),
+])
+def test_wide_bf16_full_output(batch, n, c_z, c, mask, direction):
+    note(f"wide bf16 B={batch} n={n} cz={c_z} c={c} {mask} {direction}")
+    d = make_random(batch, n, c_z, c, seed=n + c, mask=mask, random_affine=True)
+    check_full(d, "bf16", direction)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_widest_fp32_full_output(direction):
+    note(f"widest fp32 {direction}")
+    d = make_random(1, 45, 256, 128, seed=77, mask="random_pairs", random_affine=True)
+    check_full(d, "fp32", direction)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_null_mask_means_all_ones(dtype):
     d = make_random(1, 40, 32, 32, seed=5, mask="ones")
