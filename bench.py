@@ -6,7 +6,8 @@ contraction, output gate) on one seeded synthetic batch resident in HBM.
 Prints ONE JSON line:
   value         TFLOP/s over the step (matmul flops of both directions)
   roofline      the dominant kernel's algorithmic GB/s (or TFLOP/s) against the
-                MI355X peak, from HIP events around that kernel in the timed region
+                MI355X peak; its duration from HIP events recorded after every
+                kernel in a second timed region of K steps
   cpu_baseline  the fp64 oracle timed on this host (rank 0, N=1 only)
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
@@ -23,7 +24,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "triangle-mult-update TFLOP/s & pair-updates/s at N=512,c_z=128 bf16 (1 GPU)"
 KERNELS = ("k1_input_gate", "k2_contract", "k3_output_gate")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 
 
 def parse():
@@ -35,26 +36,29 @@ def parse():
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
-                   help="time whole steps only (no events between the kernels)")
+                   help="time whole steps only (skip the per-kernel timed region)")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run a plain device-to-device copy of this many MiB three times "
                         "(reference kernel for scaling HBM byte counters)")
     return p.parse_args()
 
 
-def cpu_baseline(d, directions, threads):
-    """The fp64 oracle as it stands, on the same workload, both directions."""
-    import numpy as np
+def cpu_baseline(d, directions, threads, min_seconds=10.0, max_reps=8):
+    """The fp64 oracle as it stands, on the same workload, both directions, repeated
+    until about `min_seconds` of CPU time has passed. Returns (seconds per pass, passes)."""
     import torch
     from threadpoolctl import threadpool_limits
     from oracle import tri_mul_ref
     z = torch.from_numpy(d["z"]).to(torch.bfloat16).to(torch.float64).numpy()
+    reps, total = 0, 0.0
     with threadpool_limits(limits=threads):
-        t0 = time.perf_counter()
-        for direction, w in directions:
-            tri_mul_ref(z, d["mask"], w, direction)
-        dt = time.perf_counter() - t0
-    return dt
+        while reps < max_reps and (reps == 0 or total < min_seconds):
+            t0 = time.perf_counter()
+            for direction, w in directions:
+                tri_mul_ref(z, d["mask"], w, direction)
+            total += time.perf_counter() - t0
+            reps += 1
+    return total / reps, reps
 
 
 def main():
@@ -87,16 +91,9 @@ def main():
     outs = [torch.empty_like(z) for _ in mods]
     stream = torch.cuda.current_stream(dev)
 
-    def step(events=None):
-        k = 0
+    def step():
         for (direction, mod), out in zip(mods, outs):
-            if events is None:
-                mod.forward(z, mask, out=out, direction=direction, workspace=ws)
-                continue
-            for s in (1, 2, 3):
-                mod.stage(s, z, mask, out=out, direction=direction, workspace=ws)
-                events[k + 1].record(stream)
-                k += 1
+            mod.forward(z, mask, out=out, direction=direction, workspace=ws)
 
     for _ in range(args.warmup):
         step()
@@ -111,24 +108,40 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    use_ev = not args.no_kernel_events
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+    # timed region 1: K whole steps (outgoing + incoming), HIP events on the launch stream
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
-    for k in range(args.steps):
-        if use_ev:
-            evs[k][0].record(stream)
-            step(evs[k])
-        else:
-            step()
+    for _ in range(args.steps):
+        step()
     t_end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     ms_step = total_ms / args.steps
+
+    # timed region 2: the same K steps again with a HIP event after every kernel (on the
+    # launch stream), for each kernel's duration inside the real K1 -> K2 -> K3 order.
+    # Kept apart from region 1 because every event adds a marker packet to the stream.
+    per_kernel_ms = {}
+    if not args.no_kernel_events:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+        for k in range(args.steps):
+            evs[k][0].record(stream)
+            e = 1
+            for (direction, mod), out in zip(mods, outs):
+                for s_idx in (1, 2, 3):
+                    mod.stage(s_idx, z, mask, out=out, direction=direction, workspace=ws)
+                    evs[k][e].record(stream)
+                    e += 1
+        torch.cuda.synchronize()
+        per = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(6)]
+                        for k in range(args.steps)])
+        for idx, kname in enumerate(KERNELS):
+            samples = np.concatenate([per[:, idx], per[:, idx + 3]])  # both directions
+            per_kernel_ms[kname] = (float(samples.mean()), float(np.median(samples)))
 
     pairs = B * n * n
     fl_dir = flops_per_pair(n, c_z, c) * pairs
@@ -137,40 +150,26 @@ def main():
 
     work = kernel_work(n, c_z, c, esz)
     kernels = {}
-    if use_ev:
-        per = np.zeros((args.steps, 6))
-        for k in range(args.steps):
-            for j in range(6):
-                per[k, j] = evs[k][j].elapsed_time(evs[k][j + 1])
-        for idx, kname in enumerate(KERNELS):
-            samples = np.concatenate([per[:, idx], per[:, idx + 3]])  # both directions
-            avg_ms = float(samples.mean())
-            wk = work[kname]
-            gbps = wk["bytes"] * pairs / (avg_ms * 1e-3) / 1e9
-            tfl = wk["flops"] * pairs / (avg_ms * 1e-3) / 1e12
-            ai = wk["flops"] / wk["bytes"]
-            peak_fl = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
-            ridge = peak_fl * 1e12 / (MI355X_PEAK["hbm_GBps"] * 1e9)
-            bound = "hbm" if ai < ridge else "mfma"
-            kernels[kname] = {
-                "avg_us": round(avg_ms * 1e3, 3), "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1),
-                "hbm_frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4),
-                "mfma_frac": round(tfl / peak_fl, 4), "bound": bound,
-                "bytes_per_launch": wk["bytes"] * pairs, "flops_per_launch": wk["flops"] * pairs,
-            }
+    for kname, (avg_ms, med_ms) in per_kernel_ms.items():
+        wk = work[kname]
+        gbps = wk["bytes"] * pairs / (avg_ms * 1e-3) / 1e9
+        tfl = wk["flops"] * pairs / (avg_ms * 1e-3) / 1e12
+        ai = wk["flops"] / wk["bytes"]
+        peak_fl = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+        ridge = peak_fl * 1e12 / (MI355X_PEAK["hbm_GBps"] * 1e9)
+        bound = "hbm" if ai < ridge else "mfma"
+        kernels[kname] = {
+            "avg_us": round(avg_ms * 1e3, 3), "median_us": round(med_ms * 1e3, 3), "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1),
+            "hbm_frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4),
+            "mfma_frac": round(tfl / peak_fl, 4), "bound": bound,
+            "bytes_per_launch": wk["bytes"] * pairs, "flops_per_launch": wk["flops"] * pairs,
+        }
 
     roofline = None
     if kernels:
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         kd = kernels[dom]
-        traffic = None
-        try:
-            with open(TRAFFIC_FILE) as f:
-                tr = json.load(f).get(name, {}).get(dom)
-            if tr and tr.get("source_sha") == _kernel_source_sha():
-                traffic = tr.get("bytes_per_launch")
-        except (OSError, ValueError):
-            traffic = None
+        traffic = measured_traffic(name, dom)
         if kd["bound"] == "hbm":
             roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GBps"],
                         "peak": MI355X_PEAK["hbm_GBps"], "unit": "GB/s",
@@ -183,11 +182,12 @@ def main():
     cpu = None
     if not args.no_cpu_baseline:
         threads = min(16, len(os.sched_getaffinity(0)))
-        dt = cpu_baseline(d, [("outgoing", w_out), ("incoming", w_in)], threads)
+        dt, reps = cpu_baseline(d, [("outgoing", w_out), ("incoming", w_in)], threads)
         cpu = {"value": round(2 * fl_dir / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-               "kind": "oracle", "seconds": round(dt, 2),
+               "kind": "oracle", "seconds_per_pass": round(dt, 2),
                "pair_updates_per_s": round(2 * pairs / dt, 1),
-               "sample": f"whole workload {name}, outgoing + incoming, fp64 NumPy oracle"}
+               "sample": f"whole workload {name}, outgoing + incoming, fp64 NumPy oracle "
+                         f"(BLAS on {threads} threads), {reps} passes averaged"}
 
     rec = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -206,12 +206,21 @@ def main():
     print(json.dumps(rec), flush=True)
 
 
-def _kernel_source_sha():
-    import hashlib
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "pair_rep_triangle_amd", "csrc", "kernels.hip"), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+def measured_traffic(workload, kernel):
+    """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE table,
+    or None when there is no row or the kernel source changed since it was taken."""
+    from pair_rep_triangle_amd.profile_summary import source_sha
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for line in f:
+                cells = [c.strip() for c in line.strip().strip("|").split("|")]
+                if len(cells) == 6 and cells[0] == workload and cells[1] == kernel:
+                    if cells[2] != source_sha(kernel):
+                        return None
+                    return int(float(cells[5]))
+    except OSError:
+        return None
+    return None
 
 
 if __name__ == "__main__":

@@ -13,7 +13,8 @@ constexpr int NTHREADS = 256;
 
 // k2: x[bc] = A[bc] B[bc]^T for every (batch, channel) bc; A, B, x are [np][np].
 // 128 x 128 output tile per workgroup, 4 waves as 2 x 2, each 64 x 64 (2 x 2 MFMA
-// 32x32 tiles). k advances 128 bytes per stage through a double-buffered LDS.
+// 32x32 tiles). k advances 128 bytes per stage through a double-buffered LDS, with two
+// stages of global loads in flight.
 // Flat grid of (np/128)^2 * batch*c workgroups, remapped so that consecutive tiles
 // of one channel land on the same XCD (workgroup ids are dealt round-robin over the
 // 8 XCDs) and share its L2.
@@ -44,21 +45,25 @@ __global__ __launch_bounds__(NTHREADS) void k2_contract(const T* __restrict__ A,
   const T* Ab = A + bc * mat + (size_t)ti * K2_TILE * np;
   const T* Bb = B + bc * mat + (size_t)tj * K2_TILE * np;
 
-  chunk_t ra[4], rb[4];
-  auto gload = [&](int k0) {
+  // Global -> registers -> LDS, two stages in flight: the loads of stage s+2 are issued
+  // before stage s is computed and land in LDS after it, so two stages of MFMA work cover
+  // the memory latency. The two register sets alternate (the loop is unrolled by two so
+  // that every register index is static).
+  chunk_t ra[2][4], rb[2][4];
+  auto gload = [&](int set, int k0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + NTHREADS * q, row = idx >> 3, c16 = idx & 7;
-      ra[q] = ld16(Ab + (size_t)row * np + k0 + c16 * E);
-      rb[q] = ld16(Bb + (size_t)row * np + k0 + c16 * E);
+      ra[set][q] = ld16(Ab + (size_t)row * np + k0 + c16 * E);
+      rb[set][q] = ld16(Bb + (size_t)row * np + k0 + c16 * E);
     }
   };
-  auto lstore = [&](int buf) {
+  auto lstore = [&](int buf, int set) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int idx = tid + NTHREADS * q, row = idx >> 3, c16 = idx & 7;
-      st16(&lds[buf][0][row * LROW + c16 * E], ra[q]);
-      st16(&lds[buf][1][row * LROW + c16 * E], rb[q]);
+      st16(&lds[buf][0][row * LROW + c16 * E], ra[set][q]);
+      st16(&lds[buf][1][row * LROW + c16 * E], rb[set][q]);
     }
   };
 
@@ -70,13 +75,7 @@ __global__ __launch_bounds__(NTHREADS) void k2_contract(const T* __restrict__ A,
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  const int nst = np / KT;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int s = 0; s < nst; ++s) {
-    const int cur = s & 1;
-    if (s + 1 < nst) gload((s + 1) * KT);
+  auto compute = [&](int cur) {
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
       const int koff = (2 * kk + (lane >> 5)) * E;
@@ -94,7 +93,24 @@ __global__ __launch_bounds__(NTHREADS) void k2_contract(const T* __restrict__ A,
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32(acc[mt][nt], fb[nt], fa[mt], T());
     }
-    if (s + 1 < nst) lstore(cur ^ 1);
+  };
+
+  // stage s lives in LDS buffer s % 2 and (while in flight) register set s % 2
+  const int nst = np / KT;  // even: np is a multiple of 128 and KT is 64 or 32
+  gload(0, 0);
+  gload(1, KT);
+  lstore(0, 0);
+  __syncthreads();
+  for (int s = 0; s < nst; s += 2) {
+    // even stage s: buffer 0 holds it, set 1 holds s+1, set 0 is free
+    if (s + 2 < nst) gload(0, (s + 2) * KT);
+    compute(0);
+    lstore(1, 1);  // stage s+1 always exists (nst even)
+    __syncthreads();
+    // odd stage s+1: buffer 1 holds it, set 0 holds s+2 (if any), set 1 is free
+    if (s + 3 < nst) gload(1, (s + 3) * KT);
+    compute(1);
+    if (s + 2 < nst) lstore(0, 0);
     __syncthreads();
   }
 
