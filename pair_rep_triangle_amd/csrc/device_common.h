@@ -179,6 +179,88 @@ __device__ __forceinline__ void normalize_row_stats(const chunk_t (&v)[NCH], int
   rstd = rsqrtf(group_sum<G>(q) * inv_w + TRI_MUL_LN_EPS_F);
 }
 
+// Value of `v` from lane `src` of the wave (LDS permute network; no LDS storage).
+__device__ __forceinline__ float lane_value(float v, int src) {
+  return __int_as_float(__builtin_amdgcn_ds_bpermute(src << 2, __float_as_int(v)));
+}
+// Sum over the lanes l, l^16, l^32, l^48 (the four lane groups of an MFMA operand row).
+__device__ __forceinline__ float row_groups_sum(float v, int lane) {
+  v += lane_value(v, lane ^ 16);
+  v += lane_value(v, lane ^ 32);
+  return v;
+}
+
+// acc + lo(a)*lo(b) + hi(a)*hi(b) for two bf16 pairs, fp32 accumulation (the products are
+// exact in fp32). Written as an instruction: the compiler's own route to the packed bf16
+// dot product has fed every unrolled copy the same source register.
+__device__ __forceinline__ float dot2_bf16(unsigned int a, unsigned int b, float acc) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(acc));
+  return d;
+}
+
+// LayerNorm of one pair's row held in MFMA operand layout: lane (p, q) = (lane%16,
+// lane/16) holds chunk ks of the row at element ks*KG + q*E, for ks < KM; the four lanes
+// p, p+16, p+32, p+48 hold the whole row. Chunks at or beyond `width` must be zero on entry
+// (they add nothing to the sums); every chunk becomes (x - mean) * rstd, so padding chunks
+// come out as the finite value -mean*rstd, which the zero weight columns of the padding
+// cancel. No branch on the chunk index: the normalisation stays one straight-line block.
+// bf16: one fp32 pass for sum and sum of squares (packed bf16 dot products); fp32: two
+// passes, the second one masked to the real chunks.
+template <int KM>
+__device__ __forceinline__ void normalize_operand_row(chunk_t (&v)[KM], int width, int lane, bf16) {
+  constexpr unsigned int kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
+  float s = 0.f, q = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KM; ++ks)
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      s = dot2_bf16(v[ks][d], kOnes, s);
+      q = dot2_bf16(v[ks][d], v[ks][d], q);
+    }
+  const float inv_w = 1.0f / (float)width;
+  const float mean = row_groups_sum(s, lane) * inv_w;
+  const float var = row_groups_sum(q, lane) * inv_w - mean * mean;
+  const float rstd = rsqrtf(fmaxf(var, 0.f) + TRI_MUL_LN_EPS_F);
+  const float shift = -mean * rstd;
+#pragma unroll
+  for (int ks = 0; ks < KM; ++ks) {
+    float f[8];
+    unpack(v[ks], f, bf16());
+#pragma unroll
+    for (int e = 0; e < 8; ++e) f[e] = fmaf(f[e], rstd, shift);
+    v[ks] = pack(f, bf16());
+  }
+}
+template <int KM>
+__device__ __forceinline__ void normalize_operand_row(chunk_t (&v)[KM], int width, int lane, float) {
+  const int q0 = (lane >> 4) * 4;
+  float s = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KM; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) s += __uint_as_float(v[ks][e]);
+  const float inv_w = 1.0f / (float)width;
+  const float mean = row_groups_sum(s, lane) * inv_w;
+  float q = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KM; ++ks) {
+    const float keep = ks * 16 + q0 < width ? 1.f : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float d = (__uint_as_float(v[ks][e]) - mean) * keep;
+      q = fmaf(d, d, q);
+    }
+  }
+  const float rstd = rsqrtf(row_groups_sum(q, lane) * inv_w + TRI_MUL_LN_EPS_F);
+  const float shift = -mean * rstd;
+#pragma unroll
+  for (int ks = 0; ks < KM; ++ks)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      v[ks][e] = __float_as_uint(fmaf(__uint_as_float(v[ks][e]), rstd, shift));
+}
+
 template <class T, int NCH, int G>
 __device__ __forceinline__ void normalize_row(chunk_t (&v)[NCH], int part, int nreal, int width) {
   constexpr int E = Traits<T>::E;

@@ -16,6 +16,8 @@
 // beta terms start the accumulators; the gate rows carry -log2(e) (host side). The next
 // tile's x and z are fetched into registers while the current tile's MFMAs run.
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace trimul {
@@ -243,6 +245,367 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
 }
 
 // ---------------------------------------------------------------------------------------
+// Wave-independent form (used whenever the weight slice and the per-wave staging fit
+// LDS). Workgroup = 8 waves; blockIdx.y selects a group of `ug` output units (16 output
+// channels each) whose W_o and W_g rows and start vectors are copied into LDS once. Every
+// wave then runs its own persistent loop over wave tiles of TW = 16*ST consecutive pairs
+// (i, j0 .. j0+TW-1), with no workgroup barrier:
+//   - x arrives channel-major; E x E blocks (E channels x E pairs, one 16-byte load per
+//     channel) are transposed in registers and written pair-major into the wave's LDS
+//     staging rows, then read back in MFMA operand layout; z is loaded straight from
+//     global memory in operand layout (lane (p, q) = (lane%16, lane/16) holds elements
+//     ks*KG + q*E .. of pair p);
+//   - both LayerNorms run on the operand registers (the four lanes of a pair reduce
+//     through the lane permute network);
+//   - per unit: W_o / W_g rows from LDS are the A operand, xhat / zhat the B operand, the
+//     start vectors initialise the accumulators, and m * p / (1 + 2^g2) goes to the
+//     staging rows (the same LDS, free again once the x operands are in registers);
+//   - the staged rows leave as whole 16-byte chunks of the group's channel range of
+//     each pair: consecutive pairs are consecutive lines of `out`.
+// The next tile's x blocks, z chunks and mask values are loaded while the current one is
+// computed.
+template <class T, int KXM, int KZM, int ST, int UGM, int W, int XBC>
+__global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
+    const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ mask,
+    T* __restrict__ out, const T* __restrict__ wo, const float* __restrict__ to,
+    const T* __restrict__ wg, const float* __restrict__ tg, int n, int np, int cz, int czp, int c,
+    int cp, int mask_all, int ug, int total_tiles) {
+  constexpr int E = Traits<T>::E;
+  constexpr int KG = Traits<T>::KG;
+  constexpr int THREADS = 64 * W;
+  constexpr int TW = 16 * ST;        // pairs per wave tile
+  constexpr int PO = TW / E;         // E-pair column blocks per wave tile
+  // x moves in blocks of XBC channels x E pairs (XBC loads of 16 bytes per block)
+  constexpr int XBM = (KXM * (KG / XBC) * PO + 63) / 64;  // x blocks per lane (at most)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+  const int gch = ug * 16;           // output channels of this group
+  const int ch0 = blockIdx.y * gch;  // its first output channel
+  const int wos = cp + E, wgs = czp + E;
+  const int sst = (cp > gch ? cp : gch) + E;  // staging row stride (elements)
+  T* const wo_s = (T*)smem;                   // [gch][wos]
+  T* const wg_s = wo_s + gch * wos;           // [gch][wgs]
+  float* const to_s = (float*)(wg_s + gch * wgs);
+  float* const tg_s = to_s + gch;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  T* const stg = (T*)(tg_s + gch) + wave * TW * sst;  // [TW][sst]
+  const int p = lane & 15, q = lane >> 4;
+
+  // ---- this group's weight rows and start vectors -> LDS ----
+  // All loads of a thread are issued before any LDS store (one memory round trip, not one
+  // per chunk): the trip counts are compile-time bounds with the real extents as guards.
+  {
+    constexpr int WCX = KXM * KG / E, WCZ = KZM * KG / E;  // chunks per weight row
+    constexpr int NWO = (UGM * 16 * WCX + THREADS - 1) / THREADS;
+    constexpr int NWG = (UGM * 16 * WCZ + THREADS - 1) / THREADS;
+    chunk_t vo[NWO], vg[NWG];
+#pragma unroll
+    for (int k = 0; k < NWO; ++k) {
+      const int idx = tid + THREADS * k, r = idx / WCX, cc = idx - r * WCX;
+      const int rr = r < gch ? r : 0;
+      vo[k] = ld16(wo + (size_t)(ch0 + rr) * cp + cc * E);
+    }
+#pragma unroll
+    for (int k = 0; k < NWG; ++k) {
+      const int idx = tid + THREADS * k, r = idx / WCZ, cc = idx - r * WCZ;
+      const int rr = r < gch ? r : 0;
+      vg[k] = ld16(wg + (size_t)(ch0 + rr) * czp + cc * E);
+    }
+    const float vto = tid < gch ? to[ch0 + tid] : 0.f, vtg = tid < gch ? tg[ch0 + tid] : 0.f;
+#pragma unroll
+    for (int k = 0; k < NWO; ++k) {
+      const int idx = tid + THREADS * k, r = idx / WCX, cc = idx - r * WCX;
+      if (r < gch) st16(wo_s + r * wos + cc * E, vo[k]);
+    }
+#pragma unroll
+    for (int k = 0; k < NWG; ++k) {
+      const int idx = tid + THREADS * k, r = idx / WCZ, cc = idx - r * WCZ;
+      if (r < gch) st16(wg_s + r * wgs + cc * E, vg[k]);
+    }
+    if (tid < gch) {
+      to_s[tid] = vto;
+      tg_s[tid] = vtg;
+    }
+  }
+  __syncthreads();
+
+  const int ntw = (n + TW - 1) / TW;
+  const int cbn = c / XBC;          // XBC-channel blocks of x
+  const int xblocks = cbn * PO;     // blocks per wave tile
+  const size_t plane = (size_t)np * np;
+
+  struct Pre {
+    chunk_t xv[XBM][XBC];
+    chunk_t zv[ST][KZM];
+    T m[ST];
+  };
+  // unconditional loads from clamped in-bounds addresses; selects happen at use
+  auto fetch = [&](int t, Pre& f) {
+    t = t < total_tiles ? t : total_tiles - 1;  // waves without a tile fetch the last one
+    const int bb = t / (n * ntw);
+    const int rem = t - bb * n * ntw;
+    const int i = rem / ntw, j0 = (rem - i * ntw) * TW;
+#pragma unroll
+    for (int k = 0; k < XBM; ++k) {
+      const int blk = lane + 64 * k;
+      const int bl = blk < xblocks ? blk : 0;
+      const int o = bl / cbn, cb = bl - o * cbn;
+      const T* src = x + ((size_t)bb * c + cb * XBC) * plane + (size_t)i * np + j0 + o * E;
+#pragma unroll
+      for (int e = 0; e < XBC; ++e) f.xv[k][e] = ld16(src + e * plane);
+    }
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int j = j0 + st * 16 + p;
+      const size_t pair = ((size_t)bb * n + i) * n + (j < n ? j : n - 1);
+#pragma unroll
+      for (int ks = 0; ks < KZM; ++ks) {
+        const int ch = ks * KG + q * E;
+        f.zv[st][ks] = ld16(z + pair * cz + (ch < cz ? ch : 0));
+      }
+      f.m[st] = mask[mask_all ? 0 : pair];
+    }
+  };
+
+  const int gw = blockIdx.x * W + wave;
+  const int nw = gridDim.x * W;
+  int t = gw;
+  Pre f;
+  fetch(t, f);
+  for (; t < total_tiles; t += nw) {
+    const int bb = t / (n * ntw);
+    const int rem = t - bb * n * ntw;
+    const int i = rem / ntw, j0 = (rem - i * ntw) * TW;
+
+    // x: transpose the XBC x E blocks into pair-major staging rows. Every lane stores (no
+    // predicated-off memory operations in the loop): a lane without a block writes its
+    // junk into the last E columns of the rows, which nothing reads.
+#pragma unroll
+    for (int k = 0; k < XBM; ++k) {
+      const int blk = lane + 64 * k;
+      const bool real = blk < xblocks;
+      const int bl = real ? blk : 0;
+      const int o = bl / cbn, cb = bl - o * cbn;
+      const int col0 = real ? cb * XBC : sst - E;
+      T tb[XBC][E];
+#pragma unroll
+      for (int e = 0; e < XBC; ++e) {
+        const T* pv = (const T*)&f.xv[k][e];
+#pragma unroll
+        for (int ff = 0; ff < E; ++ff) tb[e][ff] = pv[ff];
+      }
+#pragma unroll
+      for (int ff = 0; ff < E; ++ff) {
+        if constexpr (XBC == E) {
+          T col[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) col[e] = tb[e][ff];
+          st16(stg + (o * E + ff) * sst + col0, __builtin_bit_cast(chunk_t, col));
+        } else {
+          static_assert(XBC * 2 == E, "half-width x blocks");
+          T col[XBC];
+#pragma unroll
+          for (int e = 0; e < XBC; ++e) col[e] = tb[e][ff];
+          *(half_t*)(stg + (o * E + ff) * sst + col0) = __builtin_bit_cast(half_t, col);
+        }
+      }
+    }
+    // The weight and start-vector addresses and the padding masks are the same in every
+    // tile; an opaque zero, produced anew each tile, keeps the compiler from hoisting them
+    // out of the tile loop (which would pin all of them in registers for the whole launch).
+    int opaque;
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+    chunk_t bx[ST][KXM], bz[ST][KZM];
+    float mrow[ST];
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+#pragma unroll
+      for (int ks = 0; ks < KZM; ++ks) bz[st][ks] = f.zv[st][ks];
+      mrow[st] = j0 + st * 16 + p < n ? to_f32(f.m[st]) : 0.f;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int st = 0; st < ST; ++st)
+#pragma unroll
+      for (int ks = 0; ks < KXM; ++ks) bx[st][ks] = ld16(stg + (st * 16 + p) * sst + ks * KG + q * E);
+    // widths that do not fill the compiled chunk count: zero the chunks past the real
+    // channels (a wave-uniform branch, not taken at full width)
+    if (c < cp || cz < czp) {
+      const int ch0q = q * E + opaque;
+#pragma unroll
+      for (int ks = 0; ks < KXM; ++ks) {
+        const unsigned int kx = ks * KG + ch0q < c ? ~0u : 0u;
+#pragma unroll
+        for (int st = 0; st < ST; ++st) bx[st][ks] &= kx;
+      }
+#pragma unroll
+      for (int ks = 0; ks < KZM; ++ks) {
+        const unsigned int kz = ks * KG + ch0q < cz ? ~0u : 0u;
+#pragma unroll
+        for (int st = 0; st < ST; ++st) bz[st][ks] &= kz;
+      }
+    }
+
+    // the next tile's loads are in flight from here on (the last tile refetches itself)
+    fetch(t + nw < total_tiles ? t + nw : t, f);
+
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      normalize_operand_row<KXM>(bx[st], c, lane, T());
+      normalize_operand_row<KZM>(bz[st], cz, lane, T());
+    }
+
+    // units of this group (a rolled loop: unrolled, the scheduler overlaps the units' LDS
+    // reads beyond the register budget). Tiles whose pairs all have mask 1 skip the
+    // multiply by m (a wave-uniform branch).
+    const T* const wo_t = wo_s + opaque;
+    const T* const wg_t = wg_s + opaque;
+    const float* const to_t = to_s + opaque;
+    const float* const tg_t = tg_s + opaque;
+    auto units = [&](auto masked) {
+      constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll 1
+      for (int u = 0; u < ug; ++u) {
+        {
+          const int r0 = u * 16;
+          const f32x4 bo4 = ld16f(to_t + r0 + 4 * q), bg4 = ld16f(tg_t + r0 + 4 * q);
+          f32x4 ap[ST], ag[ST];
+#pragma unroll
+          for (int st = 0; st < ST; ++st) {
+            ap[st] = bo4;
+            ag[st] = bg4;
+          }
+          // all of the unit's weight chunks are requested before the first MFMA, so the
+          // LDS latency is paid once per unit rather than once per chunk
+          const T* wor = wo_t + (r0 + p) * wos + q * E;
+          const T* wgr = wg_t + (r0 + p) * wgs + q * E;
+          chunk_t wa[KXM], wb[KZM];
+#pragma unroll
+          for (int ks = 0; ks < KXM; ++ks) wa[ks] = ld16(wor + ks * KG);
+#pragma unroll
+          for (int ks = 0; ks < KZM; ++ks) wb[ks] = ld16(wgr + ks * KG);
+#pragma unroll
+          for (int ks = 0; ks < KXM; ++ks)
+#pragma unroll
+            for (int st = 0; st < ST; ++st) ap[st] = mma16(ap[st], wa[ks], bx[st][ks], T());
+#pragma unroll
+          for (int ks = 0; ks < KZM; ++ks)
+#pragma unroll
+            for (int st = 0; st < ST; ++st) ag[st] = mma16(ag[st], wb[ks], bz[st][ks], T());
+          // accumulator register r <-> output channel ch0 + r0 + 4q + r of pair st*16 + p
+#pragma unroll
+          for (int st = 0; st < ST; ++st) {
+            float o4[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              o4[r] = gate_mul(MASKED ? ap[st][r] * mrow[st] : ap[st][r], ag[st][r]);
+            store4(stg + (st * 16 + p) * sst + r0 + 4 * q, o4[0], o4[1], o4[2], o4[3]);
+          }
+        }
+      }
+    };
+    bool ones = true;
+#pragma unroll
+    for (int st = 0; st < ST; ++st) ones = ones && mrow[st] == 1.f;
+    if (__all(ones))
+      units(std::false_type());
+    else
+      units(std::true_type());
+
+    // staging -> out: the group's channel range of TW consecutive pairs. The number of
+    // stores is fixed and none is predicated off: a lane whose chunk lies past the row end
+    // (or past the group's channels) rewrites the last real chunk with the same bytes.
+    // With an unconditional store count the wait for the next tile's loads does not have
+    // to wait for these stores as well.
+    wave_lds_sync();
+    constexpr int CPPM = UGM * 16 / E;  // chunks per staged row, at most
+    const int cpp = gch / E;
+    const int last = n - 1 - j0;        // last real pair of the tile (< TW when ragged)
+    const size_t row0 = ((size_t)bb * n + i) * n + j0;
+#pragma unroll
+    for (int k = 0; k < (TW * CPPM + 63) / 64; ++k) {
+      const int idx = k * 64 + lane;
+      int pr = idx / CPPM, cc = idx - pr * CPPM;
+      pr = pr < last ? pr : last;
+      pr = pr < TW ? pr : TW - 1;
+      cc = cc < cpp ? cc : cpp - 1;
+      st16(out + (row0 + pr) * cz + ch0 + cc * E, ld16(stg + pr * sst + cc * E));
+    }
+  }
+}
+
+// Shapes of the wave-independent form. Narrow rows (KXM + KZM <= 8 chunk groups): 16
+// pairs per wave tile, 16 waves per workgroup (four per SIMD, so up to 128 VGPRs each) and
+// half-width x blocks; wider rows: 16 pairs, 8 waves, full-width blocks, if the operands and
+// the next tile's loads fit the register budget.
+template <class T, int KXM, int KZM>
+struct K3WShape {
+  static constexpr int E = Traits<T>::E;
+  static constexpr bool NARROW = KXM + KZM <= 8;
+  static constexpr int ST = 1;
+  static constexpr int W = NARROW ? 16 : 8;
+  static constexpr int XBC = NARROW ? E / 2 : E;
+  static constexpr int XBM = (KXM * (Traits<T>::KG / XBC) * (16 * ST / E) + 63) / 64;
+  static constexpr int VGPRS = 4 * (ST * (KXM + KZM) + XBM * XBC + ST * KZM);
+  static constexpr bool OK = VGPRS <= (NARROW ? 96 : 160);
+  static constexpr int UGM = KZM * Traits<T>::KG / 16 < 8 ? KZM * Traits<T>::KG / 16 : 8;
+};
+
+template <class T>
+static size_t k3w_lds(const StageArgs& a, int ug, int st, int waves) {
+  constexpr int E = Traits<T>::E;
+  const int gch = ug * 16;
+  const int sst = (a.cp > gch ? a.cp : gch) + E;
+  return (size_t)gch * ((a.cp + E) + (a.czp + E)) * sizeof(T) + 2 * (size_t)gch * sizeof(float) +
+         (size_t)waves * 16 * st * sst * sizeof(T);
+}
+
+// Launches the wave-independent form if some unit grouping fits LDS; *done = false leaves
+// the launch to the tile-shared form.
+template <class T, int KXM, int KZM>
+static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
+  *done = false;
+  if constexpr (K3WShape<T, KXM, KZM>::OK) {
+    constexpr int ST = K3WShape<T, KXM, KZM>::ST;
+    constexpr int W = K3WShape<T, KXM, KZM>::W;
+    constexpr int XBC = K3WShape<T, KXM, KZM>::XBC;
+    constexpr int UGM = K3WShape<T, KXM, KZM>::UGM;
+    const int units = a.cz / 16;
+    int ug = 0;
+    for (int g = units < UGM ? units : UGM; g >= 1; --g)
+      if (units % g == 0 && k3w_lds<T>(a, g, ST, W) <= LDS_PER_CU) {
+        ug = g;
+        break;
+      }
+    if (ug == 0) return hipSuccess;
+    const size_t lds = k3w_lds<T>(a, ug, ST, W);
+    auto fn = k3_output_gate_waves<T, KXM, KZM, ST, UGM, W, XBC>;
+    static std::atomic<int> granted{0};
+    hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
+    if (e != hipSuccess) return e;
+    const int groups = units / ug;
+    constexpr int TW = 16 * ST;
+    const int total = a.batch * a.n * ((a.n + TW - 1) / TW);
+    static std::atomic<int> occ{0};
+    static std::atomic<size_t> occ_lds{0};
+    const int per_cu = resident_blocks((const void*)fn, 64 * W, lds, occ, occ_lds);
+    const int cap = a.num_cus * per_cu / groups > 0 ? a.num_cus * per_cu / groups : 1;
+    const int need = (total + W - 1) / W;
+    const int blocks = need < cap ? need : cap;
+    const int mask_all = a.mask == nullptr;
+    hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(64 * W), lds, st, (const T*)a.x,
+                       (const T*)a.z, (const T*)(mask_all ? a.one : a.mask), (T*)a.out,
+                       (const T*)a.wo, a.to, (const T*)a.wg, a.tg, a.n, a.np, a.cz, a.czp, a.c,
+                       a.cp, mask_all, ug, total);
+    *done = true;
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------------------
 
 template <class T, int KXM, int KZM, int XB>
 static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
@@ -284,6 +647,9 @@ static hipError_t launch_k3_dispatch(const StageArgs& a, hipStream_t st) {
   // a second x block per thread is needed only for wide c (KX >= 8 after padding)
 #define TRIMUL_CALL(X_, Z_)                                      \
   if (kx == X_ && kz == Z_) {                                    \
+    bool done = false;                                           \
+    hipError_t e = launch_k3w_t<T, X_, Z_>(a, st, &done);        \
+    if (e != hipSuccess || done) return e;                       \
     if (xb == 1) return launch_k3_t<T, X_, Z_, 1>(a, st);        \
     if (X_ >= 8 && xb == 2) return launch_k3_t<T, X_, Z_, (X_ >= 8 ? 2 : 1)>(a, st); \
   }
