@@ -127,29 +127,41 @@ __device__ __forceinline__ float gate_mul(float p_times_m, float g2) {
   return p_times_m * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(g2));
 }
 
+// acc + lo(a)*lo(b) + hi(a)*hi(b) for two bf16 pairs, fp32 accumulation (the products are
+// exact in fp32). Written as an instruction: the compiler's own route to the packed bf16
+// dot product has fed every unrolled copy the same source register.
+__device__ __forceinline__ float dot2_bf16(unsigned int a, unsigned int b, float acc) {
+  float d;
+  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(acc));
+  return d;
+}
+
 // LayerNorm of one row held by the G consecutive lanes of a pair: lane `part` holds
 // chunks part, part+G, ... of the row in v[0..NCH); chunk indices >= nreal are padding
-// (zero, and not counted). Normalises v in place to (x - mean) * rstd over the `width`
-// real values; padding chunks stay zero. The bf16 version takes sum and sum of squares in
-// one fp32 pass; the fp32 version uses two passes.
+// and must be zero on entry (they add nothing to the sums). Every chunk becomes
+// (x - mean) * rstd over the `width` real values, so padding comes out as the finite
+// value -mean*rstd, which the zero weight columns of the padding cancel; there is no
+// branch on the chunk index. The bf16 version takes sum and sum of squares in one fp32
+// pass (packed bf16 dot products); the fp32 version uses two passes.
 template <int NCH, int G>
 __device__ __forceinline__ void normalize_row_stats(const chunk_t (&v)[NCH], int part, int nreal,
                                                     int width, float& mean, float& rstd, bf16) {
-  // bf16 -> fp32 by shifting (the packed bf16 dot-product route is not used: this
-  // compiler feeds every unrolled v_dot2c_f32_bf16 the same source register)
+  constexpr unsigned int kOnes = 0x3F803F80u;  // bf16 pair (1, 1)
   float s = 0.f, q = 0.f;
 #pragma unroll
-  for (int i = 0; i < NCH; ++i) {
-    float f[8];
-    unpack(v[i], f, bf16());
+  for (int i = 0; i < NCH; ++i)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      s += f[e];
-      q = fmaf(f[e], f[e], q);
+    for (int d = 0; d < 4; ++d) {
+      s = dot2_bf16(v[i][d], kOnes, s);
+      q = dot2_bf16(v[i][d], v[i][d], q);
     }
-  }
   (void)part;
   (void)nreal;
+  // The sums come out of inline-asm instructions and go straight into DPP reads, which
+  // need two wait states after the VALU write of their source; the compiler's hazard
+  // check does not see inside the asm, so the wait states are provided here (the asm
+  // takes s and q as operands, so the DPP reads cannot be scheduled ahead of it).
+  asm volatile("s_nop 1" : "+v"(s), "+v"(q));
   const float inv_w = 1.0f / (float)width;
   mean = group_sum<G>(s) * inv_w;
   const float var = group_sum<G>(q) * inv_w - mean * mean;
@@ -168,12 +180,11 @@ __device__ __forceinline__ void normalize_row_stats(const chunk_t (&v)[NCH], int
   float q = 0.f;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    if (part + G * i < nreal) {
+    const float keep = part + G * i < nreal ? 1.f : 0.f;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const float d = __uint_as_float(v[i][e]) - mean;
-        q += d * d;
-      }
+    for (int e = 0; e < 4; ++e) {
+      const float d = (__uint_as_float(v[i][e]) - mean) * keep;
+      q = fmaf(d, d, q);
     }
   }
   rstd = rsqrtf(group_sum<G>(q) * inv_w + TRI_MUL_LN_EPS_F);
@@ -188,15 +199,6 @@ __device__ __forceinline__ float row_groups_sum(float v, int lane) {
   v += lane_value(v, lane ^ 16);
   v += lane_value(v, lane ^ 32);
   return v;
-}
-
-// acc + lo(a)*lo(b) + hi(a)*hi(b) for two bf16 pairs, fp32 accumulation (the products are
-// exact in fp32). Written as an instruction: the compiler's own route to the packed bf16
-// dot product has fed every unrolled copy the same source register.
-__device__ __forceinline__ float dot2_bf16(unsigned int a, unsigned int b, float acc) {
-  float d;
-  asm("v_dot2_f32_bf16 %0, %1, %2, %3" : "=v"(d) : "v"(a), "v"(b), "v"(acc));
-  return d;
 }
 
 // LayerNorm of one pair's row held in MFMA operand layout: lane (p, q) = (lane%16,
@@ -269,13 +271,11 @@ __device__ __forceinline__ void normalize_row(chunk_t (&v)[NCH], int part, int n
   const float shift = -mean * rstd;
 #pragma unroll
   for (int i = 0; i < NCH; ++i) {
-    if (part + G * i < nreal) {
-      float f[E];
-      unpack(v[i], f, T());
+    float f[E];
+    unpack(v[i], f, T());
 #pragma unroll
-      for (int e = 0; e < E; ++e) f[e] = fmaf(f[e], rstd, shift);
-      v[i] = pack(f, T());
-    }
+    for (int e = 0; e < E; ++e) f[e] = fmaf(f[e], rstd, shift);
+    v[i] = pack(f, T());
   }
 }
 

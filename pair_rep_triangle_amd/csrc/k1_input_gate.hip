@@ -51,7 +51,8 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
   float* const mvbuf = (float*)(zbase + nbuf * TP * zstride);
   auto zbuf = [&](int b) { return zbase + b * TP * zstride; };
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   T* const stg = (T*)(mvbuf + nbuf * TP) + (size_t)wave * UPW * 16 * SROW;
   const int cblocks = c / 16, units = 2 * cblocks;
   const int ntx = np / TP;
@@ -153,17 +154,37 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
     for (int i = 0; i < NCH; ++i)
       if (!(f.valid && part + TPP * i < czc)) f.v[i] = chunk_t{0u, 0u, 0u, 0u};
     normalize_row<T, NCH, TPP>(f.v, part, czc, cz);
+    // every lane stores (no branch): a chunk index past the padded row lands in the row's
+    // spare last E columns, which no MFMA operand read touches
     T* row = zbuf(buf) + t * zstride;
 #pragma unroll
     for (int i = 0; i < NCH; ++i) {
       const int ch = part + TPP * i;
-      if (ch < cpr) st16(row + ch * E, f.v[i]);
+      st16(row + (ch < cpr ? ch * E : czp), f.v[i]);
     }
     if (part == 0) mvbuf[buf * TP + t] = f.valid ? to_f32(f.m) : 0.f;
   };
 
+  // staging -> global: UPW*16 channel rows of TP contiguous elements (full cache lines).
+  // A tile's rows are stored at the start of the next iteration (or after the loop), so
+  // that the stores are long complete when stage() waits for the next tile's loads.
+  auto store_tile = [&](Coord q) {
+    wave_lds_sync();
+    const size_t tbase = (size_t)q.bb * c * plane + (size_t)q.r * np + q.sx * TP;
+#pragma unroll
+    for (int k = 0; k < NST; ++k) {
+      const int idx = k * 64 + lane, row = idx / CPT, cc = idx - row * CPT;
+      const int j = (k * 64) / CPT / 16;  // the same unit for the whole store
+      if (uok[j]) {                       // wave-uniform
+        T* dst = (uq[j] ? b_out : a_out) + tbase + soff[k];
+        st16(dst, ld16_lds8(stg + row * SROW + cc * E));
+      }
+    }
+  };
+
   int tile = blockIdx.x;  // the grid never exceeds the tile count
   Coord cur_c = decompose(tile);
+  Coord pend = cur_c;
   {
     Pre f;
     fetch(cur_c, f);
@@ -172,6 +193,7 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
   __syncthreads();
 
   for (int it = 0; tile < total_tiles; tile += gridDim.x, ++it) {
+    if (it > 0) store_tile(pend);
     const int cur = nbuf == 2 ? (it & 1) : 0;
     const bool has_next = tile + (int)gridDim.x < total_tiles;
     const Coord next_c = has_next ? advance(cur_c) : cur_c;
@@ -217,23 +239,13 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
                gate_mul(acc[j][1][2] * m4[2], acc[j][0][2]),
                gate_mul(acc[j][1][3] * m4[3], acc[j][0][3]));
     }
-    // staging -> global: UPW*16 channel rows of TP contiguous elements (full cache lines)
-    wave_lds_sync();
-    const size_t tbase = (size_t)cur_c.bb * c * plane + (size_t)cur_c.r * np + cur_c.sx * TP;
-#pragma unroll
-    for (int k = 0; k < NST; ++k) {
-      const int idx = k * 64 + lane, row = idx / CPT, cc = idx - row * CPT;
-      const int j = (k * 64) / CPT / 16;  // the same unit for the whole store
-      if (uok[j]) {
-        T* dst = (uq[j] ? b_out : a_out) + tbase + soff[k];
-        st16(dst, ld16_lds8(stg + row * SROW + cc * E));
-      }
-    }
+    pend = cur_c;
     if (nbuf == 1) __syncthreads();  // every wave is done reading the single z buffer
     stage(nbuf == 2 ? cur ^ 1 : 0, pre);
     __syncthreads();
     cur_c = next_c;
   }
+  store_tile(pend);
 }
 
 // ---------------------------------------------------------------------------------------
