@@ -544,12 +544,12 @@ template <class T, int KXM, int KZM>
 struct K3WShape {
   static constexpr int E = Traits<T>::E;
   static constexpr bool NARROW = KXM + KZM <= 8;
-  static constexpr int ST = 1;
-  static constexpr int W = NARROW ? 16 : 8;
-  static constexpr int XBC = NARROW ? E / 2 : E;
+  static constexpr int ST = NARROW ? 2 : 1;
+  static constexpr int W = 8;
+  static constexpr int XBC = E;
   static constexpr int XBM = (KXM * (Traits<T>::KG / XBC) * (16 * ST / E) + 63) / 64;
   static constexpr int VGPRS = 4 * (ST * (KXM + KZM) + XBM * XBC + ST * KZM);
-  static constexpr bool OK = VGPRS <= (NARROW ? 96 : 160);
+  static constexpr bool OK = VGPRS <= (NARROW ? 128 : 160);
   static constexpr int UGM = KZM * Traits<T>::KG / 16 < 8 ? KZM * Traits<T>::KG / 16 : 8;
 };
 
