@@ -202,35 +202,31 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
 
     const T* zs = zbuf(cur);
     const float* mv = mvbuf + cur * TP;
+    // Software pipeline over the four 16-pair row tiles: the MFMAs of row tile rt+1 are
+    // issued before the gate epilogue of row tile rt, so the matrix cores and the
+    // VALU/transcendental units work on different row tiles at the same time.
+    auto mma_rt = [&](int rt, f32x4 (&acc)[UPW][2]) {
+      const T* arow = zs + (rt * 16 + (lane & 15)) * zstride + (lane >> 4) * E;
+      chunk_t af[KMAX];
 #pragma unroll
-    for (int rt = 0; rt < TP / 16; ++rt) {
-      // accumulator register rr <-> pair rt*16 + 4*(lane/16) + rr, channel lane%16 of unit
+      for (int ks = 0; ks < KMAX; ++ks) af[ks] = ld16(arow + ks * KG);
+#pragma unroll
+      for (int j = 0; j < UPW; ++j) {
+        acc[j][0] = mma16(bias[j][0], af[0], wgt[j][0][0], T());
+        acc[j][1] = mma16(bias[j][1], af[0], wgt[j][1][0], T());
+      }
+#pragma unroll
+      for (int ks = 1; ks < KMAX; ++ks)
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) {
+          acc[j][0] = mma16(acc[j][0], af[ks], wgt[j][0][ks], T());
+          acc[j][1] = mma16(acc[j][1], af[ks], wgt[j][1][ks], T());
+        }
+    };
+    // accumulator register rr <-> pair rt*16 + 4*(lane/16) + rr, channel lane%16 of unit
+    auto epi_rt = [&](int rt, const f32x4 (&acc)[UPW][2]) {
       const int p0 = rt * 16 + 4 * (lane >> 4);
       T* const srow = stg + (lane & 15) * SROW + p0;
-      if (__all(mv[rt * 16 + (lane & 15)] == 0.f)) {  // fully padded: zero, no MFMA
-#pragma unroll
-        for (int j = 0; j < UPW; ++j) store4(srow + j * 16 * SROW, 0.f, 0.f, 0.f, 0.f);
-        continue;
-      }
-      const T* arow = zs + (rt * 16 + (lane & 15)) * zstride + (lane >> 4) * E;
-      f32x4 acc[UPW][2];
-      {
-        const chunk_t af = ld16(arow);
-#pragma unroll
-        for (int j = 0; j < UPW; ++j) {
-          acc[j][0] = mma16(bias[j][0], af, wgt[j][0][0], T());
-          acc[j][1] = mma16(bias[j][1], af, wgt[j][1][0], T());
-        }
-      }
-#pragma unroll
-      for (int ks = 1; ks < KMAX; ++ks) {
-        const chunk_t af = ld16(arow + ks * KG);
-#pragma unroll
-        for (int j = 0; j < UPW; ++j) {
-          acc[j][0] = mma16(acc[j][0], af, wgt[j][0][ks], T());
-          acc[j][1] = mma16(acc[j][1], af, wgt[j][1][ks], T());
-        }
-      }
       const f32x4 m4 = ld16f(mv + p0);
 #pragma unroll
       for (int j = 0; j < UPW; ++j)
@@ -238,6 +234,25 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
                gate_mul(acc[j][1][1] * m4[1], acc[j][0][1]),
                gate_mul(acc[j][1][2] * m4[2], acc[j][0][2]),
                gate_mul(acc[j][1][3] * m4[3], acc[j][0][3]));
+    };
+    static_assert(TP == 64, "four row tiles per tile");
+    if (__all(mv[lane] == 0.f)) {  // whole tile padded: zeros, no MFMA (wave-uniform)
+#pragma unroll
+      for (int rt = 0; rt < TP / 16; ++rt) {
+        T* const srow = stg + (lane & 15) * SROW + rt * 16 + 4 * (lane >> 4);
+#pragma unroll
+        for (int j = 0; j < UPW; ++j) store4(srow + j * 16 * SROW, 0.f, 0.f, 0.f, 0.f);
+      }
+    } else {
+      f32x4 acc0[UPW][2], acc1[UPW][2];
+      mma_rt(0, acc0);
+      mma_rt(1, acc1);
+      epi_rt(0, acc0);
+      mma_rt(2, acc0);
+      epi_rt(1, acc1);
+      mma_rt(3, acc1);
+      epi_rt(2, acc0);
+      epi_rt(3, acc1);
     }
     pend = cur_c;
     if (nbuf == 1) __syncthreads();  // every wave is done reading the single z buffer
