@@ -98,16 +98,18 @@ __device__ __forceinline__ f32x16 mma32(f32x16 acc, chunk_t a, chunk_t b, float)
   return acc;
 }
 
-// Sum over the G consecutive lanes G*q .. G*q+G-1 (G = 4 or 8; quad permutes, then the
-// half-row mirror for 8); every lane of the group receives the total.
+// Sum over the G consecutive lanes G*q .. G*q+G-1 (G = 4, 8 or 16: quad permutes, then the
+// half-row mirror for 8, then the row mirror for 16); every lane of the group receives the
+// total.
 #define TRIMUL_DPP(v, ctrl) \
   __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), ctrl, 0xF, 0xF, true))
 template <int G>
 __device__ __forceinline__ float group_sum(float v) {
-  static_assert(G == 4 || G == 8, "group of 4 or 8 lanes");
+  static_assert(G == 4 || G == 8 || G == 16, "group of 4, 8 or 16 lanes");
   v += TRIMUL_DPP(v, 0xB1);  // quad_perm [1,0,3,2]
   v += TRIMUL_DPP(v, 0x4E);  // quad_perm [2,3,0,1]
-  if (G == 8) v += TRIMUL_DPP(v, 0x141);  // row_half_mirror
+  if (G >= 8) v += TRIMUL_DPP(v, 0x141);  // row_half_mirror
+  if (G == 16) v += TRIMUL_DPP(v, 0x140);  // row_mirror
   return v;
 }
 

@@ -22,19 +22,17 @@
 namespace trimul {
 
 constexpr int K1_TP = 64;
-constexpr int K1_WAVES = 8;
-constexpr int K1_THREADS = 64 * K1_WAVES;
-constexpr int K1_TPP = K1_THREADS / K1_TP;  // threads per pair when staging a tile
 
-template <class T, int KMAX, int UPW>
-__global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
+template <class T, int KMAX, int UPW, int W>
+__global__ __launch_bounds__(64 * W) void k1_input_gate(
     const T* __restrict__ z, const T* __restrict__ mask, T* __restrict__ a_out,
     T* __restrict__ b_out, const T* __restrict__ w1, const float* __restrict__ t1, int n, int np,
     int cz, int czp, int c, int incoming, int mask_all, int nbuf, int total_tiles) {
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int TP = K1_TP;
-  constexpr int TPP = K1_TPP;
+  constexpr int THREADS = 64 * W;
+  constexpr int TPP = THREADS / TP;  // threads per pair when staging a tile
   constexpr int NCH = (KMAX * KG / E + TPP - 1) / TPP;  // z chunks per thread
   // staging row (one channel, TP pairs): for bf16 an 8-byte-aligned stride of 34 dwords so
   // the 8-byte writes of 16 consecutive rows hit distinct banks; fp32 rows stay 16-byte
@@ -65,7 +63,7 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
   bool uok[UPW];
 #pragma unroll
   for (int j = 0; j < UPW; ++j) {
-    const int u = blockIdx.y * (K1_WAVES * UPW) + wave + K1_WAVES * j;
+    const int u = blockIdx.y * (W * UPW) + wave + W * j;
     uok[j] = u < units;
     uq[j] = uok[j] ? u / cblocks : 0;
     ucb[j] = uok[j] ? (u - uq[j] * cblocks) * 16 : 0;
@@ -265,29 +263,29 @@ __global__ __launch_bounds__(K1_THREADS) void k1_input_gate(
 
 // ---------------------------------------------------------------------------------------
 
-template <class T, int KMAX, int UPW>
+template <class T, int KMAX, int UPW, int W>
 static hipError_t launch_k1_t(const StageArgs& a, hipStream_t st) {
   constexpr int E = Traits<T>::E;
   auto lds_for = [&](int nb) {
     return nb * ((size_t)K1_TP * (a.czp + E) * sizeof(T) + K1_TP * sizeof(float)) +
-           (size_t)K1_WAVES * UPW * 16 * (K1_TP + 4) * sizeof(T);
+           (size_t)W * UPW * 16 * (K1_TP + 4) * sizeof(T);
   };
   const int nbuf = lds_for(2) <= LDS_PER_CU ? 2 : 1;
   const size_t lds = lds_for(nbuf);
-  auto fn = k1_input_gate<T, KMAX, UPW>;
+  auto fn = k1_input_gate<T, KMAX, UPW, W>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
   if (e != hipSuccess) return e;
   const int units = 2 * (a.c / 16);
-  const int groups = (units + K1_WAVES * UPW - 1) / (K1_WAVES * UPW);
+  const int groups = (units + W * UPW - 1) / (W * UPW);
   const int total = a.batch * a.np * (a.np / K1_TP);
   static std::atomic<int> occ{0};
   static std::atomic<size_t> occ_lds{0};
-  const int per_cu = resident_blocks((const void*)fn, K1_THREADS, lds, occ, occ_lds);
+  const int per_cu = resident_blocks((const void*)fn, 64 * W, lds, occ, occ_lds);
   const int cap = a.num_cus * per_cu / groups > 0 ? a.num_cus * per_cu / groups : 1;
   const int blocks = total < cap ? total : cap;
   const int mask_all = a.mask == nullptr;
-  hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K1_THREADS), lds, st, (const T*)a.z,
+  hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(64 * W), lds, st, (const T*)a.z,
                      (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b, (const T*)a.w1, a.t1,
                      a.n, a.np, a.cz, a.czp, a.c, a.incoming, mask_all, nbuf, total);
   return hipGetLastError();
@@ -298,12 +296,12 @@ static hipError_t launch_k1_t(const StageArgs& a, hipStream_t st) {
 template <class T>
 static hipError_t launch_k1_dispatch(const StageArgs& a, hipStream_t st) {
   switch (a.czp / Traits<T>::KG) {
-    case 1: return launch_k1_t<T, 1, 2>(a, st);
-    case 2: return launch_k1_t<T, 2, 2>(a, st);
-    case 4: return launch_k1_t<T, 4, 2>(a, st);
-    case 8: return launch_k1_t<T, 8, 1>(a, st);
-    case 12: return launch_k1_t<T, 12, 1>(a, st);
-    case 16: return launch_k1_t<T, 16, 1>(a, st);
+    case 1: return launch_k1_t<T, 1, 2, 8>(a, st);
+    case 2: return launch_k1_t<T, 2, 2, 8>(a, st);
+    case 4: return launch_k1_t<T, 4, 1, 16>(a, st);
+    case 8: return launch_k1_t<T, 8, 1, 8>(a, st);
+    case 12: return launch_k1_t<T, 12, 1, 8>(a, st);
+    case 16: return launch_k1_t<T, 16, 1, 8>(a, st);
     default: return hipErrorInvalidValue;
   }
 }
