@@ -73,7 +73,7 @@ typedef struct tri_mul_handle tri_mul_handle;
 
 /* Where the intermediates live inside a workspace (byte offsets from its
  * start). a, b and x are each [batch][c][n_pad][n_pad] in the handle's dtype,
- * n_pad = n rounded up to a multiple of 128, entries outside n x n are zero
+ * n_pad = n rounded up to a multiple of 256, entries outside n x n are zero
  * for a and b. For outgoing, a[b][ch][i][k] = a_bik; for incoming the input
  * kernel stores the operands transposed, a[b][ch][i][k] = a_bki (same for b),
  * so the contraction is x[b][ch][i][j] = sum_k a[..][i][k] * b[..][j][k] in

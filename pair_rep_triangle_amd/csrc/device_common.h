@@ -35,6 +35,15 @@ __device__ __forceinline__ chunk_t ld16_lds8(const bf16* p) {
 }
 __device__ __forceinline__ chunk_t ld16_lds8(const float* p) { return ld16(p); }
 
+// 16 bytes per lane from global memory straight into LDS (global_load_lds_dwordx4): lane i
+// of the wave writes lds_base + 16*i, where lds_base is wave-uniform. Completion is
+// counted by vmcnt. (Wrapped in a plain device function so that kernel templates using
+// it still get their host-side launch stubs.)
+__device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void*)lds_base, 16, 0,
+                                   0);
+}
+
 // chunk <-> floats
 __device__ __forceinline__ void unpack(chunk_t c, float* f, bf16) {
 #pragma unroll

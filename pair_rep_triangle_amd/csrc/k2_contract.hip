@@ -9,143 +9,178 @@
 
 namespace trimul {
 
-constexpr int NTHREADS = 256;
-
-// k2: x[bc] = A[bc] B[bc]^T for every (batch, channel) bc; A, B, x are [np][np].
-// 128 x 128 output tile per workgroup, 4 waves as 2 x 2, each 64 x 64 (2 x 2 MFMA
-// 32x32 tiles). k advances 128 bytes per stage through a double-buffered LDS, with two
-// stages of global loads in flight.
-// Flat grid of (np/128)^2 * batch*c workgroups, remapped so that consecutive tiles
-// of one channel land on the same XCD (workgroup ids are dealt round-robin over the
+// Workgroup tile 256 (i) x 128 (j), 4 waves as 2 x 2, each 128 x 64 (4 x 2 MFMA 32x32
+// tiles, 128 fp32 accumulators per lane). k advances 64 bytes per row and stage; stages
+// move from global memory straight into LDS (global_load_lds, no registers on the way)
+// through a ring of three LDS buffers, so two stages are in flight while one is used.
+// Inside a buffer a row is four 16-byte chunks; chunk c of row r sits at position
+// c ^ ((r ^ (r >> 2)) & 3), which keeps the MFMA operand reads free of bank conflicts
+// (checked for both 32- and 64-bank LDS). The output tile is staged in LDS and leaves as
+// 16-byte row-contiguous stores.
+// Flat grid of (np/256) * (np/128) * batch*c workgroups, remapped so that consecutive
+// tiles of one channel land on the same XCD (workgroup ids are dealt round-robin over the
 // 8 XCDs) and share its L2.
-constexpr int K2_TILE = 128;
+constexpr int K2_BM = 256, K2_BN = 128;
+constexpr int K2_THREADS = 256;
+constexpr int K2_STAGES = 3;
+constexpr int K2_KC = 4;                                   // 16-byte chunks per row and stage
+constexpr int K2_A_BYTES = K2_BM * K2_KC * 16;             // 16 KB
+constexpr int K2_B_BYTES = K2_BN * K2_KC * 16;             // 8 KB
+constexpr int K2_STAGE_BYTES = K2_A_BYTES + K2_B_BYTES;    // 24 KB
+static_assert(N_PAD % K2_BM == 0 && N_PAD % K2_BN == 0, "padded side covers whole tiles");
+
+__device__ __forceinline__ int k2_swizzle(int r) { return (r ^ (r >> 2)) & 3; }
 
 template <class T>
-__global__ __launch_bounds__(NTHREADS) void k2_contract(const T* __restrict__ A,
-                                                        const T* __restrict__ B,
-                                                        T* __restrict__ X, int np) {
+__global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict__ A,
+                                                             const T* __restrict__ B,
+                                                             T* __restrict__ X, int np) {
   constexpr int E = Traits<T>::E;
-  constexpr int KT = 8 * E;        // k per stage (128 bytes per row)
-  constexpr int LROW = KT + E;     // LDS row stride in elements (144 bytes)
-  constexpr int STAGE = K2_TILE * LROW;
-  __shared__ __attribute__((aligned(16))) T lds[2][2][STAGE];
+  constexpr int KT = K2_KC * E;  // k per stage
+  __shared__ __attribute__((aligned(16))) unsigned char lds[K2_STAGES * K2_STAGE_BYTES];
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
   const int bid = blockIdx.x, total = gridDim.x;
   const int per = total >> 3;
   const int logical = bid < (per << 3) ? (bid & 7) * per + (bid >> 3) : bid;
-  const int t1d = np / K2_TILE;
-  const int tiles = t1d * t1d;
+  const int tn = np / K2_BN;
+  const int tiles = (np / K2_BM) * tn;
   const int bc = logical / tiles, tile = logical - bc * tiles;
-  const int ti = tile / t1d, tj = tile - ti * t1d;
+  const int ti = tile / tn, tj = tile - ti * tn;
 
   const size_t mat = (size_t)np * np;
-  const T* Ab = A + bc * mat + (size_t)ti * K2_TILE * np;
-  const T* Bb = B + bc * mat + (size_t)tj * K2_TILE * np;
+  const T* Ab = A + bc * mat + (size_t)ti * K2_BM * np;
+  const T* Bb = B + bc * mat + (size_t)tj * K2_BN * np;
 
-  // Global -> registers -> LDS, two stages in flight: the loads of stage s+2 are issued
-  // before stage s is computed and land in LDS after it, so two stages of MFMA work cover
-  // the memory latency. The two register sets alternate (the loop is unrolled by two so
-  // that every register index is static).
-  chunk_t ra[2][4], rb[2][4];
-  auto gload = [&](int set, int k0) {
+  // this lane's slot in a 1 KB direct-load block: row lane/4 of the block's 16, position
+  // lane%4, which holds chunk (position ^ swizzle(row)) of the row
+  const int brow = lane >> 2;
+  auto issue = [&](int s) {
+    unsigned char* base = lds + (s % K2_STAGES) * K2_STAGE_BYTES;
+    const int k0 = s * KT;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + NTHREADS * q, row = idx >> 3, c16 = idx & 7;
-      ra[set][q] = ld16(Ab + (size_t)row * np + k0 + c16 * E);
-      rb[set][q] = ld16(Bb + (size_t)row * np + k0 + c16 * E);
+    for (int q = 0; q < K2_BM / 16 / 4; ++q) {  // A: 16 blocks of 16 rows, 4 per wave
+      const int blk = wave + 4 * q, row = blk * 16 + brow;
+      const int c = (lane & 3) ^ k2_swizzle(row);
+      lds_dma16(Ab + (size_t)row * np + k0 + c * E, base + blk * 1024);
+    }
+#pragma unroll
+    for (int q = 0; q < K2_BN / 16 / 4; ++q) {  // B: 8 blocks, 2 per wave
+      const int blk = wave + 4 * q, row = blk * 16 + brow;
+      const int c = (lane & 3) ^ k2_swizzle(row);
+      lds_dma16(Bb + (size_t)row * np + k0 + c * E, base + K2_A_BYTES + blk * 1024);
     }
   };
-  auto lstore = [&](int buf, int set) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int idx = tid + NTHREADS * q, row = idx >> 3, c16 = idx & 7;
-      st16(&lds[buf][0][row * LROW + c16 * E], ra[set][q]);
-      st16(&lds[buf][1][row * LROW + c16 * E], rb[set][q]);
-    }
-  };
+  constexpr int LOADS_PER_STAGE = K2_BM / 16 / 4 + K2_BN / 16 / 4;  // per thread
 
-  f32x16 acc[2][2];
+  f32x16 acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](int cur) {
+  // operand rows of this lane: i rows wm*128 + mt*32 + lane%32, j rows wn*64 + nt*32 +
+  // lane%32; all have the same swizzle (the row bases are multiples of 32)
+  const int sw = k2_swizzle(lane & 31);
+  auto compute = [&](int s) {
+    const unsigned char* cur = lds + (s % K2_STAGES) * K2_STAGE_BYTES;
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      const int koff = (2 * kk + (lane >> 5)) * E;
-      chunk_t fa[2], fb[2];
+    for (int step = 0; step < K2_KC / 2; ++step) {
+      const int pos = ((2 * step + (lane >> 5)) ^ sw) * 16;
+      chunk_t fa[4], fb[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-        fa[mt] = ld16(&lds[cur][0][(wm * 64 + mt * 32 + (lane & 31)) * LROW + koff]);
+      for (int mt = 0; mt < 4; ++mt)
+        fa[mt] = ld16(cur + (wm * 128 + mt * 32 + (lane & 31)) * 64 + pos);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        fb[nt] = ld16(&lds[cur][1][(wn * 64 + nt * 32 + (lane & 31)) * LROW + koff]);
+        fb[nt] = ld16(cur + K2_A_BYTES + (wn * 64 + nt * 32 + (lane & 31)) * 64 + pos);
       // operands swapped: the MFMA produces D[j][i] = x[i][j], so each lane ends up
       // with runs of 4 consecutive j of one row i.
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32(acc[mt][nt], fb[nt], fa[mt], T());
     }
   };
 
-  // stage s lives in LDS buffer s % 2 and (while in flight) register set s % 2
-  const int nst = np / KT;  // even: np is a multiple of 128 and KT is 64 or 32
-  gload(0, 0);
-  gload(1, KT);
-  lstore(0, 0);
-  __syncthreads();
-  for (int s = 0; s < nst; s += 2) {
-    // even stage s: buffer 0 holds it, set 1 holds s+1, set 0 is free
-    if (s + 2 < nst) gload(0, (s + 2) * KT);
-    compute(0);
-    lstore(1, 1);  // stage s+1 always exists (nst even)
-    __syncthreads();
-    // odd stage s+1: buffer 1 holds it, set 0 holds s+2 (if any), set 1 is free
-    if (s + 3 < nst) gload(1, (s + 3) * KT);
-    compute(1);
-    if (s + 2 < nst) lstore(0, 0);
-    __syncthreads();
+  const int nst = np / KT;  // at least 2: np is a multiple of 256
+  issue(0);
+  issue(1);
+  for (int s = 0; s < nst; ++s) {
+    // this thread's loads of stage s are done once at most the next stage's remain
+    if (s + 1 < nst)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_STAGE);  // vmcnt(LOADS_PER_STAGE)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    // every wave's part of stage s is in LDS, and every wave is done with stage s-1,
+    // whose buffer the loads of stage s+2 overwrite (its LDS reads all fed MFMAs, so
+    // they have completed). A bare s_barrier: __syncthreads() would also wait for the
+    // stage s+1 loads still in flight. The empty asm statements keep the compiler from
+    // moving LDS accesses across it.
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + 2 < nst) issue(s + 2);
+    compute(s);
   }
+  __syncthreads();  // all waves are done reading the ring before it holds the output
 
-  // epilogue: stage the 128 x 128 tile in LDS as [i][j], then 16-byte coalesced stores
-  constexpr int XROW = K2_TILE + E;
-  T* xs = &lds[0][0][0];
+  T* Xb = X + bc * mat + (size_t)ti * K2_BM * np + tj * K2_BN;
+  if constexpr (sizeof(T) == 2) {
+    // stage the 256 x 128 tile as [i][j] rows, then 16-byte row-contiguous stores
+    constexpr int XROW = K2_BN + E;
+    static_assert(K2_BM * XROW * sizeof(T) <= K2_STAGES * K2_STAGE_BYTES, "output staging fits");
+    T* xs = (T*)lds;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt)
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int i = wm * 64 + mt * 32 + (lane & 31);
-        const int j = wn * 64 + nt * 32 + 8 * q + 4 * (lane >> 5);
-        store4(xs + i * XROW + j, acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1],
-               acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
-      }
-  __syncthreads();
-  T* Xb = X + bc * mat + (size_t)ti * K2_TILE * np + tj * K2_TILE;
-  constexpr int CPR = K2_TILE / E;
-  for (int idx = tid; idx < K2_TILE * CPR; idx += NTHREADS) {
-    const int row = idx / CPR, cc = idx - row * CPR;
-    st16(Xb + (size_t)row * np + cc * E, ld16(xs + row * XROW + cc * E));
+        for (int q = 0; q < 4; ++q) {
+          const int i = wm * 128 + mt * 32 + (lane & 31);
+          const int j = wn * 64 + nt * 32 + 8 * q + 4 * (lane >> 5);
+          store4(xs + i * XROW + j, acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1],
+                 acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
+        }
+    __syncthreads();
+    constexpr int CPR = K2_BN / E;
+#pragma unroll 4
+    for (int idx = tid; idx < K2_BM * CPR; idx += K2_THREADS) {
+      const int row = idx / CPR, cc = idx - row * CPR;
+      st16(Xb + (size_t)row * np + cc * E, ld16(xs + row * XROW + cc * E));
+    }
+  } else {
+    // fp32: four consecutive j per lane are one 16-byte store
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int i = wm * 128 + mt * 32 + (lane & 31);
+          const int j = wn * 64 + nt * 32 + 8 * q + 4 * (lane >> 5);
+          store4(Xb + (size_t)i * np + j, acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1],
+                 acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
+        }
   }
 }
 
+size_t k2_grid(int np, int batch, int c) {
+  return (size_t)(np / K2_BM) * (np / K2_BN) * batch * c;
+}
 
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st) {
-  const size_t t1d = a.np / K2_TILE;
-  dim3 grid((unsigned)(t1d * t1d * (size_t)a.batch * a.c));
+  dim3 grid((unsigned)k2_grid(a.np, a.batch, a.c));
   if (bf16_storage)
-    hipLaunchKernelGGL(k2_contract<bf16>, grid, dim3(NTHREADS), 0, st, (const bf16*)a.a,
+    hipLaunchKernelGGL(k2_contract<bf16>, grid, dim3(K2_THREADS), 0, st, (const bf16*)a.a,
                        (const bf16*)a.b, (bf16*)a.x, a.np);
   else
-    hipLaunchKernelGGL(k2_contract<float>, grid, dim3(NTHREADS), 0, st, (const float*)a.a,
+    hipLaunchKernelGGL(k2_contract<float>, grid, dim3(K2_THREADS), 0, st, (const float*)a.a,
                        (const float*)a.b, (float*)a.x, a.np);
   return hipGetLastError();
 }

@@ -32,7 +32,7 @@ struct StageArgs {
 // k extent of one 16x16 MFMA chunk group: 32 (bf16) or 16 (fp32).
 inline int k_group(bool bf16_storage) { return bf16_storage ? 32 : 16; }
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
-constexpr int N_PAD = 128;  // side padding of a, b, x (the contraction tile)
+constexpr int N_PAD = 256;  // side padding of a, b, x (covers whole contraction tiles)
 constexpr size_t LDS_PER_CU = 160 * 1024;  // gfx950 LDS per CU (the most one workgroup may use)
 
 // The projection kernels keep their weights in registers, sized at compile time by the
@@ -81,6 +81,7 @@ inline int resident_blocks(const void* fn, int threads, size_t lds, std::atomic<
 
 hipError_t launch_k1(bool bf16_storage, const StageArgs& a, hipStream_t st);
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st);
+size_t k2_grid(int np, int batch, int c);  // contraction workgroups per launch
 hipError_t launch_k3(bool bf16_storage, const StageArgs& a, hipStream_t st);
 
 }  // namespace trimul

@@ -110,8 +110,7 @@ int validate_call(const tri_mul_handle* h, int stage, const void* z, const void*
   if (direction != TRI_MUL_OUTGOING && direction != TRI_MUL_INCOMING) return TRI_MUL_ERR_INVALID_ARG;
   if (!z || !out || !ws) return TRI_MUL_ERR_INVALID_ARG;
   const Layout L = layout_of(h, batch, n);
-  const size_t t1d = (size_t)L.np / trimul::N_PAD;
-  if (t1d * t1d * (size_t)batch * h->c > 0x7fffffffu) return TRI_MUL_ERR_INVALID_ARG;
+  if (trimul::k2_grid(L.np, batch, h->c) > 0x7fffffffu) return TRI_MUL_ERR_INVALID_ARG;
   if (((uintptr_t)z | (uintptr_t)out | (uintptr_t)ws) & 15u) return TRI_MUL_ERR_ALIGNMENT;
   if (mask && ((uintptr_t)mask & (uintptr_t)(L.esz - 1))) return TRI_MUL_ERR_ALIGNMENT;
   if (ws_bytes < L.total) return TRI_MUL_ERR_WORKSPACE_TOO_SMALL;
