@@ -9,8 +9,11 @@ Prints ONE JSON line:
                 MI355X peak; its duration from HIP events recorded after every
                 kernel in a second timed region of K steps
   cpu_baseline  the fp64 oracle timed on this host (rank 0, N=1 only)
+With --chained the step is the pair update in model order instead (outgoing with
+its residual add, then incoming on that result with its residual add); the
+per-kernel region still times the plain stages.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--chained] [--no-cpu-baseline]
 """
 
 import argparse
@@ -33,6 +36,9 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=10)
     p.add_argument("--workload", default=None)
+    p.add_argument("--chained", action="store_true",
+                   help="time the pair update in model order instead: outgoing with its residual "
+                        "add, then incoming on that result with its residual add")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
@@ -92,6 +98,11 @@ def main():
     stream = torch.cuda.current_stream(dev)
 
     def step():
+        if args.chained:  # z -> outs[0] = z + upd_out(z) -> outs[1] = outs[0] + upd_in(outs[0])
+            mods[0][1].forward_residual(z, mask, out=outs[0], direction="outgoing", workspace=ws)
+            mods[1][1].forward_residual(outs[0], mask, out=outs[1], direction="incoming",
+                                        workspace=ws)
+            return
         for (direction, mod), out in zip(mods, outs):
             mod.forward(z, mask, out=out, direction=direction, workspace=ws)
 
@@ -196,7 +207,9 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "n": n, "c_z": c_z, "c": c,
                    "valid_length": d["meta"].get("valid_length", n),
-                   "directions": "outgoing+incoming", "mask": spec["mask"]},
+                   "directions": ("outgoing->incoming, chained with residual adds"
+                                  if args.chained else "outgoing+incoming"),
+                   "mask": spec["mask"]},
         "pair_updates_per_s": round(pair_updates, 1),
         "wall_s": round(wall, 3),
         "roofline": roofline,

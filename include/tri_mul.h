@@ -111,6 +111,21 @@ int tri_mul_forward(tri_mul_handle* h, const void* z, const void* pair_mask, voi
                     int batch, int n, int direction, void* workspace, size_t workspace_bytes,
                     void* stream);
 
+/* The update followed by its residual add, in one pass over the output:
+ *   z_out = z + out,  out as in tri_mul_forward (so z_out = z on pairs with mask 0).
+ * The masked residual add of a pair-update step, fused into the last kernel (the
+ * kernel table on the RFProteína architecture page lists it as the separate "masked
+ * residual" kernel after each pair operation). Running it for the outgoing direction
+ * and then, on its result, for the incoming direction is the pair update's order
+ * ("Inside the velocity network": outgoing, then incoming triangle multiplication).
+ *   z_out  [batch][n][n][c_z], handle dtype, 16-byte aligned; either z itself (in
+ *          place) or a buffer that does not overlap z, pair_mask or the workspace.
+ * The sum is taken in fp32 and rounded once to the handle dtype. Other arguments and
+ * errors as for tri_mul_forward. */
+int tri_mul_forward_residual(tri_mul_handle* h, const void* z, const void* pair_mask,
+                             void* z_out, int batch, int n, int direction, void* workspace,
+                             size_t workspace_bytes, void* stream);
+
 /* One kernel of the chain, same arguments as tri_mul_forward:
  *   stage 1: input LayerNorm + gated dual projection + mask -> a, b (workspace)
  *   stage 2: contraction over k -> x (workspace)

@@ -182,3 +182,18 @@ def tri_mul_ref_pairs(z, mask, weights, direction, bidx, iidx, jidx, eps=EPS):
         out[s] = output_stage(x, zhat_ij, np.float64(mij), w, eps)
     return out
 
+
+def tri_mul_residual_ref(z, mask, weights, direction, eps=EPS):
+    """z + out: the update followed by the masked residual add of the pair update
+    [RFProteína architecture page, kernel table: a "masked residual" kernel follows each
+    pair operation; out already carries the mask (reading R7), so padded pairs keep z]."""
+    return _f64(z) + tri_mul_ref(z, mask, weights, direction, eps)
+
+
+def pair_update_ref(z, mask, w_outgoing, w_incoming, eps=EPS):
+    """The two triangle multiplicative updates of one pair-update step in model order:
+    outgoing on z, then incoming on the result, each with its residual add
+    [RFProteína architecture, "Inside the velocity network": the pair update runs the
+    outgoing, then the incoming triangle multiplication]."""
+    z1 = tri_mul_residual_ref(z, mask, w_outgoing, "outgoing", eps)
+    return tri_mul_residual_ref(z1, mask, w_incoming, "incoming", eps)

@@ -72,6 +72,35 @@ __device__ __forceinline__ chunk_t pack(const float* f, float) {
   return c;
 }
 
+// Element-wise a + b of two chunks, summed in fp32 and rounded once to the storage type.
+__device__ __forceinline__ chunk_t add_chunks(chunk_t a, chunk_t b, bf16) {
+  float fa[8], fb[8];
+  unpack(a, fa, bf16());
+  unpack(b, fb, bf16());
+#pragma unroll
+  for (int e = 0; e < 8; ++e) fa[e] += fb[e];
+  return pack(fa, bf16());
+}
+__device__ __forceinline__ chunk_t add_chunks(chunk_t a, chunk_t b, float) {
+  chunk_t c;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) c[e] = __float_as_uint(__uint_as_float(a[e]) + __uint_as_float(b[e]));
+  return c;
+}
+// v[r] += p[r] for four consecutive elements at p (8-byte bf16 / 16-byte fp32 load).
+__device__ __forceinline__ void add4(float (&v)[4], const bf16* p) {
+  const half_t h = *(const half_t*)p;
+  v[0] += __uint_as_float(h[0] << 16);
+  v[1] += __uint_as_float(h[0] & 0xffff0000u);
+  v[2] += __uint_as_float(h[1] << 16);
+  v[3] += __uint_as_float(h[1] & 0xffff0000u);
+}
+__device__ __forceinline__ void add4(float (&v)[4], const float* p) {
+  const f32x4 f = *(const f32x4*)p;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] += f[r];
+}
+
 // Four values -> one 8-byte (bf16) or 16-byte (fp32) store.
 __device__ __forceinline__ void store4(bf16* p, float a, float b, float c, float d) {
   bf16x2 lo = {(bf16)a, (bf16)b}, hi = {(bf16)c, (bf16)d};

@@ -22,6 +22,13 @@
 
 namespace trimul {
 
+// z and out are distinct buffers (restrict-qualified) unless the kernel adds the update
+// to z, where out may be z itself.
+template <class T, bool RESID>
+using ZIn = std::conditional_t<RESID, const T*, const T* __restrict__>;
+template <class T, bool RESID>
+using ZOut = std::conditional_t<RESID, T*, T* __restrict__>;
+
 constexpr int K3_TP = 64;
 constexpr int K3_WAVES = 4;
 constexpr int K3_THREADS = 64 * K3_WAVES;
@@ -29,10 +36,10 @@ constexpr int K3_TPP = K3_THREADS / K3_TP;  // threads per pair when staging a t
 constexpr int K3_UPW = 2;                   // 16-channel output units per wave
 constexpr size_t K3_LDS_BUDGET = 80 * 1024;  // double-buffer only while two workgroups fit a CU
 
-template <class T, int KXM, int KZM, int XB>
+template <class T, int KXM, int KZM, int XB, bool RESID>
 __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
-    const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ mask,
-    T* __restrict__ out, const T* __restrict__ wo, const float* __restrict__ to,
+    const T* __restrict__ x, ZIn<T, RESID> z, const T* __restrict__ mask, ZOut<T, RESID> out,
+    const T* __restrict__ wo, const float* __restrict__ to,
     const T* __restrict__ wg, const float* __restrict__ tg, int n, int np, int cz, int czp, int c,
     int cp, int mask_all, int nbuf, int total_tiles) {
   constexpr int E = Traits<T>::E;
@@ -230,9 +237,12 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
 #pragma unroll
       for (int jj = 0; jj < UPW; ++jj) {
         if (uok[jj] && j < n) {
-          T* dst = out + (((size_t)bb * n + i) * n + j) * cz + oc0[jj];
-          store4(dst, gate_mul(ap[jj][0] * m, ag[jj][0]), gate_mul(ap[jj][1] * m, ag[jj][1]),
-                 gate_mul(ap[jj][2] * m, ag[jj][2]), gate_mul(ap[jj][3] * m, ag[jj][3]));
+          const size_t off = (((size_t)bb * n + i) * n + j) * cz + oc0[jj];
+          float o4[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o4[r] = gate_mul(ap[jj][r] * m, ag[jj][r]);
+          if constexpr (RESID) add4(o4, z + off);  // out = z + update (out may be z)
+          store4(out + off, o4[0], o4[1], o4[2], o4[3]);
         }
       }
     }
@@ -264,10 +274,10 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
 //     each pair: consecutive pairs are consecutive lines of `out`.
 // The next tile's x blocks, z chunks and mask values are loaded while the current one is
 // computed.
-template <class T, int KXM, int KZM, int ST, int UGM, int W, int XBC>
+template <class T, int KXM, int KZM, int ST, int UGM, int W, int XBC, bool RESID>
 __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
-    const T* __restrict__ x, const T* __restrict__ z, const T* __restrict__ mask,
-    T* __restrict__ out, const T* __restrict__ wo, const float* __restrict__ to,
+    const T* __restrict__ x, ZIn<T, RESID> z, const T* __restrict__ mask, ZOut<T, RESID> out,
+    const T* __restrict__ wo, const float* __restrict__ to,
     const T* __restrict__ wg, const float* __restrict__ tg, int n, int np, int cz, int czp, int c,
     int cp, int mask_all, int ug, int total_tiles) {
   constexpr int E = Traits<T>::E;
@@ -524,22 +534,39 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     const int cpp = gch / E;
     const int last = n - 1 - j0;        // last real pair of the tile (< TW when ragged)
     const size_t row0 = ((size_t)bb * n + i) * n + j0;
+    constexpr int NOUT = (TW * CPPM + 63) / 64;
+    size_t goff[NOUT];
+    int soff[NOUT];
 #pragma unroll
-    for (int k = 0; k < (TW * CPPM + 63) / 64; ++k) {
+    for (int k = 0; k < NOUT; ++k) {
       const int idx = k * 64 + lane;
       int pr = idx / CPPM, cc = idx - pr * CPPM;
       pr = pr < last ? pr : last;
       pr = pr < TW ? pr : TW - 1;
       cc = cc < cpp ? cc : cpp - 1;
-      st16(out + (row0 + pr) * cz + ch0 + cc * E, ld16(stg + pr * sst + cc * E));
+      goff[k] = (row0 + pr) * cz + ch0 + cc * E;
+      soff[k] = pr * sst + cc * E;
+    }
+    if constexpr (RESID) {
+      // out = z + update. Every z chunk is read before any chunk is written, so the
+      // duplicate stores past the row end also add the update to the original z (out may
+      // be z itself: each pair is read and written only by this wave, in this tile).
+      chunk_t zr[NOUT];
+#pragma unroll
+      for (int k = 0; k < NOUT; ++k) zr[k] = ld16(z + goff[k]);
+#pragma unroll
+      for (int k = 0; k < NOUT; ++k) st16(out + goff[k], add_chunks(ld16(stg + soff[k]), zr[k], T()));
+    } else {
+#pragma unroll
+      for (int k = 0; k < NOUT; ++k) st16(out + goff[k], ld16(stg + soff[k]));
     }
   }
 }
 
-// Shapes of the wave-independent form. Narrow rows (KXM + KZM <= 8 chunk groups): 16
-// pairs per wave tile, 16 waves per workgroup (four per SIMD, so up to 128 VGPRs each) and
-// half-width x blocks; wider rows: 16 pairs, 8 waves, full-width blocks, if the operands and
-// the next tile's loads fit the register budget.
+// Shapes of the wave-independent form: 8 waves per workgroup; narrow rows (KXM + KZM <= 8
+// chunk groups) take 32-pair wave tiles, wider rows 16-pair tiles, if the operands and the
+// next tile's loads fit the register budget. (16-pair tiles with 16 waves and half-width x
+// blocks are faster with hot caches but fetch x poorly from DRAM.)
 template <class T, int KXM, int KZM>
 struct K3WShape {
   static constexpr int E = Traits<T>::E;
@@ -564,7 +591,7 @@ static size_t k3w_lds(const StageArgs& a, int ug, int st, int waves) {
 
 // Launches the wave-independent form if some unit grouping fits LDS; *done = false leaves
 // the launch to the tile-shared form.
-template <class T, int KXM, int KZM>
+template <class T, int KXM, int KZM, bool RESID>
 static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
   *done = false;
   if constexpr (K3WShape<T, KXM, KZM>::OK) {
@@ -581,7 +608,7 @@ static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
       }
     if (ug == 0) return hipSuccess;
     const size_t lds = k3w_lds<T>(a, ug, ST, W);
-    auto fn = k3_output_gate_waves<T, KXM, KZM, ST, UGM, W, XBC>;
+    auto fn = k3_output_gate_waves<T, KXM, KZM, ST, UGM, W, XBC, RESID>;
     static std::atomic<int> granted{0};
     hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
     if (e != hipSuccess) return e;
@@ -607,7 +634,7 @@ static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
 
 // ---------------------------------------------------------------------------------------
 
-template <class T, int KXM, int KZM, int XB>
+template <class T, int KXM, int KZM, int XB, bool RESID>
 static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
   constexpr int E = Traits<T>::E;
   auto lds_for = [&](int nb) {
@@ -616,7 +643,7 @@ static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
   };
   const int nbuf = lds_for(2) <= K3_LDS_BUDGET ? 2 : 1;
   const size_t lds = lds_for(nbuf);
-  auto fn = k3_output_gate<T, KXM, KZM, XB>;
+  auto fn = k3_output_gate<T, KXM, KZM, XB, RESID>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
   if (e != hipSuccess) return e;
@@ -638,7 +665,7 @@ static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
 
 // The compiled (KX, KZ) variants are listed in launch.h (TRIMUL_K3_VARIANTS); the host
 // pads cp and czp to exactly one of them.
-template <class T>
+template <class T, bool RESID>
 static hipError_t launch_k3_dispatch(const StageArgs& a, hipStream_t st) {
   constexpr int E = Traits<T>::E;
   const int kx = a.cp / Traits<T>::KG, kz = a.czp / Traits<T>::KG;
@@ -648,10 +675,10 @@ static hipError_t launch_k3_dispatch(const StageArgs& a, hipStream_t st) {
 #define TRIMUL_CALL(X_, Z_)                                      \
   if (kx == X_ && kz == Z_) {                                    \
     bool done = false;                                           \
-    hipError_t e = launch_k3w_t<T, X_, Z_>(a, st, &done);        \
+    hipError_t e = launch_k3w_t<T, X_, Z_, RESID>(a, st, &done); \
     if (e != hipSuccess || done) return e;                       \
-    if (xb == 1) return launch_k3_t<T, X_, Z_, 1>(a, st);        \
-    if (X_ >= 8 && xb == 2) return launch_k3_t<T, X_, Z_, (X_ >= 8 ? 2 : 1)>(a, st); \
+    if (xb == 1) return launch_k3_t<T, X_, Z_, 1, RESID>(a, st); \
+    if (X_ >= 8 && xb == 2) return launch_k3_t<T, X_, Z_, (X_ >= 8 ? 2 : 1), RESID>(a, st); \
   }
   TRIMUL_K3_VARIANTS(TRIMUL_CALL)
 #undef TRIMUL_CALL
@@ -659,7 +686,11 @@ static hipError_t launch_k3_dispatch(const StageArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_k3(bool bf16_storage, const StageArgs& a, hipStream_t st) {
-  return bf16_storage ? launch_k3_dispatch<bf16>(a, st) : launch_k3_dispatch<float>(a, st);
+  if (a.residual)
+    return bf16_storage ? launch_k3_dispatch<bf16, true>(a, st)
+                        : launch_k3_dispatch<float, true>(a, st);
+  return bf16_storage ? launch_k3_dispatch<bf16, false>(a, st)
+                      : launch_k3_dispatch<float, false>(a, st);
 }
 
 }  // namespace trimul

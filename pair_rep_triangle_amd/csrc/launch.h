@@ -27,6 +27,7 @@ struct StageArgs {
   const float* tg;   // [cz]         (W_g beta_in + b_g) times -log2(e)
   const void* one;   // one element of value 1 in the storage type (stands in for no mask)
   int batch, n, np, cz, czp, c, cp, incoming, num_cus;
+  int residual;      // stage 3 writes z + update instead of the update (out may be z)
 };
 
 // k extent of one 16x16 MFMA chunk group: 32 (bf16) or 16 (fp32).

@@ -103,7 +103,7 @@ int check_device(int* dev_out, int* cus_out) {
 
 int validate_call(const tri_mul_handle* h, int stage, const void* z, const void* mask,
                   const void* out, int batch, int n, int direction, const void* ws,
-                  size_t ws_bytes) {
+                  size_t ws_bytes, bool residual) {
   if (!h) return TRI_MUL_ERR_INVALID_ARG;
   if (stage < 0 || stage > 3) return TRI_MUL_ERR_INVALID_ARG;
   if (batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N) return TRI_MUL_ERR_INVALID_ARG;
@@ -116,15 +116,18 @@ int validate_call(const tri_mul_handle* h, int stage, const void* z, const void*
   if (ws_bytes < L.total) return TRI_MUL_ERR_WORKSPACE_TOO_SMALL;
   const size_t pairs = (size_t)batch * n * n;
   const size_t zb = pairs * h->c_z * L.esz, mb = pairs * L.esz;
-  if (overlaps(out, zb, z, zb) || overlaps(out, zb, mask, mb) || overlaps(out, zb, ws, L.total) ||
+  // with the residual add, out may be z itself (in place) but not overlap it otherwise
+  const bool in_place = residual && out == z;
+  if ((!in_place && overlaps(out, zb, z, zb)) || overlaps(out, zb, mask, mb) ||
+      overlaps(out, zb, ws, L.total) ||
       overlaps(ws, L.total, z, zb) || overlaps(ws, L.total, mask, mb))
     return TRI_MUL_ERR_ALIAS;
   return TRI_MUL_OK;
 }
 
 int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out, int batch, int n,
-        int direction, void* ws, size_t ws_bytes, void* stream) {
-  int rc = validate_call(h, stage, z, mask, out, batch, n, direction, ws, ws_bytes);
+        int direction, void* ws, size_t ws_bytes, void* stream, bool residual = false) {
+  int rc = validate_call(h, stage, z, mask, out, batch, n, direction, ws, ws_bytes, residual);
   if (rc != TRI_MUL_OK) return rc;
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
@@ -143,6 +146,7 @@ int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out
   a.np = L.np;
   a.incoming = direction == TRI_MUL_INCOMING;
   a.num_cus = h->num_cus;
+  a.residual = residual ? 1 : 0;
   hipStream_t st = (hipStream_t)stream;
   if (stage == 0 || stage == 1) {
     e = trimul::launch_k1(h->bf16, a, st);
@@ -282,6 +286,13 @@ int tri_mul_workspace_layout(const tri_mul_handle* h, int batch, int n, tri_mul_
 int tri_mul_forward(tri_mul_handle* h, const void* z, const void* pair_mask, void* out, int batch,
                     int n, int direction, void* workspace, size_t workspace_bytes, void* stream) {
   return run(h, 0, z, pair_mask, out, batch, n, direction, workspace, workspace_bytes, stream);
+}
+
+int tri_mul_forward_residual(tri_mul_handle* h, const void* z, const void* pair_mask, void* z_out,
+                             int batch, int n, int direction, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return run(h, 0, z, pair_mask, z_out, batch, n, direction, workspace, workspace_bytes, stream,
+             true);
 }
 
 int tri_mul_forward_stage(tri_mul_handle* h, int stage, const void* z, const void* pair_mask,

@@ -24,8 +24,8 @@ ERRORS = {
     -5: "ALIAS", -6: "WORKSPACE_TOO_SMALL", -7: "HIP", -8: "OUT_OF_MEMORY",
 }
 EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
-           "tri_mul_forward", "tri_mul_forward_stage", "tri_mul_destroy", "tri_mul_strerror",
-           "tri_mul_last_hip_error")
+           "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage",
+           "tri_mul_destroy", "tri_mul_strerror", "tri_mul_last_hip_error")
 
 
 class TriMulError(RuntimeError):
@@ -62,6 +62,7 @@ def load_library(path=LIB_PATH):
     lib.tri_mul_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.tri_mul_workspace_layout.argtypes = [vp, i, i, ctypes.POINTER(Layout)]
     lib.tri_mul_forward.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+    lib.tri_mul_forward_residual.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_forward_stage.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_destroy.argtypes = [vp]
     lib.tri_mul_destroy.restype = None
@@ -70,7 +71,7 @@ def load_library(path=LIB_PATH):
     lib.tri_mul_last_hip_error.argtypes = []
     lib.tri_mul_last_hip_error.restype = ctypes.c_char_p
     for name in ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
-                 "tri_mul_forward", "tri_mul_forward_stage"):
+                 "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage"):
         getattr(lib, name).restype = i
     _lib = lib
     return lib
@@ -180,6 +181,13 @@ class TriMul:
         return out
 
     __call__ = forward
+
+    def forward_residual(self, z, mask=None, out=None, direction="outgoing", workspace=None,
+                         stream=None):
+        """out = z + update (out may be z itself for an in-place pair update)."""
+        args, out, _ = self._args(z, mask, out, workspace, direction, stream)
+        _check(self.lib.tri_mul_forward_residual(self._h, *args), "tri_mul_forward_residual")
+        return out
 
     def stage(self, stage, z, mask=None, out=None, direction="outgoing", workspace=None,
               stream=None):

@@ -37,6 +37,34 @@ def test_bruteforce(direction, B, N, c_z, c, mask):
     np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
 
 
+# --- residual add and the chained pair update, against brute force ------------------------
+
+@pytest.mark.parametrize("B,N,c_z,c,mask", [
+    (1, 3, 2, 2, "ones"), (2, 4, 3, 2, "block"), (1, 4, 2, 3, "random_pairs"),
+])
+def test_pair_update_bruteforce(B, N, c_z, c, mask):
+    z, m, w_out = _case(B, N, c_z, c, seed=50 + N, mask=mask, random_affine=True)
+    w_in = make_random(B, N, c_z, c, seed=60 + N, random_affine=True)["weights"]
+    z1 = z + np.array(brute_force(z.tolist(), m.tolist(), _tolist(w_out), "outgoing"))
+    z2 = z1 + np.array(brute_force(z1.tolist(), m.tolist(), _tolist(w_in), "incoming"))
+    np.testing.assert_allclose(ref.tri_mul_residual_ref(z, m, w_out, "outgoing"), z1,
+                               rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(ref.pair_update_ref(z, m, w_out, w_in), z2, rtol=1e-12, atol=1e-12)
+    # the order matters: incoming first gives another result
+    swapped = ref.tri_mul_residual_ref(ref.tri_mul_residual_ref(z, m, w_in, "incoming"), m,
+                                       w_out, "outgoing")
+    assert np.abs(swapped - z2).max() > 1e-6
+
+
+def test_pair_update_leaves_padded_pairs():
+    z, m, w_out = _case(1, 6, 3, 2, seed=71, mask="block", valid=[4])
+    w_in = make_random(1, 6, 3, 2, seed=72)["weights"]
+    z2 = ref.pair_update_ref(z, m, w_out, w_in)
+    pad = m == 0
+    assert pad.any()
+    assert np.array_equal(z2[pad], z[pad])
+
+
 # --- independent composition of torch library routines in float64 -------------------------
 
 def torch_compose(z, m, w, direction, eps=1e-5):
