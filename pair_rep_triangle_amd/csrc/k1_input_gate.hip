@@ -262,6 +262,338 @@ __global__ __launch_bounds__(64 * W) void k1_input_gate(
 }
 
 // ---------------------------------------------------------------------------------------
+// Wave-independent form for c_z of four chunk groups (97..128 channels in bf16, 49..64 in
+// fp32: sixteen 16-byte chunks per weight row). A workgroup of 8 waves copies the
+// gate/projection rows of its group of units (a unit = 16 channels of a or b) into LDS
+// once; then every wave runs its own loop over 64-pair tiles (one storage row, 64
+// consecutive columns) with no workgroup barrier:
+//   - z comes straight from global memory into MFMA operand layout and is normalised in
+//     registers. Row i of the A operand of subtile st (st = 0..3) holds pair
+//     16*(i/4) + 4*st + i%4 of the tile, so that accumulator register rr of lane
+//     (p, q) = (lane%16, lane/16) is pair 16q + 4st + rr, channel p: across the subtiles a
+//     lane holds 16 consecutive pairs of one channel and writes them as whole 16-byte
+//     pieces of the [c][Np][Np] operand, with no staging;
+//   - per unit, the gate and projection rows (the B operand) come from LDS and the start
+//     vectors initialise the accumulators; the epilogue is m * p / (1 + 2^g);
+//   - units go two at a time through a software pipeline: the MFMAs of one unit are
+//     issued alongside the epilogue of the previous one.
+// In LDS a weight row is sixteen chunks with chunk c at position c ^ (row & 15), which
+// keeps the reads free of bank conflicts without padding.
+// Issue priority from a wave's progress (level = half tiles done): the wave of a SIMD that
+// is behind issues first, so the two waves sharing a SIMD finish together instead of the
+// younger one running alone at the end.
+__device__ __forceinline__ void progress_priority(int level) {
+  if (level <= 0) __builtin_amdgcn_s_setprio(3);
+  else if (level == 1) __builtin_amdgcn_s_setprio(2);
+  else if (level == 2) __builtin_amdgcn_s_setprio(1);
+  else __builtin_amdgcn_s_setprio(0);
+}
+
+constexpr int K1W_WAVES = 8;
+constexpr int K1W_THREADS = 64 * K1W_WAVES;
+constexpr int K1W_TP = 64;  // pairs per wave tile
+
+template <class T>
+__global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
+    const T* __restrict__ z, const T* __restrict__ mask, T* __restrict__ a_out,
+    T* __restrict__ b_out, const T* __restrict__ w1, const float* __restrict__ t1, int n, int np,
+    int cz, int c, int incoming, int mask_all, int ug, int total_tiles) {
+  constexpr int E = Traits<T>::E;
+  constexpr int KG = Traits<T>::KG;
+  constexpr int KZ = 4;               // chunk groups along c_z
+  constexpr int RC = KZ * KG / E;     // 16 chunks per weight row
+  constexpr int ST = K1W_TP / 16;     // 16-pair subtiles per tile
+  constexpr int NOUT = 16 / E;        // 16-byte stores per lane and unit (16 pairs)
+  static_assert(RC == 16, "chunk count the swizzle assumes");
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int czp = KZ * KG;
+  const int rows = ug * 32;  // gate and projection rows of this group's units
+  T* const wl = (T*)smem;                                 // [rows][czp], swizzled chunks
+  float* const tl = (float*)(wl + (size_t)rows * czp);    // [rows]
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* const mb = tl + rows + wave * K1W_TP;            // per-wave tile masks [64]
+  const int p = lane & 15, q = lane >> 4;
+  const int cblocks = c / 16;
+  const int u0 = blockIdx.y * ug;  // first unit of this group
+  const size_t plane = (size_t)np * np;
+  const int ntx = np / K1W_TP;
+  const int arow = 16 * (p >> 2) + (p & 3);  // tile pair of A row p in subtile 0 (+4 per st)
+
+  // ---- the group's weight rows and start values -> LDS (all loads issued first) ----
+  // LDS row lr = 32*uu + 16*gp + r holds device row (2*uq + gp)*c + ucb + r of unit u0+uu
+  auto dev_row = [&](int lr) {
+    const int uu = lr >> 5, gp = (lr >> 4) & 1, r = lr & 15;
+    const int u = u0 + uu, uq = u / cblocks, ucb = (u - uq * cblocks) * 16;
+    return (2 * uq + gp) * c + ucb + r;
+  };
+  {
+    constexpr int NW = (16 * 32 * RC + K1W_THREADS - 1) / K1W_THREADS;  // at most 16 units
+    chunk_t v[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
+      v[k] = ld16(w1 + (size_t)dev_row(lr < rows ? lr : 0) * czp + cc * E);
+    }
+    const float tv = tid < rows ? t1[dev_row(tid)] : 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
+      if (lr < rows) st16(wl + lr * czp + ((cc ^ (lr & 15)) * E), v[k]);
+    }
+    if (tid < rows) tl[tid] = tv;
+  }
+  __syncthreads();
+
+  // tile t -> (bb, r, sx): storage row r, columns sx*64 .. +63; the z pairs are (r, s)
+  // outgoing and (s, r) incoming
+  auto coords = [&](int t, int& bb, int& r, int& s0) {
+    bb = t / (np * ntx);
+    const int rem = t - bb * np * ntx;
+    r = rem / ntx;
+    s0 = (rem - r * ntx) * K1W_TP;
+  };
+  struct Pre {
+    chunk_t zv[ST][KZ];
+    T m[ST];
+  };
+  auto fetch = [&](int t, Pre& f) {
+    int bb, r, s0;
+    coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);  // waves past the end refetch
+    const bool row_ok = r < n;
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const int s = s0 + arow + 4 * st;
+      const bool ok = row_ok && s < n;
+      const int rr = ok ? r : 0, ss = ok ? s : 0;
+      const size_t pair = incoming ? ((size_t)bb * n + ss) * n + rr : ((size_t)bb * n + rr) * n + ss;
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) {
+        const int ch = ks * KG + q * E;
+        f.zv[st][ks] = ld16(z + pair * cz + (ch < cz ? ch : 0));
+      }
+      f.m[st] = mask[mask_all ? 0 : pair];
+    }
+  };
+
+  typedef chunk_t WUnit[2][KZ];  // gate and projection chunks of one unit
+  typedef f32x4 AUnit[ST][2];    // gate and projection accumulators of one unit
+
+  const int gw = blockIdx.x * K1W_WAVES + wave;
+  const int nw = gridDim.x * K1W_WAVES;
+
+  // Tile t's fetched z -> normalised A operand in za; masks -> m4 (lane (p, q): pairs
+  // 16q + 4st + rr). Pairs outside n x n become zero rows with mask 0 (branch-free). The
+  // pass runs at the end of the previous tile, right after the fetch and the last stores,
+  // so its waits count only those.
+  chunk_t za[ST][KZ];
+  f32x4 m4[ST];
+  Pre f;
+  auto prepare = [&](int t) {
+    int bb, r, s0;
+    coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);
+    int opaque;  // keeps the loop-invariant masks inside the loop
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+    float mv[ST];
+#pragma unroll
+    for (int st = 0; st < ST; ++st) {
+      const unsigned int okm = 0u - (unsigned int)(r < n && s0 + arow + 4 * st < n);
+      mv[st] = __uint_as_float(__float_as_uint(to_f32(f.m[st])) & okm);
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) {
+        const unsigned int keep = 0u - (unsigned int)(ks * KG + q * E + opaque < cz);
+        za[st][ks] = f.zv[st][ks] & (okm & keep);
+      }
+    }
+    // A row p of subtile st -> mb[st*16 + p] (lanes of equal p write equal values), read
+    // back as the four pairs 16q + 4st + 0..3 = A rows 4q..4q+3
+#pragma unroll
+    for (int st = 0; st < ST; ++st) mb[st * 16 + p] = mv[st];
+    wave_lds_sync();
+#pragma unroll
+    for (int st = 0; st < ST; ++st) m4[st] = ld16f(mb + st * 16 + 4 * q);
+#pragma unroll
+    for (int st = 0; st < ST; ++st) normalize_operand_row<KZ>(za[st], cz, lane, T());
+  };
+
+  fetch(gw, f);
+  prepare(gw);
+  int done = 0;  // tiles this wave has finished
+  for (int t = gw; t < total_tiles; t += nw) {
+    int bb, r, s0;
+    coords(t, bb, r, s0);
+    int opaque;  // keeps the loop-invariant LDS reads inside the loop
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+    // this lane's 16 pairs of channel p (the unit's channel block is added per unit)
+    const size_t tbase = (size_t)bb * c * plane + (size_t)p * plane + (size_t)r * np + s0 + 16 * q;
+    const T* const wlt = wl + opaque;
+    const float* const tlt = tl + opaque;
+
+    // unit uu's weights (B operand) and start values from LDS
+    auto load_w = [&](int uu, WUnit& w, float (&bias)[2]) {
+      const int lr0 = uu * 32 + p;  // gate row; the projection row is 16 further
+      bias[0] = tlt[lr0];
+      bias[1] = tlt[lr0 + 16];
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) {
+        const int pos = ((ks * 4 + q) ^ p) * E;
+        w[0][ks] = ld16(wlt + lr0 * czp + pos);
+        w[1][ks] = ld16(wlt + (lr0 + 16) * czp + pos);
+      }
+    };
+    auto mma_unit = [&](const WUnit& w, const float (&bias)[2], AUnit& acc) {
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        acc[st][0] = f32x4{bias[0], bias[0], bias[0], bias[0]};
+        acc[st][1] = f32x4{bias[1], bias[1], bias[1], bias[1]};
+      }
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks)
+#pragma unroll
+        for (int st = 0; st < ST; ++st) {
+          acc[st][0] = mma16(acc[st][0], za[st][ks], w[0][ks], T());
+          acc[st][1] = mma16(acc[st][1], za[st][ks], w[1][ks], T());
+        }
+    };
+    // output row block of unit uu: channel rows ucb .. ucb+15 of a or b
+    auto unit_dst = [&](int uu) {
+      const int u = u0 + uu;
+      const bool isb = u >= cblocks;  // units 0 .. c/16-1 are a, the rest b
+      return (isb ? b_out : a_out) + tbase + (size_t)((isb ? u - cblocks : u) * 16) * plane;
+    };
+    // 16 outputs (pairs 16q .. 16q+15 of channel p) -> two (bf16) or four (fp32) 16-byte
+    // stores
+    auto store16 = [&](T* dst, const float (&o)[16]) {
+      T ot[16];
+#pragma unroll
+      for (int j = 0; j < 16; j += 4) store4(ot + j, o[j], o[j + 1], o[j + 2], o[j + 3]);
+#pragma unroll
+      for (int k = 0; k < NOUT; ++k) st16(dst + k * E, ld16(ot + k * E));
+    };
+    // m * p / (1 + 2^g) of one unit, on its own (the last unit of a tile)
+    auto emit = [&](T* dst, const AUnit& acc) {
+      float o[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        o[j] = gate_mul(acc[j >> 2][1][j & 3] * m4[j >> 2][j & 3], acc[j >> 2][0][j & 3]);
+      store16(dst, o);
+    };
+    // One pipeline step, scheduled by hand: the 32 MFMAs of a unit (weights w, start values
+    // bias -> acc), each followed by two or three VALU instructions of the previous unit's
+    // epilogue (old -> dst), so that matrix and vector work issue side by side from one
+    // wave; the next unit's weights are read from LDS in the first slots. The epilogue of
+    // value v (pair 16q + v) runs as a five-stage pipeline over the slots -- exp2 and p*m in
+    // slot 2v, +1 in slot 2v+1, the reciprocal in slot 2v+2, the product in slot 2v+5 --
+    // so no instruction of a slot waits on another of the same slot.
+    auto step = [&](const WUnit& w, const float (&bias)[2], AUnit& acc, const AUnit& old,
+                    T* dst, bool load_next, int next_uu, WUnit& wn, float (&bn)[2]) {
+      const f32x4 bg = {bias[0], bias[0], bias[0], bias[0]};
+      const f32x4 bp = {bias[1], bias[1], bias[1], bias[1]};
+      float e[16], a[16], d[16], r[16], o[16];
+      const int lr0 = next_uu * 32 + p;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        const int ks = k >> 3, st = (k >> 1) & 3, gp = k & 1;
+        acc[st][gp] = mma16(ks == 0 ? (gp ? bp : bg) : acc[st][gp], za[st][ks], w[gp][ks], T());
+        if (load_next && k < 8) {
+          const int nks = k >> 1, ngp = k & 1;
+          wn[ngp][nks] = ld16(wlt + (lr0 + 16 * ngp) * czp + (((nks * 4 + q) ^ p) * E));
+          if (k == 7) {
+            bn[0] = tlt[lr0];
+            bn[1] = tlt[lr0 + 16];
+          }
+        }
+        const int v = k >> 1;
+        // the empty volatile statements pin each slot's results in program order
+        if ((k & 1) == 0) {
+          e[v] = __builtin_amdgcn_exp2f(old[v >> 2][0][v & 3]);
+          a[v] = old[v >> 2][1][v & 3] * m4[v >> 2][v & 3];
+          if (v >= 1) {
+            r[v - 1] = __builtin_amdgcn_rcpf(d[v - 1]);
+            asm volatile("" : "+v"(acc[st][gp]), "+v"(e[v]), "+v"(a[v]), "+v"(r[v - 1]));
+          } else {
+            asm volatile("" : "+v"(acc[st][gp]), "+v"(e[v]), "+v"(a[v]));
+          }
+        } else {
+          d[v] = 1.0f + e[v];
+          if (v >= 2) {
+            o[v - 2] = a[v - 2] * r[v - 2];
+            asm volatile("" : "+v"(acc[st][gp]), "+v"(d[v]), "+v"(o[v - 2]));
+          } else {
+            asm volatile("" : "+v"(acc[st][gp]), "+v"(d[v]));
+          }
+        }
+      }
+      r[15] = __builtin_amdgcn_rcpf(d[15]);
+      o[14] = a[14] * r[14];
+      o[15] = a[15] * r[15];
+      store16(dst, o);
+    };
+
+    // Software pipeline over the group's units, two at a time (ug is even).
+    progress_priority(2 * done);
+    WUnit wa, wb;
+    float ba[2], bbias[2];
+    AUnit acca, accb;
+    load_w(0, wa, ba);
+    mma_unit(wa, ba, acca);
+    load_w(1, wb, bbias);
+#pragma unroll 1
+    for (int uu = 0; uu + 2 < ug; uu += 2) {
+      step(wb, bbias, accb, acca, unit_dst(uu), true, uu + 2, wa, ba);         // MFMA uu+1
+      step(wa, ba, acca, accb, unit_dst(uu + 1), true, uu + 3, wb, bbias);     // MFMA uu+2
+      if (2 * (uu + 2) == ug) progress_priority(2 * done + 1);
+    }
+    step(wb, bbias, accb, acca, unit_dst(ug - 2), false, 0, wa, ba);           // MFMA ug-1
+    fetch(t + nw, f);             // za is dead: the next tile's z loads go out now
+    emit(unit_dst(ug - 1), accb);
+    prepare(t + nw);
+    ++done;
+  }
+}
+
+template <class T>
+static size_t k1w_lds(int ug) {
+  constexpr int czp = 4 * Traits<T>::KG;
+  return (size_t)ug * 32 * czp * sizeof(T) + (size_t)ug * 32 * sizeof(float) +
+         (size_t)K1W_WAVES * K1W_TP * sizeof(float);
+}
+
+// Launches the wave-independent form if the units split into groups that fit LDS;
+// *done = false leaves the launch to the tile-shared form.
+template <class T>
+static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
+  *done = false;
+  const int units = 2 * (a.c / 16);
+  int ug = 0;
+  for (int g = units < 16 ? units : 16; g >= 2; g -= 2)  // even: units go in pairs
+    if (units % g == 0 && k1w_lds<T>(g) <= LDS_PER_CU) {
+      ug = g;
+      break;
+    }
+  if (ug == 0) return hipSuccess;
+  const size_t lds = k1w_lds<T>(ug);
+  auto fn = k1_input_gate_waves<T>;
+  static std::atomic<int> granted{0};
+  hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
+  if (e != hipSuccess) return e;
+  const int groups = units / ug;
+  const int total = a.batch * a.np * (a.np / K1W_TP);
+  static std::atomic<int> occ{0};
+  static std::atomic<size_t> occ_lds{0};
+  const int per_cu = resident_blocks((const void*)fn, K1W_THREADS, lds, occ, occ_lds);
+  const int cap = a.num_cus * per_cu / groups > 0 ? a.num_cus * per_cu / groups : 1;
+  const int need = (total + K1W_WAVES - 1) / K1W_WAVES;
+  const int blocks = need < cap ? need : cap;
+  const int mask_all = a.mask == nullptr;
+  hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K1W_THREADS), lds, st, (const T*)a.z,
+                     (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b, (const T*)a.w1,
+                     a.t1, a.n, a.np, a.cz, a.c, a.incoming, mask_all, ug, total);
+  *done = true;
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 
 template <class T, int KMAX, int UPW, int W>
 static hipError_t launch_k1_t(const StageArgs& a, hipStream_t st) {
@@ -298,7 +630,12 @@ static hipError_t launch_k1_dispatch(const StageArgs& a, hipStream_t st) {
   switch (a.czp / Traits<T>::KG) {
     case 1: return launch_k1_t<T, 1, 2, 8>(a, st);
     case 2: return launch_k1_t<T, 2, 2, 8>(a, st);
-    case 4: return launch_k1_t<T, 4, 1, 16>(a, st);
+    case 4: {
+      bool done = false;
+      hipError_t e = launch_k1w<T>(a, st, &done);
+      if (e != hipSuccess || done) return e;
+      return launch_k1_t<T, 4, 1, 16>(a, st);
+    }
     case 8: return launch_k1_t<T, 8, 1, 8>(a, st);
     case 12: return launch_k1_t<T, 12, 1, 8>(a, st);
     case 16: return launch_k1_t<T, 16, 1, 8>(a, st);
