@@ -17,6 +17,8 @@
 // The next tile's z is fetched into registers while the MFMAs of the current tile run.
 // Results are staged per wave in LDS and written as whole rows of TP contiguous pairs.
 
+#include <type_traits>
+
 #include "device_common.h"
 
 namespace trimul {
@@ -320,31 +322,6 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   const int ntx = np / K1W_TP;
   const int arow = 16 * (p >> 2) + (p & 3);  // tile pair of A row p in subtile 0 (+4 per st)
 
-  // ---- the group's weight rows and start values -> LDS (all loads issued first) ----
-  // LDS row lr = 32*uu + 16*gp + r holds device row (2*uq + gp)*c + ucb + r of unit u0+uu
-  auto dev_row = [&](int lr) {
-    const int uu = lr >> 5, gp = (lr >> 4) & 1, r = lr & 15;
-    const int u = u0 + uu, uq = u / cblocks, ucb = (u - uq * cblocks) * 16;
-    return (2 * uq + gp) * c + ucb + r;
-  };
-  {
-    constexpr int NW = (16 * 32 * RC + K1W_THREADS - 1) / K1W_THREADS;  // at most 16 units
-    chunk_t v[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
-      v[k] = ld16(w1 + (size_t)dev_row(lr < rows ? lr : 0) * czp + cc * E);
-    }
-    const float tv = tid < rows ? t1[dev_row(tid)] : 0.f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
-      if (lr < rows) st16(wl + lr * czp + ((cc ^ (lr & 15)) * E), v[k]);
-    }
-    if (tid < rows) tl[tid] = tv;
-  }
-  __syncthreads();
-
   // tile t -> (bb, r, sx): storage row r, columns sx*64 .. +63; the z pairs are (r, s)
   // outgoing and (s, r) incoming
   auto coords = [&](int t, int& bb, int& r, int& s0) {
@@ -376,11 +353,39 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     }
   };
 
+  const int gw = blockIdx.x * K1W_WAVES + wave;
+  const int nw = gridDim.x * K1W_WAVES;
+  Pre f;
+  fetch(gw, f);  // the first tile's z is in flight while the weights go to LDS
+
+  // ---- the group's weight rows and start values -> LDS (all loads issued first) ----
+  // LDS row lr = 32*uu + 16*gp + r holds device row (2*uq + gp)*c + ucb + r of unit u0+uu
+  auto dev_row = [&](int lr) {
+    const int uu = lr >> 5, gp = (lr >> 4) & 1, r = lr & 15;
+    const int u = u0 + uu, uq = u / cblocks, ucb = (u - uq * cblocks) * 16;
+    return (2 * uq + gp) * c + ucb + r;
+  };
+  {
+    constexpr int NW = (16 * 32 * RC + K1W_THREADS - 1) / K1W_THREADS;  // at most 16 units
+    chunk_t v[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
+      v[k] = ld16(w1 + (size_t)dev_row(lr < rows ? lr : 0) * czp + cc * E);
+    }
+    const float tv = tid < rows ? t1[dev_row(tid)] : 0.f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
+      if (lr < rows) st16(wl + lr * czp + ((cc ^ (lr & 15)) * E), v[k]);
+    }
+    if (tid < rows) tl[tid] = tv;
+  }
+  __syncthreads();
+
   typedef chunk_t WUnit[2][KZ];  // gate and projection chunks of one unit
   typedef f32x4 AUnit[ST][2];    // gate and projection accumulators of one unit
 
-  const int gw = blockIdx.x * K1W_WAVES + wave;
-  const int nw = gridDim.x * K1W_WAVES;
 
   // Tile t's fetched z -> normalised A operand in za; masks -> m4 (lane (p, q): pairs
   // 16q + 4st + rr). Pairs outside n x n become zero rows with mask 0 (branch-free). The
@@ -388,7 +393,7 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   // so its waits count only those.
   chunk_t za[ST][KZ];
   f32x4 m4[ST];
-  Pre f;
+  bool ones = false;  // every mask value of the tile is 1 (wave-uniform)
   auto prepare = [&](int t) {
     int bb, r, s0;
     coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);
@@ -409,6 +414,7 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     // back as the four pairs 16q + 4st + 0..3 = A rows 4q..4q+3
 #pragma unroll
     for (int st = 0; st < ST; ++st) mb[st * 16 + p] = mv[st];
+    ones = __all(mv[0] == 1.f && mv[1] == 1.f && mv[2] == 1.f && mv[3] == 1.f);
     wave_lds_sync();
 #pragma unroll
     for (int st = 0; st < ST; ++st) m4[st] = ld16f(mb + st * 16 + 4 * q);
@@ -416,7 +422,6 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     for (int st = 0; st < ST; ++st) normalize_operand_row<KZ>(za[st], cz, lane, T());
   };
 
-  fetch(gw, f);
   prepare(gw);
   int done = 0;  // tiles this wave has finished
   for (int t = gw; t < total_tiles; t += nw) {
@@ -471,11 +476,13 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
       for (int k = 0; k < NOUT; ++k) st16(dst + k * E, ld16(ot + k * E));
     };
     // m * p / (1 + 2^g) of one unit, on its own (the last unit of a tile)
-    auto emit = [&](T* dst, const AUnit& acc) {
+    auto emit = [&](T* dst, const AUnit& acc, auto masked) {
       float o[16];
 #pragma unroll
-      for (int j = 0; j < 16; ++j)
-        o[j] = gate_mul(acc[j >> 2][1][j & 3] * m4[j >> 2][j & 3], acc[j >> 2][0][j & 3]);
+      for (int j = 0; j < 16; ++j) {
+        const float pm = masked ? acc[j >> 2][1][j & 3] * m4[j >> 2][j & 3] : acc[j >> 2][1][j & 3];
+        o[j] = gate_mul(pm, acc[j >> 2][0][j & 3]);
+      }
       store16(dst, o);
     };
     // One pipeline step, scheduled by hand: the 32 MFMAs of a unit (weights w, start values
@@ -486,7 +493,8 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     // slot 2v, +1 in slot 2v+1, the reciprocal in slot 2v+2, the product in slot 2v+5 --
     // so no instruction of a slot waits on another of the same slot.
     auto step = [&](const WUnit& w, const float (&bias)[2], AUnit& acc, const AUnit& old,
-                    T* dst, bool load_next, int next_uu, WUnit& wn, float (&bn)[2]) {
+                    T* dst, bool load_next, int next_uu, WUnit& wn, float (&bn)[2],
+                    auto masked) {
       const f32x4 bg = {bias[0], bias[0], bias[0], bias[0]};
       const f32x4 bp = {bias[1], bias[1], bias[1], bias[1]};
       float e[16], a[16], d[16], r[16], o[16];
@@ -507,7 +515,7 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
         // the empty volatile statements pin each slot's results in program order
         if ((k & 1) == 0) {
           e[v] = __builtin_amdgcn_exp2f(old[v >> 2][0][v & 3]);
-          a[v] = old[v >> 2][1][v & 3] * m4[v >> 2][v & 3];
+          a[v] = masked ? old[v >> 2][1][v & 3] * m4[v >> 2][v & 3] : old[v >> 2][1][v & 3];
           if (v >= 1) {
             r[v - 1] = __builtin_amdgcn_rcpf(d[v - 1]);
             asm volatile("" : "+v"(acc[st][gp]), "+v"(e[v]), "+v"(a[v]), "+v"(r[v - 1]));
@@ -530,23 +538,30 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
       store16(dst, o);
     };
 
-    // Software pipeline over the group's units, two at a time (ug is even).
-    progress_priority(2 * done);
-    WUnit wa, wb;
-    float ba[2], bbias[2];
-    AUnit acca, accb;
-    load_w(0, wa, ba);
-    mma_unit(wa, ba, acca);
-    load_w(1, wb, bbias);
+    // Software pipeline over the group's units, two at a time (ug is even). Tiles whose
+    // mask is all ones skip the multiply by m.
+    auto run_units = [&](auto masked) {
+      progress_priority(2 * done);
+      WUnit wa, wb;
+      float ba[2], bbias[2];
+      AUnit acca, accb;
+      load_w(0, wa, ba);
+      mma_unit(wa, ba, acca);
+      load_w(1, wb, bbias);
 #pragma unroll 1
-    for (int uu = 0; uu + 2 < ug; uu += 2) {
-      step(wb, bbias, accb, acca, unit_dst(uu), true, uu + 2, wa, ba);         // MFMA uu+1
-      step(wa, ba, acca, accb, unit_dst(uu + 1), true, uu + 3, wb, bbias);     // MFMA uu+2
-      if (2 * (uu + 2) == ug) progress_priority(2 * done + 1);
-    }
-    step(wb, bbias, accb, acca, unit_dst(ug - 2), false, 0, wa, ba);           // MFMA ug-1
-    fetch(t + nw, f);             // za is dead: the next tile's z loads go out now
-    emit(unit_dst(ug - 1), accb);
+      for (int uu = 0; uu + 2 < ug; uu += 2) {
+        step(wb, bbias, accb, acca, unit_dst(uu), true, uu + 2, wa, ba, masked);      // MFMA uu+1
+        step(wa, ba, acca, accb, unit_dst(uu + 1), true, uu + 3, wb, bbias, masked);  // MFMA uu+2
+        if (2 * (uu + 2) == ug) progress_priority(2 * done + 1);
+      }
+      step(wb, bbias, accb, acca, unit_dst(ug - 2), false, 0, wa, ba, masked);        // MFMA ug-1
+      fetch(t + nw, f);  // za is dead: the next tile's z loads go out now
+      emit(unit_dst(ug - 1), accb, masked);
+    };
+    if (ones)
+      run_units(std::false_type{});
+    else
+      run_units(std::true_type{});
     prepare(t + nw);
     ++done;
   }
