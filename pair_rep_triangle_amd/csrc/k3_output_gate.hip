@@ -274,6 +274,14 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
 //     each pair: consecutive pairs are consecutive lines of `out`.
 // The next tile's x blocks, z chunks and mask values are loaded while the current one is
 // computed.
+// one element of the storage type through a buffer resource
+__device__ __forceinline__ bf16 load_elem(__amdgpu_buffer_rsrc_t r, int voff, bf16) {
+  return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0));
+}
+__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t r, int voff, float) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
+}
+
 template <class T, int KXM, int KZM, int ST, int UGM, int W, int XBC, bool RESID>
 __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     const T* __restrict__ x, ZIn<T, RESID> z, const T* __restrict__ mask, ZOut<T, RESID> out,
@@ -351,31 +359,56 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     chunk_t zv[ST][KZM];
     T m[ST];
   };
-  // unconditional loads from clamped in-bounds addresses; selects happen at use
+  // The loads are buffer loads: a scalar base and byte offset per tile plus a per-lane
+  // offset that is the same in every tile. No address arithmetic lands in a register a
+  // load still has to read, so the loads issue back to back. The z and mask resources end
+  // at the row end n: pairs past it read as zero (their mask is 0). Every load is
+  // unconditional; selects happen at use.
+  unsigned int xoff[XBM][XBC], zoff[ST][KZM], moff[ST];
+#pragma unroll
+  for (int k = 0; k < XBM; ++k) {
+    const int blk = lane + 64 * k;
+    const int bl = blk < xblocks ? blk : 0;
+    const int o = bl / cbn, cb = bl - o * cbn;
+#pragma unroll
+    for (int e = 0; e < XBC; ++e)
+      xoff[k][e] = (unsigned int)(((size_t)(cb * XBC + e) * plane + o * E) * sizeof(T));
+  }
+#pragma unroll
+  for (int st = 0; st < ST; ++st) {
+#pragma unroll
+    for (int ks = 0; ks < KZM; ++ks) {
+      const int ch = ks * KG + q * E;
+      zoff[st][ks] = (unsigned int)(((st * 16 + p) * cz + (ch < cz ? ch : 0)) * sizeof(T));
+    }
+    moff[st] = mask_all ? 0u : (unsigned int)((st * 16 + p) * sizeof(T));
+  }
   auto fetch = [&](int t, Pre& f) {
     t = t < total_tiles ? t : total_tiles - 1;  // waves without a tile fetch the last one
     const int bb = t / (n * ntw);
     const int rem = t - bb * n * ntw;
     const int i = rem / ntw, j0 = (rem - i * ntw) * TW;
+    const size_t xext = (size_t)c * plane * sizeof(T);  // below 2^31 (checked at launch)
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(x + (size_t)bb * c * plane), (short)0, (int)xext, 0x00020000);
+    const size_t row0 = ((size_t)bb * n + i) * n + j0;  // first pair of the tile
+    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(z + row0 * cz), (short)0, (int)((size_t)(n - j0) * cz * sizeof(T)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(mask_all ? mask : mask + row0), (short)0,
+        (int)(mask_all ? sizeof(T) : (size_t)(n - j0) * sizeof(T)), 0x00020000);
+    const int xs = (int)(((size_t)i * np + j0) * sizeof(T));
 #pragma unroll
-    for (int k = 0; k < XBM; ++k) {
-      const int blk = lane + 64 * k;
-      const int bl = blk < xblocks ? blk : 0;
-      const int o = bl / cbn, cb = bl - o * cbn;
-      const T* src = x + ((size_t)bb * c + cb * XBC) * plane + (size_t)i * np + j0 + o * E;
+    for (int k = 0; k < XBM; ++k)
 #pragma unroll
-      for (int e = 0; e < XBC; ++e) f.xv[k][e] = ld16(src + e * plane);
-    }
+      for (int e = 0; e < XBC; ++e)
+        f.xv[k][e] = __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xoff[k][e], xs, 0));
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
-      const int j = j0 + st * 16 + p;
-      const size_t pair = ((size_t)bb * n + i) * n + (j < n ? j : n - 1);
 #pragma unroll
-      for (int ks = 0; ks < KZM; ++ks) {
-        const int ch = ks * KG + q * E;
-        f.zv[st][ks] = ld16(z + pair * cz + (ch < cz ? ch : 0));
-      }
-      f.m[st] = mask[mask_all ? 0 : pair];
+      for (int ks = 0; ks < KZM; ++ks)
+        f.zv[st][ks] = __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(rz, (int)zoff[st][ks], 0, 0));
+      f.m[st] = load_elem(rm, (int)moff[st], T());
     }
   };
 
@@ -594,6 +627,9 @@ static size_t k3w_lds(const StageArgs& a, int ug, int st, int waves) {
 template <class T, int KXM, int KZM, bool RESID>
 static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
   *done = false;
+  // the per-lane x offsets of the wave-independent form are 32-bit byte offsets into one
+  // batch item's x: larger x goes to the tile-shared form
+  if ((size_t)a.c * a.np * a.np * sizeof(T) >= 0x80000000ull) return hipSuccess;
   if constexpr (K3WShape<T, KXM, KZM>::OK) {
     constexpr int ST = K3WShape<T, KXM, KZM>::ST;
     constexpr int W = K3WShape<T, KXM, KZM>::W;
