@@ -44,6 +44,26 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
                                    0);
 }
 
+// Buffer resources for plain byte-addressed reads: a read at or past `bytes` returns
+// zero instead of touching memory. Loads through them take a 32-bit per-lane offset and a
+// scalar offset, so per-lane offsets that stay the same from tile to tile never have to be
+// recomputed into registers a load in flight still reads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
+                                           (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
+                                           0x00020000);
+}
+__device__ __forceinline__ chunk_t load16(__amdgpu_buffer_rsrc_t r, unsigned int voff, int soff) {
+  return __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));
+}
+// one element of the storage type
+__device__ __forceinline__ bf16 load_elem(__amdgpu_buffer_rsrc_t r, unsigned int voff, int soff, bf16) {
+  return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, (int)voff, soff, 0));
+}
+__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t r, unsigned int voff, int soff, float) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, soff, 0));
+}
+
 // chunk <-> floats
 __device__ __forceinline__ void unpack(chunk_t c, float* f, bf16) {
 #pragma unroll

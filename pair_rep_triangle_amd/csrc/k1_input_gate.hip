@@ -334,22 +334,33 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     chunk_t zv[ST][KZ];
     T m[ST];
   };
+  // Buffer loads: per tile a scalar base (the tile's first pair) and an extent ending at
+  // the last real pair of its storage row; per lane a byte offset that is the same in
+  // every tile (consecutive pairs of a tile are 1 (outgoing) or n (incoming) pairs
+  // apart). Pairs past the extent, and whole tiles in padding rows, read as zero.
+  const size_t pstride = incoming ? (size_t)n : 1;  // pairs between consecutive columns
+  // lane offsets: pair arow of the tile, chunk q of the first chunk group; subtile st adds
+  // the scalar 4 * st columns, chunk group ks the immediate ks * KG elements
+  const unsigned int zoff = (unsigned int)(((size_t)arow * pstride * cz + q * E) * sizeof(T));
+  const unsigned int moff = mask_all ? 0u : (unsigned int)((size_t)arow * pstride * sizeof(T));
+  const int zstep = (int)(4 * pstride * cz * sizeof(T)), mstep = mask_all ? 0 : (int)(4 * pstride * sizeof(T));
   auto fetch = [&](int t, Pre& f) {
     int bb, r, s0;
     coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);  // waves past the end refetch
-    const bool row_ok = r < n;
+    const bool row_ok = r < n && s0 < n;
+    const size_t p0 = row_ok ? (incoming ? ((size_t)bb * n + s0) * n + r : ((size_t)bb * n + r) * n + s0) : 0;
+    const size_t cols = row_ok ? (size_t)(n - s0) : 0;  // real pairs from the first one on
+    const __amdgpu_buffer_rsrc_t rz =
+        buffer_rsrc(z + p0 * cz, cols == 0 ? 0 : ((cols - 1) * pstride + 1) * cz * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(
+        mask_all ? mask : mask + p0,
+        mask_all ? sizeof(T) : (cols == 0 ? 0 : ((cols - 1) * pstride + 1) * sizeof(T)));
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
-      const int s = s0 + arow + 4 * st;
-      const bool ok = row_ok && s < n;
-      const int rr = ok ? r : 0, ss = ok ? s : 0;
-      const size_t pair = incoming ? ((size_t)bb * n + ss) * n + rr : ((size_t)bb * n + rr) * n + ss;
 #pragma unroll
-      for (int ks = 0; ks < KZ; ++ks) {
-        const int ch = ks * KG + q * E;
-        f.zv[st][ks] = ld16(z + pair * cz + (ch < cz ? ch : 0));
-      }
-      f.m[st] = mask[mask_all ? 0 : pair];
+      for (int ks = 0; ks < KZ; ++ks)
+        f.zv[st][ks] = load16(rz, zoff + ks * KG * (unsigned int)sizeof(T), st * zstep);
+      f.m[st] = load_elem(rm, moff, st * mstep, T());
     }
   };
 
@@ -579,6 +590,8 @@ static size_t k1w_lds(int ug) {
 template <class T>
 static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
   *done = false;
+  // the per-lane z offsets are 32-bit byte offsets within one batch item's z
+  if ((size_t)a.n * a.n * a.cz * sizeof(T) >= 0x80000000ull) return hipSuccess;
   const int units = 2 * (a.c / 16);
   int ug = 0;
   for (int g = units < 16 ? units : 16; g >= 2; g -= 2)  // even: units go in pairs

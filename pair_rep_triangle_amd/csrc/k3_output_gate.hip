@@ -274,14 +274,6 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
 //     each pair: consecutive pairs are consecutive lines of `out`.
 // The next tile's x blocks, z chunks and mask values are loaded while the current one is
 // computed.
-// one element of the storage type through a buffer resource
-__device__ __forceinline__ bf16 load_elem(__amdgpu_buffer_rsrc_t r, int voff, bf16) {
-  return __builtin_bit_cast(bf16, __builtin_amdgcn_raw_buffer_load_b16(r, voff, 0, 0));
-}
-__device__ __forceinline__ float load_elem(__amdgpu_buffer_rsrc_t r, int voff, float) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, 0));
-}
-
 template <class T, int KXM, int KZM, int ST, int UGM, int W, int XBC, bool RESID>
 __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     const T* __restrict__ x, ZIn<T, RESID> z, const T* __restrict__ mask, ZOut<T, RESID> out,
@@ -389,26 +381,21 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     const int rem = t - bb * n * ntw;
     const int i = rem / ntw, j0 = (rem - i * ntw) * TW;
     const size_t xext = (size_t)c * plane * sizeof(T);  // below 2^31 (checked at launch)
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(x + (size_t)bb * c * plane), (short)0, (int)xext, 0x00020000);
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)bb * c * plane, xext);
     const size_t row0 = ((size_t)bb * n + i) * n + j0;  // first pair of the tile
-    const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(z + row0 * cz), (short)0, (int)((size_t)(n - j0) * cz * sizeof(T)), 0x00020000);
-    const __amdgpu_buffer_rsrc_t rm = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(mask_all ? mask : mask + row0), (short)0,
-        (int)(mask_all ? sizeof(T) : (size_t)(n - j0) * sizeof(T)), 0x00020000);
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(z + row0 * cz, (size_t)(n - j0) * cz * sizeof(T));
+    const __amdgpu_buffer_rsrc_t rm =
+        buffer_rsrc(mask_all ? mask : mask + row0, mask_all ? sizeof(T) : (size_t)(n - j0) * sizeof(T));
     const int xs = (int)(((size_t)i * np + j0) * sizeof(T));
 #pragma unroll
     for (int k = 0; k < XBM; ++k)
 #pragma unroll
-      for (int e = 0; e < XBC; ++e)
-        f.xv[k][e] = __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(rx, (int)xoff[k][e], xs, 0));
+      for (int e = 0; e < XBC; ++e) f.xv[k][e] = load16(rx, xoff[k][e], xs);
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
 #pragma unroll
-      for (int ks = 0; ks < KZM; ++ks)
-        f.zv[st][ks] = __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(rz, (int)zoff[st][ks], 0, 0));
-      f.m[st] = load_elem(rm, (int)moff[st], T());
+      for (int ks = 0; ks < KZM; ++ks) f.zv[st][ks] = load16(rz, zoff[st][ks], 0);
+      f.m[st] = load_elem(rm, moff[st], 0, T());
     }
   };
 
