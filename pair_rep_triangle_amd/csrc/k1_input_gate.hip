@@ -600,13 +600,16 @@ static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
       break;
     }
   if (ug == 0) return hipSuccess;
+  // each wave pays the weight copy and its first tile's loads up front: with fewer than
+  // two tiles per wave of a full grid the tile-shared form is faster
+  const int total = a.batch * a.np * (a.np / K1W_TP);
+  if (total < 2 * a.num_cus * K1W_WAVES) return hipSuccess;
   const size_t lds = k1w_lds<T>(ug);
   auto fn = k1_input_gate_waves<T>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
   if (e != hipSuccess) return e;
   const int groups = units / ug;
-  const int total = a.batch * a.np * (a.np / K1W_TP);
   static std::atomic<int> occ{0};
   static std::atomic<size_t> occ_lds{0};
   const int per_cu = resident_blocks((const void*)fn, K1W_THREADS, lds, occ, occ_lds);

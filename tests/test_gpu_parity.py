@@ -91,6 +91,20 @@ def test_ragged_full_output(batch, n, c_z, c, mask, direction, dtype):
     check_full(d, dtype, direction)
 
 
+# Four chunk groups along c_z (97..128 channels in bf16, 49..64 in fp32) with at least two
+# 64-pair tiles per wave of a full grid select the wave-independent input-gate kernel:
+# ragged row ends (n < n_pad), batch items past the first, both storage types.
+@pytest.mark.parametrize("direction", DIRS)
+@pytest.mark.parametrize("dtype,batch,n,c_z,c,mask", [
+    ("bf16", 1, 450, 128, 128, "random_pairs"), ("fp32", 1, 450, 64, 32, "block"),
+    ("bf16", 2, 300, 112, 64, "random_residues"),
+])
+def test_wave_input_gate_ragged_full_output(dtype, batch, n, c_z, c, mask, direction):
+    note(f"wave input gate {dtype} B={batch} n={n} cz={c_z} c={c} {mask} {direction}")
+    d = make_random(batch, n, c_z, c, seed=n + c_z, mask=mask, random_affine=True)
+    check_full(d, dtype, direction)
+
+
 @pytest.mark.parametrize("direction", DIRS)
 @pytest.mark.parametrize("batch,n,c_z,c,mask", [
     (1, 70, 64, 512, "random_pairs"), (1, 50, 384, 256, "block"), (2, 33, 512, 384, "ones"),
