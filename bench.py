@@ -13,7 +13,12 @@ With --chained the step is the pair update in model order instead (outgoing with
 its residual add, then incoming on that result with its residual add); the
 per-kernel region still times the plain stages.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--chained] [--no-cpu-baseline]
+The timed steps launch their six kernels one by one; --launch graph captures the
+step once in a HIP graph and times replays of it instead (the eager step time is
+reported in both cases). The per-kernel region always launches eagerly.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--chained]
+                    [--launch graph|eager] [--no-cpu-baseline]
 """
 
 import argparse
@@ -39,6 +44,9 @@ def parse():
     p.add_argument("--chained", action="store_true",
                    help="time the pair update in model order instead: outgoing with its residual "
                         "add, then incoming on that result with its residual add")
+    p.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                   help="timed steps launch their kernels one by one (default) or replay one "
+                        "captured HIP graph of the step")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
@@ -119,19 +127,36 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # timed region 1: K whole steps (outgoing + incoming), HIP events on the launch stream
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_start.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
+    # timed region 1: K whole steps (outgoing + incoming), HIP events on the launch stream;
+    # eager launches, then (--launch graph) the same step captured once and replayed K times
+    def timed(run):
+        t_start = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        wall0 = time.perf_counter()
+        t_start.record(stream)
+        for _ in range(args.steps):
+            run()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / args.steps, time.perf_counter() - wall0
+
+    ms_eager, wall = timed(step)
+    ms_step, launch = ms_eager, "eager"
+    if args.launch == "graph":
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream(dev)
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):  # a step on a side stream before capture
+            step()
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph):
+            step()
+        torch.cuda.synchronize()
+        graph.replay()  # one untimed replay
+        ms_step, wall = timed(graph.replay)
+        launch = "hipgraph"
 
     # timed region 2: the same K steps again with a HIP event after every kernel (on the
     # launch stream), for each kernel's duration inside the real K1 -> K2 -> K3 order.
@@ -203,13 +228,14 @@ def main():
     rec = {
         "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
+        "ms_per_step_eager": round(ms_eager, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
         "data": "synthetic",
         "config": {"workload": name, "batch": B, "n": n, "c_z": c_z, "c": c,
                    "valid_length": d["meta"].get("valid_length", n),
                    "directions": ("outgoing->incoming, chained with residual adds"
                                   if args.chained else "outgoing+incoming"),
-                   "mask": spec["mask"]},
+                   "mask": spec["mask"], "launch": launch},
         "pair_updates_per_s": round(pair_updates, 1),
         "wall_s": round(wall, 3),
         "roofline": roofline,
