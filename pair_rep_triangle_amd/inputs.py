@@ -69,6 +69,27 @@ def make_weights(rng, c_z, c, random_affine=False):
     return out
 
 
+def transition_weight_shapes(c_z, hidden):
+    return {"ln_gamma": (c_z,), "ln_beta": (c_z,), "w1": (hidden, c_z), "b1": (hidden,),
+            "w2": (c_z, hidden), "b2": (c_z,)}
+
+
+def make_transition_weights(rng, c_z, hidden, random_affine=False):
+    """float32 pair-transition weights (nn.Linear orientation). Matrices N(0, 1/fan_in);
+    LayerNorm gamma 1 / beta 0 and zero biases unless random_affine."""
+    out = {}
+    for name, shape in transition_weight_shapes(c_z, hidden).items():
+        if name.startswith("w"):
+            out[name] = (rng.standard_normal(shape) / np.sqrt(shape[1])).astype(np.float32)
+        elif name == "ln_gamma":
+            out[name] = (1.0 + 0.2 * rng.standard_normal(shape) if random_affine
+                         else np.ones(shape)).astype(np.float32)
+        else:
+            out[name] = (0.2 * rng.standard_normal(shape) if random_affine
+                         else np.zeros(shape)).astype(np.float32)
+    return out
+
+
 def block_mask(batch, n, lengths):
     """1 on the leading L x L block of each item, 0 on padding."""
     m = np.zeros((batch, n, n), dtype=np.float32)
