@@ -44,14 +44,29 @@ __device__ __forceinline__ void lds_dma16(const void* src, void* lds_base) {
                                    0);
 }
 
-// Buffer resources for plain byte-addressed reads: a read at or past `bytes` returns
-// zero instead of touching memory. Loads through them take a 32-bit per-lane offset and a
-// scalar offset, so per-lane offsets that stay the same from tile to tile never have to be
-// recomputed into registers a load in flight still reads.
+// Buffer resources for plain byte-addressed access: a read whose per-lane plus immediate
+// offset is at or past `bytes` returns zero, a store there is dropped. The scalar offset
+// of a load or store is NOT part of that check, so anything that must stay inside the
+// extent goes in the per-lane or immediate offset, or moves the resource's base. Loads
+// through them take a 32-bit per-lane offset, so per-lane offsets that stay the same from
+// tile to tile never have to be recomputed into registers a load in flight still reads.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, size_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0,
                                            (int)(bytes < 0x7fffffffu ? bytes : 0x7fffffffu),
                                            0x00020000);
+}
+// The same with an extent the caller already holds in 32 bits (scalar compares only; a
+// 64-bit ordered compare has no scalar form and would take vector registers).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_u32(const void* base, unsigned int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+// Bytes left of an extent `bytes` after skipping `skip` (both below 2^31), at least 0. A
+// signed max: the unsigned "a > b ? a - b : 0" becomes a saturating subtract, which has
+// only a vector form, and a resource field in a vector register turns every load through
+// it into a loop over lanes.
+__device__ __forceinline__ unsigned int bytes_after(unsigned int bytes, unsigned int skip) {
+  const int d = (int)bytes - (int)skip;
+  return (unsigned int)(d > 0 ? d : 0);
 }
 __device__ __forceinline__ chunk_t load16(__amdgpu_buffer_rsrc_t r, unsigned int voff, int soff) {
   return __builtin_bit_cast(chunk_t, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, soff, 0));

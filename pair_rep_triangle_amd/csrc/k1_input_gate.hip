@@ -334,33 +334,41 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     chunk_t zv[ST][KZ];
     T m[ST];
   };
-  // Buffer loads: per tile a scalar base (the tile's first pair) and an extent ending at
-  // the last real pair of its storage row; per lane a byte offset that is the same in
-  // every tile (consecutive pairs of a tile are 1 (outgoing) or n (incoming) pairs
-  // apart). Pairs past the extent, and whole tiles in padding rows, read as zero.
+  // Buffer loads: per subtile a scalar base (its first pair) and an extent ending at the
+  // last real pair of its storage row; per lane a byte offset that is the same in every
+  // tile (consecutive pairs of a tile are 1 (outgoing) or n (incoming) pairs apart). The
+  // bounds check covers the lane and immediate offsets only, so each subtile gets its own
+  // resource rather than a scalar offset. Pairs past the extent, and whole tiles in
+  // padding rows, read as zero.
   const size_t pstride = incoming ? (size_t)n : 1;  // pairs between consecutive columns
-  // lane offsets: pair arow of the tile, chunk q of the first chunk group; subtile st adds
-  // the scalar 4 * st columns, chunk group ks the immediate ks * KG elements
+  // lane offsets: pair arow of the subtile, chunk q of the first chunk group; subtile st
+  // starts 4 * st columns on, chunk group ks adds the immediate ks * KG elements
   const unsigned int zoff = (unsigned int)(((size_t)arow * pstride * cz + q * E) * sizeof(T));
   const unsigned int moff = mask_all ? 0u : (unsigned int)((size_t)arow * pstride * sizeof(T));
-  const int zstep = (int)(4 * pstride * cz * sizeof(T)), mstep = mask_all ? 0 : (int)(4 * pstride * sizeof(T));
+  // byte sizes below 2^31: this form runs only where one batch item of z is under 2 GiB
+  const unsigned int zstep = (unsigned int)(4 * pstride * cz * sizeof(T));
+  const unsigned int mstep = (unsigned int)(4 * pstride * sizeof(T));
   auto fetch = [&](int t, Pre& f) {
     int bb, r, s0;
     coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);  // waves past the end refetch
     const bool row_ok = r < n && s0 < n;
     const size_t p0 = row_ok ? (incoming ? ((size_t)bb * n + s0) * n + r : ((size_t)bb * n + r) * n + s0) : 0;
-    const size_t cols = row_ok ? (size_t)(n - s0) : 0;  // real pairs from the first one on
-    const __amdgpu_buffer_rsrc_t rz =
-        buffer_rsrc(z + p0 * cz, cols == 0 ? 0 : ((cols - 1) * pstride + 1) * cz * sizeof(T));
-    const __amdgpu_buffer_rsrc_t rm = buffer_rsrc(
-        mask_all ? mask : mask + p0,
-        mask_all ? sizeof(T) : (cols == 0 ? 0 : ((cols - 1) * pstride + 1) * sizeof(T)));
+    // pairs of the storage row from the tile's first one to the last real one
+    const unsigned int span = row_ok ? (unsigned int)(n - s0 - 1) * (unsigned int)pstride + 1 : 0u;
+    const unsigned int zext = span * (unsigned int)(cz * sizeof(T));
+    const unsigned int mext = span * (unsigned int)sizeof(T);
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
+      const unsigned int zs = st * zstep, ms = st * mstep;
+      const __amdgpu_buffer_rsrc_t rz =
+          buffer_rsrc_u32((const unsigned char*)(z + p0 * cz) + zs, bytes_after(zext, zs));
+      const __amdgpu_buffer_rsrc_t rm =
+          mask_all ? buffer_rsrc_u32(mask, sizeof(T))
+                   : buffer_rsrc_u32((const unsigned char*)(mask + p0) + ms, bytes_after(mext, ms));
 #pragma unroll
       for (int ks = 0; ks < KZ; ++ks)
-        f.zv[st][ks] = load16(rz, zoff + ks * KG * (unsigned int)sizeof(T), st * zstep);
-      f.m[st] = load_elem(rm, moff, st * mstep, T());
+        f.zv[st][ks] = load16(rz, zoff + ks * KG * (unsigned int)sizeof(T), 0);
+      f.m[st] = load_elem(rm, moff, 0, T());
     }
   };
 
