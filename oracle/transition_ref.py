@@ -13,9 +13,9 @@ What is computed (per batch item b and residue pair (i, j); float64 NumPy):
    kernels at every site; the transition is taken to act on the normalised pair
    tensor, the usual pre-norm form, and the HIP kernel fuses that norm.]
 2. h = relu(zhat W_1^T + b_1), hidden width = expansion x c_z.  [RFProteína
-   architecture, the pair-transition paragraph of "Kernel dispatch": both linears
-   and the ReLU in one launch, the hidden activation kept on chip; the released
-   pair width 384 uses an expansion of 2.]
+   architecture, "Kernel support", the pair-transition paragraph of "Dispatch and
+   fallback": both linears and the ReLU in one launch, the hidden activation kept
+   on chip; the released pair width 384 uses an expansion of 2.]
 3. u = h W_2^T + b_2 (back to c_z channels).
 4. out_bij = z_bij + m_bij * u_bij.  [RFProteína architecture, "Inside the velocity
    network": the pair transition is applied as a masked residual, like the two

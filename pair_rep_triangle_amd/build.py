@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtrimul.so")
-SOURCES = ("k1_input_gate.hip", "k2_contract.hip", "k3_output_gate.hip", "tri_mul.cpp")
+SOURCES = ("k1_input_gate.hip", "k2_contract.hip", "k3_output_gate.hip", "kt_transition.hip",
+           "tri_mul.cpp", "pair_transition.cpp")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,257 @@
+// kt: the pair transition as a masked residual, one kernel:
+//   out = z + m * (W_2 relu(W_1 LN(z) + b_1) + b_2)
+// RFProteína architecture page, "Kernel support": the table's pair-transition row and the
+// pair-transition paragraph of "Dispatch and fallback" (both linears, the ReLU, the mask
+// and the residual in one launch, the hidden activation kept on chip); and "Inside the
+// velocity network" (the pair update ends with a pair transition
+// applied as a masked residual). LN gamma/beta are folded into W_1 and b_1 on the host.
+//
+// The map is pointwise over pairs, so a wave tile is 32 consecutive pairs (two subtiles
+// of 16). A workgroup of 8 waves copies W_1, W_2 and the biases into LDS once (16-byte
+// chunk c of row r at c ^ (r & m), m+1 the largest power of two dividing the row's chunk
+// count: no bank conflicts, no padding), then every wave loops over its own tiles with no
+// workgroup barrier:
+//   - z arrives straight in MFMA operand layout (lane (p, q) = (lane%16, lane/16) holds
+//     chunk ks*4 + q of pair p); the raw chunks are kept for the residual, a copy is
+//     normalised in registers;
+//   - the hidden width goes in groups of one MFMA k extent (32 bf16 / 16 fp32 values).
+//     First GEMM with W_1 rows as the A operand and zhat as B: lane (p, q) ends up with
+//     hidden rows 4q..4q+3 of each 16-row unit for pair p. Bias (the accumulator's start)
+//     and ReLU applied, those values ARE the lane's B-operand chunk of the second GEMM once
+//     W_2's columns are stored in the matching order (bf16: slots 8q..8q+3 <- rows 4q..4q+3
+//     of the group's first unit, slots 8q+4..8q+7 <- of its second) - no data movement;
+//   - second GEMM with W_2 rows as A: W_2's rows (output channels) are stored so that the
+//     accumulator registers of lane (p, q) are exactly the channels its z chunks hold.
+//     The epilogue z + m * acc is lane-local and leaves as 16-byte chunks.
+// Loads and stores are buffer operations on per-subtile resources that end at the last
+// pair: the ragged last tile reads zeros and its stores past the end are dropped.
+
+#include "device_common.h"
+#include "transition_launch.h"
+
+namespace trimul {
+
+constexpr int KT_WAVES = 8;
+constexpr int KT_THREADS = 64 * KT_WAVES;
+constexpr int KT_ST = 2;            // 16-pair subtiles per wave tile
+constexpr int KT_TW = 16 * KT_ST;   // pairs per wave tile
+
+// The scalar offset stays 0: a 16-byte store still reads its data registers after it
+// issues, and the compiler only guards those registers against the next write when the
+// store has no scalar offset register.
+__device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, chunk_t v, unsigned int voff) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, 0);
+}
+
+template <class T, int KZ>
+__global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
+    const T* __restrict__ z, const T* __restrict__ mask, T* out, const T* __restrict__ w1,
+    const T* __restrict__ w2, const float* __restrict__ b1, const float* __restrict__ b2,
+    int tiles, int last_pairs, int hp, int mask_all) {
+  constexpr int E = Traits<T>::E;
+  constexpr int KG = Traits<T>::KG;
+  constexpr int CZ = KZ * KG;       // pair width
+  constexpr int UO = CZ / 16;       // output units of 16 channels
+  constexpr int UPG = KG / 16;      // hidden units per k group of the second GEMM
+  constexpr int RC1 = CZ / E;       // chunks per W_1 row
+  constexpr int SW1 = (RC1 & -RC1) - 1;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* const w1s = (T*)smem;                   // [hp][CZ]
+  T* const w2s = w1s + (size_t)hp * CZ;      // [CZ][hp]
+  float* const b1s = (float*)(w2s + (size_t)CZ * hp);  // [hp]
+  float* const b2s = b1s + hp;                          // [CZ]
+  const int rc2 = hp / E;                    // chunks per W_2 row
+  const int sw2 = (rc2 & -rc2) - 1;
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int p = lane & 15, q = lane >> 4;
+
+  // ---- weights and start values -> LDS ----
+  for (int idx = tid; idx < hp * RC1; idx += KT_THREADS) {
+    const int r = idx / RC1, c = idx - r * RC1;
+    st16(w1s + r * CZ + ((c ^ (r & SW1)) * E), ld16(w1 + (size_t)r * CZ + c * E));
+  }
+  for (int idx = tid; idx < CZ * rc2; idx += KT_THREADS) {
+    const int r = idx / rc2, c = idx - r * rc2;
+    st16(w2s + (size_t)r * hp + ((c ^ (r & sw2)) * E), ld16(w2 + (size_t)r * hp + c * E));
+  }
+  for (int idx = tid; idx < hp; idx += KT_THREADS) b1s[idx] = b1[idx];
+  for (int idx = tid; idx < CZ; idx += KT_THREADS) b2s[idx] = b2[idx];
+  __syncthreads();
+
+  // tiles: 32-pair tiles in all (the last one holds last_pairs pairs)
+  const int gw = blockIdx.x * KT_WAVES + wave;
+  const int nw = gridDim.x * KT_WAVES;
+
+  // per-lane byte offsets, the same in every tile: pair p of a subtile, chunk q of the
+  // first k group (k groups step in the immediate). Each subtile has a resource of its
+  // own: the bounds check covers the lane and immediate offsets, not the scalar one, so a
+  // subtile's extent must start at the subtile.
+  const unsigned int zoff = (unsigned int)((p * CZ + q * E) * sizeof(T));
+  const unsigned int moff = mask_all ? 0u : (unsigned int)(p * sizeof(T));
+  // resource of subtile st of tile t over `base` (pair-major, `unit` bytes per pair): it
+  // ends at the last pair, so the ragged last tile reads zeros and drops its stores
+  auto sub_rsrc = [&](const void* base, int t, int st, unsigned int unit) {
+    const unsigned int left = (t < tiles - 1 ? KT_TW : last_pairs) * unit;  // from the tile start
+    const unsigned int skip = st * 16 * unit;
+    return buffer_rsrc_u32((const unsigned char*)base + (size_t)t * KT_TW * unit + skip,
+                           bytes_after(left, skip));
+  };
+
+  struct Pre {
+    chunk_t zv[KT_ST][KZ];
+    T m[KT_ST];
+  };
+  auto fetch = [&](int t, Pre& f) {
+    t = t < tiles ? t : tiles - 1;  // waves past the end refetch the last tile
+#pragma unroll
+    for (int st = 0; st < KT_ST; ++st) {
+      const __amdgpu_buffer_rsrc_t rz = sub_rsrc(z, t, st, CZ * sizeof(T));
+      const __amdgpu_buffer_rsrc_t rm =
+          mask_all ? buffer_rsrc_u32(mask, sizeof(T)) : sub_rsrc(mask, t, st, sizeof(T));
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks)
+        f.zv[st][ks] = load16(rz, zoff + ks * KG * (unsigned int)sizeof(T), 0);
+      f.m[st] = load_elem(rm, moff, 0, T());
+    }
+  };
+
+  chunk_t zr[KT_ST][KZ], za[KT_ST][KZ];
+  float mv[KT_ST];
+  Pre f;
+  auto prepare = [&]() {
+#pragma unroll
+    for (int st = 0; st < KT_ST; ++st) {
+      mv[st] = to_f32(f.m[st]);
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) {
+        zr[st][ks] = f.zv[st][ks];
+        za[st][ks] = f.zv[st][ks];
+      }
+      normalize_operand_row<KZ>(za[st], CZ, lane, T());
+    }
+  };
+
+  fetch(gw, f);
+  prepare();
+  const int groups = hp / KG;
+  for (int t = gw; t < tiles; t += nw) {
+    int opaque;  // keeps the loop-invariant LDS reads inside the loop
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+    const T* const w1t = w1s + opaque;
+    const T* const w2t = w2s + opaque;
+
+    f32x4 acc2[UO][KT_ST];
+#pragma unroll
+    for (int v = 0; v < UO; ++v) {
+      const f32x4 bv = ld16f(b2s + 16 * v + 4 * q + opaque);
+#pragma unroll
+      for (int st = 0; st < KT_ST; ++st) acc2[v][st] = bv;
+    }
+    // one k group of the second GEMM: its hidden units from the first GEMM, ReLU, then the
+    // group's contribution to every output unit. After the last group's first GEMM zhat
+    // is dead and the next tile's loads go out.
+    auto group = [&](int g, bool last) {
+      f32x4 h[UPG][KT_ST];
+#pragma unroll
+      for (int uu = 0; uu < UPG; ++uu) {
+        const int u = g * UPG + uu;
+        const int row = 16 * u + p;
+        chunk_t wa[KZ];
+#pragma unroll
+        for (int ks = 0; ks < KZ; ++ks) wa[ks] = ld16(w1t + row * CZ + (((ks * 4 + q) ^ (row & SW1)) * E));
+        const f32x4 bv = ld16f(b1s + 16 * u + 4 * q + opaque);
+#pragma unroll
+        for (int st = 0; st < KT_ST; ++st) {
+          h[uu][st] = bv;
+#pragma unroll
+          for (int ks = 0; ks < KZ; ++ks) h[uu][st] = mma16(h[uu][st], wa[ks], za[st][ks], T());
+        }
+      }
+      if (last) fetch(t + nw, f);
+      chunk_t hb[KT_ST];
+#pragma unroll
+      for (int st = 0; st < KT_ST; ++st) {
+        float hv[8];
+#pragma unroll
+        for (int uu = 0; uu < UPG; ++uu)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) hv[4 * uu + r] = fmaxf(h[uu][st][r], 0.f);
+        hb[st] = pack(hv, T());
+      }
+#pragma unroll
+      for (int v = 0; v < UO; ++v) {
+        const int row = 16 * v + p;
+        const chunk_t wb = ld16(w2t + (size_t)row * hp + (((g * 4 + q) ^ (row & sw2)) * E));
+#pragma unroll
+        for (int st = 0; st < KT_ST; ++st) acc2[v][st] = mma16(acc2[v][st], wb, hb[st], T());
+      }
+    };
+#pragma unroll 1
+    for (int g = 0; g + 1 < groups; ++g) group(g, false);
+    group(groups - 1, true);
+
+    // out = z + m * acc: accumulator register r of output unit v is element
+    // e = 4 (v % 2) + r of z chunk v / 2 (bf16), element r of chunk v (fp32)
+#pragma unroll
+    for (int st = 0; st < KT_ST; ++st) {
+      const __amdgpu_buffer_rsrc_t ro = sub_rsrc(out, t, st, CZ * sizeof(T));
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) {
+        float zf[8], o[8];
+        unpack(zr[st][ks], zf, T());
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int v = ks * (E / 4) + e / 4, r = e % 4;
+          o[e] = zf[e] + mv[st] * acc2[v][st][r];
+        }
+        store16(ro, pack(o, T()), zoff + ks * KG * (unsigned int)sizeof(T));
+      }
+    }
+    prepare();
+  }
+}
+
+template <class T, int KZ>
+static hipError_t launch_kt(const TransitionArgs& a, hipStream_t st) {
+  constexpr int E = Traits<T>::E;
+  (void)E;
+  const size_t lds = ((size_t)a.hp * a.cz * 2) * sizeof(T) + ((size_t)a.hp + a.cz) * sizeof(float);
+  auto fn = pair_transition_kernel<T, KZ>;
+  static std::atomic<int> granted{0};
+  hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
+  if (e != hipSuccess) return e;
+  const long long tiles = (a.pairs + KT_TW - 1) / KT_TW;
+  if (tiles <= 0) return hipSuccess;
+  if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;  // tile indices are 32-bit
+  static std::atomic<int> occ{0};
+  static std::atomic<size_t> occ_lds{0};
+  const int per_cu = resident_blocks((const void*)fn, KT_THREADS, lds, occ, occ_lds);
+  const long long cap = (long long)a.num_cus * (per_cu > 0 ? per_cu : 1);
+  const long long need = (tiles + KT_WAVES - 1) / KT_WAVES;
+  const int blocks = (int)(need < cap ? need : cap);
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fn, dim3(blocks), dim3(KT_THREADS), lds, st, (const T*)a.z,
+                     (const T*)a.mask, (T*)a.out, (const T*)a.w1, (const T*)a.w2, a.b1, a.b2,
+                     (int)tiles, (int)(a.pairs - (tiles - 1) * KT_TW), a.hp, a.mask_all);
+  return hipGetLastError();
+}
+
+template <class T>
+static hipError_t launch_kt_dispatch(const TransitionArgs& a, hipStream_t st) {
+  switch (a.cz / Traits<T>::KG) {
+    case 1: return launch_kt<T, 1>(a, st);
+    case 2: return launch_kt<T, 2>(a, st);
+    case 3: return launch_kt<T, 3>(a, st);
+    case 4: return launch_kt<T, 4>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_transition(bool bf16_storage, const TransitionArgs& a, hipStream_t st) {
+  return bf16_storage ? launch_kt_dispatch<bf16>(a, st) : launch_kt_dispatch<float>(a, st);
+}
+
+}  // namespace trimul

@@ -1,0 +1,172 @@
+// Host side of the C ABI declared in include/pair_transition.h: validation, LayerNorm
+// folding, the kernel's weight order, launch.
+
+#include "pair_transition.h"
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include <new>
+#include <vector>
+
+#include "host_common.h"
+#include "transition_launch.h"
+
+struct pair_transition_handle {
+  int c_z, hidden, hp, dtype, device, num_cus;
+  bool bf16;
+  void* block;  // w1 | w2 | b1 | b2 | one
+  const void *w1, *w2, *one;
+  const float *b1, *b2;
+};
+
+namespace {
+
+using namespace trimul_host;
+
+// Output channel held by accumulator row R of the second GEMM. bf16: row 16v + 4q + r of
+// output unit v is element 4 (v % 2) + r of the lane's z chunk v / 2, i.e. channel
+// 32 (v / 2) + 8q + 4 (v % 2) + r; fp32: the natural order.
+int out_channel(int R, bool bf16) {
+  if (!bf16) return R;
+  const int v = R / 16, q = (R % 16) / 4, r = R % 4;
+  return 32 * (v / 2) + 8 * q + 4 * (v % 2) + r;
+}
+
+// Hidden unit in k slot s of the second GEMM. bf16: slots 8q..8q+3 of a 32-wide group
+// hold rows 4q..4q+3 of the group's first 16-row unit, slots 8q+4..8q+7 those of its
+// second; fp32: the natural order.
+int hidden_of_slot(int s, bool bf16) {
+  if (!bf16) return s;
+  const int g = s / 32, w = s % 32, q = w / 8, j = w % 8;
+  return 32 * g + (j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4));
+}
+
+}  // namespace
+
+extern "C" {
+
+int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden, int dtype,
+                           pair_transition_handle** out) {
+  if (!out) return TRI_MUL_ERR_INVALID_ARG;
+  *out = nullptr;
+  if (!w || !w->w1 || !w->w2 || c_z < 1 || hidden < 1) return TRI_MUL_ERR_INVALID_ARG;
+  if (dtype != TRI_MUL_FP32 && dtype != TRI_MUL_BF16) return TRI_MUL_ERR_UNSUPPORTED;
+  const bool bf16 = dtype == TRI_MUL_BF16;
+  const int kg = bf16 ? 32 : 16;
+  if (hidden > 1 << 20) return TRI_MUL_ERR_UNSUPPORTED;
+  const int hp = (hidden + kg - 1) / kg * kg;
+  if (!trimul::transition_supported(bf16, c_z, hp)) return TRI_MUL_ERR_UNSUPPORTED;
+  int dev = -1, cus = 0;
+  int rc = check_device(&dev, &cus);
+  if (rc != TRI_MUL_OK) return rc;
+
+  const size_t esz = bf16 ? 2 : 4;
+  const size_t w1b = align256((size_t)hp * c_z * esz), w2b = align256((size_t)c_z * hp * esz);
+  const size_t b1b = align256((size_t)hp * 4), b2b = align256((size_t)c_z * 4), oneb = 256;
+  const size_t total = w1b + w2b + b1b + b2b + oneb;
+  std::vector<unsigned char> host(total, 0);
+  unsigned char* hw1 = host.data();
+  unsigned char* hw2 = hw1 + w1b;
+  float* hb1 = (float*)(hw2 + w2b);
+  float* hb2 = (float*)((unsigned char*)hb1 + b1b);
+  unsigned char* hone = (unsigned char*)hb2 + b2b;
+  store_elem(hone, 1.0f, bf16);
+
+  // W_1' = W_1 diag(gamma), b_1' = W_1 beta + b_1 (sums in double); padded units stay 0
+  for (int h = 0; h < hidden; ++h) {
+    double t = w->b1 ? (double)w->b1[h] : 0.0;
+    for (int k = 0; k < c_z; ++k) {
+      const double wk = w->w1[(size_t)h * c_z + k];
+      store_elem(hw1 + ((size_t)h * c_z + k) * esz,
+                 (float)(wk * (w->ln_gamma ? (double)w->ln_gamma[k] : 1.0)), bf16);
+      if (w->ln_beta) t += wk * (double)w->ln_beta[k];
+    }
+    hb1[h] = (float)t;
+  }
+  // W_2 and b_2 in the kernel's row and column order
+  for (int R = 0; R < c_z; ++R) {
+    const int ch = out_channel(R, bf16);
+    hb2[R] = w->b2 ? w->b2[ch] : 0.f;
+    for (int s = 0; s < hp; ++s) {
+      const int hu = hidden_of_slot(s, bf16);
+      const float v = hu < hidden ? w->w2[(size_t)ch * hidden + hu] : 0.f;
+      store_elem(hw2 + ((size_t)R * hp + s) * esz, v, bf16);
+    }
+  }
+
+  pair_transition_handle* h = new (std::nothrow) pair_transition_handle();
+  if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
+  void* dptr = nullptr;
+  hipError_t e = hipMalloc(&dptr, total);
+  if (e != hipSuccess) {
+    delete h;
+    if (e == hipErrorOutOfMemory) return TRI_MUL_ERR_OUT_OF_MEMORY;
+    return hip_fail(e, "hipMalloc(transition weights)");
+  }
+  e = hipMemcpy(dptr, host.data(), total, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(dptr);
+    delete h;
+    return hip_fail(e, "hipMemcpy(transition weights)");
+  }
+  unsigned char* d = (unsigned char*)dptr;
+  h->c_z = c_z;
+  h->hidden = hidden;
+  h->hp = hp;
+  h->dtype = dtype;
+  h->device = dev;
+  h->num_cus = cus;
+  h->bf16 = bf16;
+  h->block = dptr;
+  h->w1 = d;
+  h->w2 = d + w1b;
+  h->b1 = (const float*)(d + w1b + w2b);
+  h->b2 = (const float*)(d + w1b + w2b + b1b);
+  h->one = d + w1b + w2b + b1b + b2b;
+  *out = h;
+  return TRI_MUL_OK;
+}
+
+int pair_transition_forward(pair_transition_handle* h, const void* z, const void* pair_mask,
+                            void* out, int batch, int n, void* stream) {
+  if (!h || !z || !out) return TRI_MUL_ERR_INVALID_ARG;
+  if (batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N) return TRI_MUL_ERR_INVALID_ARG;
+  const size_t esz = h->bf16 ? 2 : 4;
+  if (((uintptr_t)z | (uintptr_t)out) & 15u) return TRI_MUL_ERR_ALIGNMENT;
+  if (pair_mask && ((uintptr_t)pair_mask & (uintptr_t)(esz - 1))) return TRI_MUL_ERR_ALIGNMENT;
+  const size_t pairs = (size_t)batch * n * n;
+  if (pairs > (size_t)32 * 0x7fffffff) return TRI_MUL_ERR_UNSUPPORTED;  // 32-bit tile indices
+  const size_t zb = pairs * h->c_z * esz, mb = pairs * esz;
+  if ((out != z && overlaps(out, zb, z, zb)) || overlaps(out, zb, pair_mask, mb))
+    return TRI_MUL_ERR_ALIAS;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != h->device) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
+  trimul::TransitionArgs a;
+  a.z = z;
+  a.mask = pair_mask ? pair_mask : h->one;
+  a.out = out;
+  a.w1 = h->w1;
+  a.w2 = h->w2;
+  a.b1 = h->b1;
+  a.b2 = h->b2;
+  a.pairs = (long long)pairs;
+  a.cz = h->c_z;
+  a.hp = h->hp;
+  a.mask_all = pair_mask ? 0 : 1;
+  a.num_cus = h->num_cus;
+  e = trimul::launch_transition(h->bf16, a, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launch pair_transition");
+  return TRI_MUL_OK;
+}
+
+void pair_transition_destroy(pair_transition_handle* h) {
+  if (!h) return;
+  if (h->block) (void)hipFree(h->block);
+  delete h;
+}
+
+}  // extern "C"

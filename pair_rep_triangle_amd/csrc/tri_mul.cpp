@@ -11,6 +11,7 @@
 #include <new>
 #include <vector>
 
+#include "host_common.h"
 #include "launch.h"
 
 struct tri_mul_handle {
@@ -22,22 +23,7 @@ struct tri_mul_handle {
 
 namespace {
 
-thread_local char g_hip_err[256] = "no HIP error recorded";
-
-int hip_fail(hipError_t e, const char* what) {
-  snprintf(g_hip_err, sizeof(g_hip_err), "%s: %s (%d)", what, hipGetErrorString(e), (int)e);
-  return TRI_MUL_ERR_HIP;
-}
-
-uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u;
-  memcpy(&u, &f, 4);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+using namespace trimul_host;
 
 // Folds y = scale * (W (gamma (.) xhat + beta) + bias) into the stored matrix
 // W' = scale * W diag(gamma) (rounded to the storage type, zero-padded from `cols` to
@@ -65,12 +51,6 @@ void fold(const float* W, const float* gamma, const float* beta, const float* bi
   }
 }
 
-bool overlaps(const void* p, size_t pn, const void* q, size_t qn) {
-  if (!p || !q || pn == 0 || qn == 0) return false;
-  const uintptr_t a = (uintptr_t)p, b = (uintptr_t)q;
-  return a < b + qn && b < a + pn;
-}
-
 struct Layout {
   size_t a, b, x, total;
   int np, esz;
@@ -86,19 +66,6 @@ Layout layout_of(const tri_mul_handle* h, int batch, int n) {
   L.x = 2 * one;
   L.total = 3 * one;
   return L;
-}
-
-int check_device(int* dev_out, int* cus_out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  hipDeviceProp_t prop;
-  e = hipGetDeviceProperties(&prop, dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
-  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
-  *dev_out = dev;
-  *cus_out = prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 256;
-  return TRI_MUL_OK;
 }
 
 int validate_call(const tri_mul_handle* h, int stage, const void* z, const void* mask,
@@ -323,6 +290,6 @@ const char* tri_mul_strerror(int code) {
   }
 }
 
-const char* tri_mul_last_hip_error(void) { return g_hip_err; }
+const char* tri_mul_last_hip_error(void) { return trimul_host::g_hip_err; }
 
 }  // extern "C"

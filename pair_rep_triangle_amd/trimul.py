@@ -1,7 +1,8 @@
 """Python binding of libtrimul.so (ctypes): argument marshalling only.
 
-Every step of the operator runs in the HIP kernels behind the C ABI
-(include/tri_mul.h); PyTorch supplies device memory and the stream. There is
+Every step of the operators runs in the HIP kernels behind the C ABI
+(include/tri_mul.h, include/pair_transition.h); PyTorch supplies device memory and
+the stream. There is
 no other execution path: if the library is missing or the call fails, this
 module raises.
 """
@@ -12,6 +13,8 @@ import os
 import numpy as np
 
 from .inputs import WEIGHT_FIELDS
+
+TRANSITION_FIELDS = ("ln_gamma", "ln_beta", "w1", "b1", "w2", "b2")
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtrimul.so")
@@ -26,6 +29,8 @@ ERRORS = {
 EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
            "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage",
            "tri_mul_destroy", "tri_mul_strerror", "tri_mul_last_hip_error")
+TRANSITION_EXPORTS = ("pair_transition_create", "pair_transition_forward",
+                      "pair_transition_destroy")
 
 
 class TriMulError(RuntimeError):
@@ -37,6 +42,10 @@ class TriMulError(RuntimeError):
 
 class Weights(ctypes.Structure):
     _fields_ = [(name, ctypes.POINTER(ctypes.c_float)) for name in WEIGHT_FIELDS]
+
+
+class TransitionWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.POINTER(ctypes.c_float)) for name in TRANSITION_FIELDS]
 
 
 class Layout(ctypes.Structure):
@@ -70,8 +79,14 @@ def load_library(path=LIB_PATH):
     lib.tri_mul_strerror.restype = ctypes.c_char_p
     lib.tri_mul_last_hip_error.argtypes = []
     lib.tri_mul_last_hip_error.restype = ctypes.c_char_p
+    lib.pair_transition_create.argtypes = [ctypes.POINTER(TransitionWeights), i, i, i,
+                                           ctypes.POINTER(vp)]
+    lib.pair_transition_forward.argtypes = [vp, vp, vp, vp, i, i, vp]
+    lib.pair_transition_destroy.argtypes = [vp]
+    lib.pair_transition_destroy.restype = None
     for name in ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
-                 "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage"):
+                 "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage",
+                 "pair_transition_create", "pair_transition_forward"):
         getattr(lib, name).restype = i
     _lib = lib
     return lib
@@ -198,6 +213,71 @@ class TriMul:
     def close(self):
         if getattr(self, "_h", None):
             self.lib.tri_mul_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class PairTransition:
+    """The pair transition as a masked residual (one weight set, one dtype):
+    out = z + m * (W2 relu(W1 LN(z) + b1) + b2), hidden width `hidden`.
+
+    weights: mapping with the pair_transition_weights field names, fp32 host arrays in
+    nn.Linear orientation (missing gamma -> ones, missing beta / biases -> zeros).
+    """
+
+    def __init__(self, weights, c_z, hidden, dtype="bf16"):
+        self.lib = load_library()
+        self.c_z, self.hidden, self.dtype = int(c_z), int(hidden), dtype
+        if dtype not in DTYPES:
+            raise ValueError(f"dtype must be one of {sorted(DTYPES)}")
+        keep = {}
+        ws = TransitionWeights()
+        for name in TRANSITION_FIELDS:
+            v = weights.get(name) if hasattr(weights, "get") else None
+            if v is None:
+                continue
+            keep[name] = _host_f32(v)
+            setattr(ws, name, keep[name].ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        h = ctypes.c_void_p()
+        _check(self.lib.pair_transition_create(ctypes.byref(ws), self.c_z, self.hidden,
+                                               DTYPES[dtype], ctypes.byref(h)),
+               "pair_transition_create")
+        self._h = h
+
+    def forward(self, z, mask=None, out=None, stream=None):
+        """out = z + m * transition(z); out may be z itself (in place)."""
+        import torch
+        dt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        if z.dim() != 4 or z.shape[1] != z.shape[2] or z.shape[3] != self.c_z:
+            raise ValueError(f"z must be [B, N, N, {self.c_z}], got {tuple(z.shape)}")
+        if z.dtype != dt or not z.is_cuda or not z.is_contiguous():
+            raise ValueError("z must be a contiguous CUDA tensor of the handle's dtype")
+        batch, n = int(z.shape[0]), int(z.shape[1])
+        if mask is not None and (tuple(mask.shape) != (batch, n, n) or mask.dtype != z.dtype
+                                 or not mask.is_contiguous()):
+            raise ValueError("mask must be a contiguous [B, N, N] tensor of z's dtype")
+        if out is None:
+            out = torch.empty_like(z)
+        elif out.shape != z.shape or out.dtype != z.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor shaped like z")
+        if stream is None:
+            stream = torch.cuda.current_stream(z.device).cuda_stream
+        _check(self.lib.pair_transition_forward(self._h, z.data_ptr(),
+                                                None if mask is None else mask.data_ptr(),
+                                                out.data_ptr(), batch, n, stream),
+               "pair_transition_forward")
+        return out
+
+    __call__ = forward
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self.lib.pair_transition_destroy(self._h)
             self._h = None
 
     def __del__(self):

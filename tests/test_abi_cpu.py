@@ -1,6 +1,6 @@
 """C-ABI contract checks that need no GPU: the library loads, exports every
-symbol include/tri_mul.h declares, and rejects bad create arguments before any
-HIP call."""
+symbol include/tri_mul.h and include/pair_transition.h declare, and rejects bad
+create arguments before any HIP call."""
 
 import ctypes
 import os
@@ -10,16 +10,16 @@ import numpy as np
 import pytest
 
 from pair_rep_triangle_amd import trimul as tm
-from pair_rep_triangle_amd.inputs import make_weights
+from pair_rep_triangle_amd.inputs import make_transition_weights, make_weights
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
-def _declared_functions():
-    with open(os.path.join(ROOT, "include", "tri_mul.h")) as f:
+def _declared_functions(header="tri_mul.h", prefix="tri_mul_"):
+    with open(os.path.join(ROOT, "include", header)) as f:
         src = f.read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(tri_mul_[a-z_]+)\s*\(", src)))
+    return sorted(set(re.findall(r"\b(" + prefix + r"[a-z_]+)\s*\(", src)))
 
 
 @pytest.fixture(scope="module")
@@ -31,8 +31,12 @@ def test_header_declares_the_entry_points():
     assert _declared_functions() == sorted(tm.EXPORTS)
 
 
+def test_transition_header_declares_the_entry_points():
+    assert _declared_functions("pair_transition.h", "pair_transition_") == sorted(tm.TRANSITION_EXPORTS)
+
+
 def test_library_exports_every_declared_symbol(lib):
-    for name in _declared_functions():
+    for name in _declared_functions() + _declared_functions("pair_transition.h", "pair_transition_"):
         assert hasattr(lib, name), name
 
 
@@ -87,3 +91,36 @@ def test_binding_raises_with_a_named_error():
     with pytest.raises(tm.TriMulError) as ei:
         tm.TriMul(make_weights(np.random.default_rng(0), 16, 16), 20, 16, "bf16")
     assert ei.value.name == "UNSUPPORTED"
+
+
+def _transition_struct(w):
+    keep = {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in w.items()}
+    s = tm.TransitionWeights()
+    for k, v in keep.items():
+        setattr(s, k, v.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return s, keep
+
+
+@pytest.mark.parametrize("c_z,hidden,dtype,code", [
+    (48, 96, tm.TRI_MUL_BF16, -2), (160, 320, tm.TRI_MUL_BF16, -2), (128, 512, tm.TRI_MUL_BF16, -2),
+    (24, 48, tm.TRI_MUL_FP32, -2), (128, 256, tm.TRI_MUL_FP32, -2), (64, 64, 9, -2),
+    (0, 64, tm.TRI_MUL_BF16, -1), (64, 0, tm.TRI_MUL_BF16, -1),
+])
+def test_transition_create_rejects_bad_shapes(lib, c_z, hidden, dtype, code):
+    w = make_transition_weights(np.random.default_rng(0), max(c_z, 1), max(hidden, 1))
+    s, keep = _transition_struct(w)
+    h = ctypes.c_void_p(1)
+    assert lib.pair_transition_create(ctypes.byref(s), c_z, hidden, dtype, ctypes.byref(h)) == code
+    assert h.value is None
+
+
+def test_transition_null_arguments(lib):
+    w = make_transition_weights(np.random.default_rng(0), 64, 128)
+    s, keep = _transition_struct(w)
+    h = ctypes.c_void_p()
+    assert lib.pair_transition_create(None, 64, 128, tm.TRI_MUL_BF16, ctypes.byref(h)) == -1
+    assert lib.pair_transition_create(ctypes.byref(s), 64, 128, tm.TRI_MUL_BF16, None) == -1
+    s.w2 = None
+    assert lib.pair_transition_create(ctypes.byref(s), 64, 128, tm.TRI_MUL_BF16, ctypes.byref(h)) == -1
+    assert lib.pair_transition_forward(None, 16, None, 32, 1, 8, None) == -1
+    lib.pair_transition_destroy(None)  # no-op
