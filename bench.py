@@ -17,8 +17,12 @@ The timed steps launch their six kernels one by one; --launch graph captures the
 step once in a HIP graph and times replays of it instead (the eager step time is
 reported in both cases). The per-kernel region always launches eagerly.
 
+With --op transition the step is the pair transition instead (one kernel: LayerNorm,
+c_z -> 2 c_z -> c_z with ReLU, masked residual) on the same workload's z and mask; its
+line reports pair-updates/s with the same roofline and cpu_baseline objects.
+
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--chained]
-                    [--launch graph|eager] [--no-cpu-baseline]
+                    [--launch graph|eager] [--op trimul|transition] [--no-cpu-baseline]
 """
 
 import argparse
@@ -31,8 +35,13 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "triangle-mult-update TFLOP/s & pair-updates/s at N=512,c_z=128 bf16 (1 GPU)"
+TRANSITION_METRIC = "pair-transition pair-updates/s (expansion 2, masked residual, 1 GPU)"
 KERNELS = ("k1_input_gate", "k2_contract", "k3_output_gate")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+# A bounded spin on the GPU queued ahead of each per-kernel event region, so the host has
+# enqueued the region's launches before the GPU reaches them: the event pair around a
+# kernel then brackets the kernel, not the host's launch gap.
+HOST_AHEAD_CYCLES = 20_000_000
 
 
 def parse():
@@ -47,6 +56,8 @@ def parse():
     p.add_argument("--launch", choices=("eager", "graph"), default="eager",
                    help="timed steps launch their kernels one by one (default) or replay one "
                         "captured HIP graph of the step")
+    p.add_argument("--op", choices=("trimul", "transition"), default="trimul",
+                   help="time the triangle multiplicative update (default) or the pair transition")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
@@ -75,12 +86,179 @@ def cpu_baseline(d, directions, threads, min_seconds=10.0, max_reps=8):
     return total / reps, reps
 
 
+def timed_steps(run, steps, stream):
+    """Milliseconds per call of `run` over `steps` calls between two HIP events on
+    `stream` (synchronised on both sides), and the wall seconds of the region."""
+    import torch
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for _ in range(steps):
+        run()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    return t_start.elapsed_time(t_end) / steps, time.perf_counter() - wall0
+
+
+def copy_calibration(mib, dev):
+    """A plain device-to-device copy of `mib` MiB, three times (the reference kernel the
+    HBM byte counters are scaled by); nothing when `mib` is 0."""
+    if not mib:
+        return
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def graph_of(step, dev):
+    """`step` captured once in a HIP graph (after one run on a side stream)."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph.replay()  # one untimed replay
+    return graph
+
+
+def roofline_of(kname, avg_ms, bytes_per_launch, flops_per_launch, dtype, traffic):
+    from pair_rep_triangle_amd.metrics import MI355X_PEAK
+    gbps = bytes_per_launch / (avg_ms * 1e-3) / 1e9
+    tfl = flops_per_launch / (avg_ms * 1e-3) / 1e12
+    peak_fl = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+    ridge = peak_fl * 1e12 / (MI355X_PEAK["hbm_GBps"] * 1e9)
+    if flops_per_launch / bytes_per_launch < ridge:
+        return {"kernel": kname, "bound": "hbm", "achieved": round(gbps, 1),
+                "peak": MI355X_PEAK["hbm_GBps"], "unit": "GB/s",
+                "frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4), "traffic": traffic}
+    return {"kernel": kname, "bound": "mfma", "achieved": round(tfl, 1), "peak": peak_fl,
+            "unit": "TFLOP/s", "frac": round(tfl / peak_fl, 4), "traffic": traffic}
+
+
+def bench_transition(args):
+    """The pair transition (hidden = 2 c_z, the expansion the pages give for the pair
+    track) on the workload's z and mask, out of place."""
+    import numpy as np
+    import torch
+    from pair_rep_triangle_amd.inputs import HEADLINE, WORKLOADS, make_transition_weights, make_workload
+    from pair_rep_triangle_amd.metrics import MI355X_PEAK, transition_work
+    from pair_rep_triangle_amd.trimul import PairTransition
+
+    name = args.workload or HEADLINE
+    spec = WORKLOADS[name]
+    d = make_workload(name, seed=args.seed)
+    B, n, c_z, dtype = spec["batch"], spec["n"], spec["c_z"], spec["dtype"]
+    hidden = 2 * c_z
+    wt = make_transition_weights(np.random.default_rng(args.seed + 2), c_z, hidden, random_affine=True)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    esz = 2 if dtype == "bf16" else 4
+    dev = torch.device("cuda:0")
+    z = torch.from_numpy(d["z"]).to(tdt).to(dev)
+    mask = torch.from_numpy(d["mask"]).to(tdt).to(dev)
+    mod = PairTransition(wt, c_z, hidden, dtype)
+    out = torch.empty_like(z)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        mod.forward(z, mask, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    copy_calibration(args.copy_calibration_mb, dev)
+    ms_eager, wall = timed_steps(step, args.steps, stream)
+    ms_step, launch = ms_eager, "eager"
+    if args.launch == "graph":
+        graph = graph_of(step, dev)
+        ms_step, wall = timed_steps(graph.replay, args.steps, stream)
+        launch = "hipgraph"
+
+    # the kernel alone: a HIP event before and after each launch
+    kernels, roofline = {}, None
+    pairs = B * n * n
+    wk = transition_work(c_z, hidden, esz)
+    if not args.no_kernel_events:
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda._sleep(HOST_AHEAD_CYCLES)
+        for a, b in evs:
+            a.record(stream)
+            step()
+            b.record(stream)
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) for a, b in evs])
+        avg_ms = float(per.mean())
+        bytes_l, flops_l = wk["bytes"] * pairs, wk["flops"] * pairs
+        roofline = roofline_of("pair_transition", avg_ms, bytes_l, flops_l, dtype,
+                               measured_traffic(name, "pair_transition"))
+        peak_fl = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+        kernels["pair_transition"] = {
+            "avg_us": round(avg_ms * 1e3, 3), "median_us": round(float(np.median(per)) * 1e3, 3),
+            "GBps": round(bytes_l / (avg_ms * 1e-3) / 1e9, 1),
+            "TFLOPs": round(flops_l / (avg_ms * 1e-3) / 1e12, 1),
+            "hbm_frac": round(bytes_l / (avg_ms * 1e-3) / 1e9 / MI355X_PEAK["hbm_GBps"], 4),
+            "mfma_frac": round(flops_l / (avg_ms * 1e-3) / 1e12 / peak_fl, 4),
+            "bytes_per_launch": bytes_l, "flops_per_launch": flops_l,
+        }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import pair_transition_ref
+        threads = min(16, len(os.sched_getaffinity(0)))
+        zh = torch.from_numpy(d["z"]).to(torch.bfloat16).to(torch.float64).numpy()
+        reps, total = 0, 0.0
+        with threadpool_limits(limits=threads):
+            while reps < 8 and (reps == 0 or total < 10.0):
+                t0 = time.perf_counter()
+                pair_transition_ref(zh, d["mask"], wt)
+                total += time.perf_counter() - t0
+                reps += 1
+        dt = total / reps
+        cpu = {"value": round(pairs / dt, 1), "unit": "pair-updates/s", "cores": threads,
+               "kind": "oracle", "seconds_per_pass": round(dt, 3),
+               "sample": f"whole workload {name}, fp64 NumPy oracle (BLAS on {threads} "
+                         f"threads), {reps} passes averaged"}
+
+    rec = {
+        "metric": TRANSITION_METRIC, "value": round(pairs / (ms_step * 1e-3), 1),
+        "unit": "pair-updates/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5), "ms_per_step_eager": round(ms_eager, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": f"pair_transition_{name}", "batch": B, "n": n, "c_z": c_z,
+                   "hidden": hidden, "mask": spec["mask"], "launch": launch},
+        "tflops": round(wk["flops"] * pairs / (ms_step * 1e-3) / 1e12, 2),
+        "wall_s": round(wall, 3),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build measures one GPU only; the operator is not sharded "
               "across GPUs (run with --gpus 1).", file=sys.stderr)
         sys.exit(2)
+    if args.op == "transition":
+        bench_transition(args)
+        return
 
     import numpy as np
     import torch
@@ -118,52 +296,25 @@ def main():
         step()
     torch.cuda.synchronize()
 
-    if args.copy_calibration_mb:
-        src = torch.empty(args.copy_calibration_mb << 20, dtype=torch.uint8, device=dev)
-        dst = torch.empty_like(src)
-        src.fill_(1)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+    copy_calibration(args.copy_calibration_mb, dev)
 
     # timed region 1: K whole steps (outgoing + incoming), HIP events on the launch stream;
     # eager launches, then (--launch graph) the same step captured once and replayed K times
-    def timed(run):
-        t_start = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        wall0 = time.perf_counter()
-        t_start.record(stream)
-        for _ in range(args.steps):
-            run()
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        return t_start.elapsed_time(t_end) / args.steps, time.perf_counter() - wall0
-
-    ms_eager, wall = timed(step)
+    ms_eager, wall = timed_steps(step, args.steps, stream)
     ms_step, launch = ms_eager, "eager"
     if args.launch == "graph":
-        graph = torch.cuda.CUDAGraph()
-        side = torch.cuda.Stream(dev)
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):  # a step on a side stream before capture
-            step()
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        with torch.cuda.graph(graph):
-            step()
-        torch.cuda.synchronize()
-        graph.replay()  # one untimed replay
-        ms_step, wall = timed(graph.replay)
+        graph = graph_of(step, dev)
+        ms_step, wall = timed_steps(graph.replay, args.steps, stream)
         launch = "hipgraph"
 
     # timed region 2: the same K steps again with a HIP event after every kernel (on the
     # launch stream), for each kernel's duration inside the real K1 -> K2 -> K3 order.
     # Kept apart from region 1 because every event adds a marker packet to the stream.
+    # The host queues it while the GPU runs a short spin, so no launch gap is timed.
     per_kernel_ms = {}
     if not args.no_kernel_events:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
+        torch.cuda._sleep(HOST_AHEAD_CYCLES)
         for k in range(args.steps):
             evs[k][0].record(stream)
             e = 1

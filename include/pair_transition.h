@@ -45,7 +45,8 @@ typedef struct pair_transition_handle pair_transition_handle;
  * and b_1, rounds the weights to `dtype` and stores them on the device in the kernel's
  * order. Supported: c_z a multiple of 32 up to 128 (bf16) or of 16 up to 64 (fp32);
  * hidden >= 1 (padded with zero units to a multiple of 32 / 16), with the padded
- * weights of both layers fitting 128 KB (bf16 c_z = 128: hidden <= 256).
+ * weights of both layers (16 bytes of padding per row) and the fp32 biases fitting one
+ * workgroup's 160 KB of LDS (bf16 c_z = 128: hidden <= 288).
  * Returns TRI_MUL_ERR_UNSUPPORTED for other shapes, TRI_MUL_ERR_INVALID_ARG for NULL
  * w / w1 / w2 / out or non-positive sizes. On error *out is NULL. */
 int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden, int dtype,

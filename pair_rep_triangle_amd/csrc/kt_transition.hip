@@ -7,17 +7,19 @@
 // applied as a masked residual). LN gamma/beta are folded into W_1 and b_1 on the host.
 //
 // The map is pointwise over pairs, so a wave tile is 32 consecutive pairs (two subtiles
-// of 16). A workgroup of 8 waves copies W_1, W_2 and the biases into LDS once (16-byte
-// chunk c of row r at c ^ (r & m), m+1 the largest power of two dividing the row's chunk
-// count: no bank conflicts, no padding), then every wave loops over its own tiles with no
-// workgroup barrier:
+// of 16). A workgroup of 8 waves copies W_1, W_2 and the biases into LDS once (each row
+// padded by 16 bytes: the row stride is an odd multiple of 16 bytes, so the 16 rows one
+// operand read touches land in 16 different bank groups, and every offset inside a k
+// group is an immediate), then every wave loops over its own tiles with no workgroup
+// barrier:
 //   - z arrives straight in MFMA operand layout (lane (p, q) = (lane%16, lane/16) holds
 //     chunk ks*4 + q of pair p); the raw chunks are kept for the residual, a copy is
 //     normalised in registers;
 //   - the hidden width goes in groups of one MFMA k extent (32 bf16 / 16 fp32 values).
 //     First GEMM with W_1 rows as the A operand and zhat as B: lane (p, q) ends up with
 //     hidden rows 4q..4q+3 of each 16-row unit for pair p. Bias (the accumulator's start)
-//     and ReLU applied, those values ARE the lane's B-operand chunk of the second GEMM once
+//     and ReLU applied (after rounding to bf16, as a packed 16-bit integer max: rounding
+//     keeps the sign), those values ARE the lane's B-operand chunk of the second GEMM once
 //     W_2's columns are stored in the matching order (bf16: slots 8q..8q+3 <- rows 4q..4q+3
 //     of the group's first unit, slots 8q+4..8q+7 <- of its second) - no data movement;
 //   - second GEMM with W_2 rows as A: W_2's rows (output channels) are stored so that the
@@ -44,6 +46,28 @@ __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, chunk_t v, uns
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, 0);
 }
 
+// max(x, 0) on packed storage values: a negative bf16 or fp32 value is a negative 16- or
+// 32-bit integer (sign bit set), so a signed integer max with 0 is the ReLU, two bf16
+// values per instruction (a float max would also canonicalise its input first). The
+// empty asm keeps each packed dword whole, so the conversion before it stays one
+// two-value instruction rather than two conversions and a byte permute.
+__device__ __forceinline__ chunk_t relu_packed(chunk_t c, bf16) {
+  typedef short s16x2 __attribute__((ext_vector_type(2)));
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    unsigned int u = c[i];
+    asm volatile("" : "+v"(u));
+    c[i] = __builtin_bit_cast(unsigned int,
+                              __builtin_elementwise_max(__builtin_bit_cast(s16x2, u), (s16x2)0));
+  }
+  return c;
+}
+__device__ __forceinline__ chunk_t relu_packed(chunk_t c, float) {
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const i32x4 v = __builtin_bit_cast(i32x4, c);
+  return __builtin_bit_cast(chunk_t, __builtin_elementwise_max(v, (i32x4)0));
+}
+
 template <class T, int KZ>
 __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
     const T* __restrict__ z, const T* __restrict__ mask, T* out, const T* __restrict__ w1,
@@ -55,14 +79,14 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
   constexpr int UO = CZ / 16;       // output units of 16 channels
   constexpr int UPG = KG / 16;      // hidden units per k group of the second GEMM
   constexpr int RC1 = CZ / E;       // chunks per W_1 row
-  constexpr int SW1 = (RC1 & -RC1) - 1;
+  constexpr int RS1 = CZ + E;       // W_1 row stride in LDS (one chunk of padding)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  T* const w1s = (T*)smem;                   // [hp][CZ]
-  T* const w2s = w1s + (size_t)hp * CZ;      // [CZ][hp]
-  float* const b1s = (float*)(w2s + (size_t)CZ * hp);  // [hp]
-  float* const b2s = b1s + hp;                          // [CZ]
+  const int rs2 = hp + E;                    // W_2 row stride in LDS
+  T* const w1s = (T*)smem;                   // [hp][RS1]
+  T* const w2s = w1s + (size_t)hp * RS1;     // [CZ][rs2]
+  float* const b1s = (float*)(w2s + (size_t)CZ * rs2);  // [hp]
+  float* const b2s = b1s + hp;                           // [CZ]
   const int rc2 = hp / E;                    // chunks per W_2 row
-  const int sw2 = (rc2 & -rc2) - 1;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -71,11 +95,11 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
   // ---- weights and start values -> LDS ----
   for (int idx = tid; idx < hp * RC1; idx += KT_THREADS) {
     const int r = idx / RC1, c = idx - r * RC1;
-    st16(w1s + r * CZ + ((c ^ (r & SW1)) * E), ld16(w1 + (size_t)r * CZ + c * E));
+    st16(w1s + r * RS1 + c * E, ld16(w1 + (size_t)r * CZ + c * E));
   }
   for (int idx = tid; idx < CZ * rc2; idx += KT_THREADS) {
     const int r = idx / rc2, c = idx - r * rc2;
-    st16(w2s + (size_t)r * hp + ((c ^ (r & sw2)) * E), ld16(w2 + (size_t)r * hp + c * E));
+    st16(w2s + r * rs2 + c * E, ld16(w2 + (size_t)r * hp + c * E));
   }
   for (int idx = tid; idx < hp; idx += KT_THREADS) b1s[idx] = b1[idx];
   for (int idx = tid; idx < CZ; idx += KT_THREADS) b2s[idx] = b2[idx];
@@ -138,10 +162,9 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
   prepare();
   const int groups = hp / KG;
   for (int t = gw; t < tiles; t += nw) {
-    int opaque;  // keeps the loop-invariant LDS reads inside the loop
+    fetch(t + nw, f);  // the next tile's loads have this whole tile to land
+    int opaque;  // keeps the loop-invariant bias reads inside the loop
     asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
-    const T* const w1t = w1s + opaque;
-    const T* const w2t = w2s + opaque;
 
     f32x4 acc2[UO][KT_ST];
 #pragma unroll
@@ -151,18 +174,19 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
       for (int st = 0; st < KT_ST; ++st) acc2[v][st] = bv;
     }
     // one k group of the second GEMM: its hidden units from the first GEMM, ReLU, then the
-    // group's contribution to every output unit. After the last group's first GEMM zhat
-    // is dead and the next tile's loads go out.
-    auto group = [&](int g, bool last) {
+    // group's contribution to every output unit
+    auto group = [&](int g) {
       f32x4 h[UPG][KT_ST];
+      // this lane's row p of the group's first W_1 unit / chunk q of the group's W_2 columns
+      const T* const w1g = w1s + (g * UPG * 16 + p) * RS1 + q * E;
+      const T* const w2g = w2s + p * rs2 + (g * 4 + q) * E;
 #pragma unroll
       for (int uu = 0; uu < UPG; ++uu) {
         const int u = g * UPG + uu;
-        const int row = 16 * u + p;
         chunk_t wa[KZ];
 #pragma unroll
-        for (int ks = 0; ks < KZ; ++ks) wa[ks] = ld16(w1t + row * CZ + (((ks * 4 + q) ^ (row & SW1)) * E));
-        const f32x4 bv = ld16f(b1s + 16 * u + 4 * q + opaque);
+        for (int ks = 0; ks < KZ; ++ks) wa[ks] = ld16(w1g + uu * 16 * RS1 + ks * 4 * E);
+        const f32x4 bv = ld16f(b1s + 16 * u + 4 * q);
 #pragma unroll
         for (int st = 0; st < KT_ST; ++st) {
           h[uu][st] = bv;
@@ -170,7 +194,6 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
           for (int ks = 0; ks < KZ; ++ks) h[uu][st] = mma16(h[uu][st], wa[ks], za[st][ks], T());
         }
       }
-      if (last) fetch(t + nw, f);
       chunk_t hb[KT_ST];
 #pragma unroll
       for (int st = 0; st < KT_ST; ++st) {
@@ -178,20 +201,18 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
 #pragma unroll
         for (int uu = 0; uu < UPG; ++uu)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) hv[4 * uu + r] = fmaxf(h[uu][st][r], 0.f);
-        hb[st] = pack(hv, T());
+          for (int r = 0; r < 4; ++r) hv[4 * uu + r] = h[uu][st][r];
+        hb[st] = relu_packed(pack(hv, T()), T());
       }
 #pragma unroll
       for (int v = 0; v < UO; ++v) {
-        const int row = 16 * v + p;
-        const chunk_t wb = ld16(w2t + (size_t)row * hp + (((g * 4 + q) ^ (row & sw2)) * E));
+        const chunk_t wb = ld16(w2g + v * 16 * rs2);
 #pragma unroll
         for (int st = 0; st < KT_ST; ++st) acc2[v][st] = mma16(acc2[v][st], wb, hb[st], T());
       }
     };
 #pragma unroll 1
-    for (int g = 0; g + 1 < groups; ++g) group(g, false);
-    group(groups - 1, true);
+    for (int g = 0; g < groups; ++g) group(g);
 
     // out = z + m * acc: accumulator register r of output unit v is element
     // e = 4 (v % 2) + r of z chunk v / 2 (bf16), element r of chunk v (fp32)
@@ -218,7 +239,7 @@ template <class T, int KZ>
 static hipError_t launch_kt(const TransitionArgs& a, hipStream_t st) {
   constexpr int E = Traits<T>::E;
   (void)E;
-  const size_t lds = ((size_t)a.hp * a.cz * 2) * sizeof(T) + ((size_t)a.hp + a.cz) * sizeof(float);
+  const size_t lds = transition_lds_bytes(a.cz, a.hp, sizeof(T));
   auto fn = pair_transition_kernel<T, KZ>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);

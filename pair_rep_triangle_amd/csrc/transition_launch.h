@@ -17,13 +17,19 @@ struct TransitionArgs {
   int cz, hp, mask_all, num_cus;
 };
 
-// c_z chunk groups the kernel is compiled for (c_z = kz * 32 in bf16, kz * 16 in fp32)
+// LDS of one workgroup: W_1 [hp][cz] and W_2 [cz][hp] with 16 bytes of padding per row,
+// then the fp32 biases
+inline size_t transition_lds_bytes(int cz, int hp, size_t esz) {
+  return (size_t)hp * (cz * esz + 16) + (size_t)cz * (hp * esz + 16) + ((size_t)hp + cz) * 4;
+}
+
+// c_z chunk groups the kernel is compiled for (c_z = kz * 32 in bf16, kz * 16 in fp32);
+// both layers' weights must fit one workgroup's LDS
 inline bool transition_supported(bool bf16, int cz, int hp) {
   const int kg = bf16 ? 32 : 16;
   if (cz % kg || cz / kg < 1 || cz / kg > 4) return false;
   if (hp % kg || hp < kg) return false;
-  const size_t esz = bf16 ? 2 : 4;
-  return (size_t)hp * cz * 2 * esz <= 128 * 1024;  // both layers' weights in LDS
+  return transition_lds_bytes(cz, hp, bf16 ? 2 : 4) <= 160 * 1024;
 }
 
 hipError_t launch_transition(bool bf16, const TransitionArgs& a, hipStream_t st);

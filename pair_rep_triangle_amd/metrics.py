@@ -8,6 +8,9 @@ Per pair (b, i, j), storage element size `esz` (2 for bf16, 4 for fp32):
                   flops: 2 N c
   k3 output gate  reads x (c), z (c_z), mask (1); writes out (c_z)
                   flops: c -> c_z projection 2 c c_z, c_z -> c_z gate 2 c_z^2
+and of the pair transition (one kernel), per pair:
+  pair_transition reads z (c_z) and the mask (1), writes out (c_z)
+                  flops: c_z -> hidden and hidden -> c_z linears, 4 c_z hidden
 """
 
 MI355X_PEAK = {
@@ -28,3 +31,7 @@ def kernel_work(n, c_z, c, esz):
 def flops_per_pair(n, c_z, c):
     """Matmul flops of one direction per output pair: 2Nc + 10 c c_z + 2 c_z^2."""
     return 2 * n * c + 10 * c * c_z + 2 * c_z * c_z
+
+
+def transition_work(c_z, hidden, esz):
+    return {"bytes": esz * (2 * c_z + 1), "flops": 4 * c_z * hidden}
