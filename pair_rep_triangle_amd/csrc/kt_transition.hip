@@ -40,10 +40,15 @@ constexpr int KT_TW = 16 * KT_ST;   // pairs per wave tile
 
 // The scalar offset stays 0: a 16-byte store still reads its data registers after it
 // issues, and the compiler only guards those registers against the next write when the
-// store has no scalar offset register.
+// store has no scalar offset register. Device-scope stores (sc1): the output is written
+// through this XCD's L2 as it is produced, instead of sitting dirty there until the
+// end-of-kernel release writes it back (each XCD has its own L2; the next kernel may
+// read the output from any of them).
 __device__ __forceinline__ void store16(__amdgpu_buffer_rsrc_t r, chunk_t v, unsigned int voff) {
   typedef __attribute__((ext_vector_type(4))) int i32x4;
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, 0);
+  constexpr int kDeviceScope = 0x10;  // cache policy bit sc1
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0,
+                                         kDeviceScope);
 }
 
 // max(x, 0) on packed storage values: a negative bf16 or fp32 value is a negative 16- or
@@ -70,15 +75,14 @@ __device__ __forceinline__ chunk_t relu_packed(chunk_t c, float) {
 
 template <class T, int KZ>
 __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
-    const T* __restrict__ z, const T* __restrict__ mask, T* out, const T* __restrict__ w1,
-    const T* __restrict__ w2, const float* __restrict__ b1, const float* __restrict__ b2,
-    int tiles, int last_pairs, int hp, int mask_all) {
+    const T* __restrict__ z, const T* __restrict__ mask, T* out,
+    const chunk_t* __restrict__ image, int image_chunks, int tiles, int last_pairs, int hp,
+    int mask_all) {
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int CZ = KZ * KG;       // pair width
   constexpr int UO = CZ / 16;       // output units of 16 channels
   constexpr int UPG = KG / 16;      // hidden units per k group of the second GEMM
-  constexpr int RC1 = CZ / E;       // chunks per W_1 row
   constexpr int RS1 = CZ + E;       // W_1 row stride in LDS (one chunk of padding)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int rs2 = hp + E;                    // W_2 row stride in LDS
@@ -86,24 +90,10 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
   T* const w2s = w1s + (size_t)hp * RS1;     // [CZ][rs2]
   float* const b1s = (float*)(w2s + (size_t)CZ * rs2);  // [hp]
   float* const b2s = b1s + hp;                           // [CZ]
-  const int rc2 = hp / E;                    // chunks per W_2 row
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = lane & 15, q = lane >> 4;
-
-  // ---- weights and start values -> LDS ----
-  for (int idx = tid; idx < hp * RC1; idx += KT_THREADS) {
-    const int r = idx / RC1, c = idx - r * RC1;
-    st16(w1s + r * RS1 + c * E, ld16(w1 + (size_t)r * CZ + c * E));
-  }
-  for (int idx = tid; idx < CZ * rc2; idx += KT_THREADS) {
-    const int r = idx / rc2, c = idx - r * rc2;
-    st16(w2s + r * rs2 + c * E, ld16(w2 + (size_t)r * hp + c * E));
-  }
-  for (int idx = tid; idx < hp; idx += KT_THREADS) b1s[idx] = b1[idx];
-  for (int idx = tid; idx < CZ; idx += KT_THREADS) b2s[idx] = b2[idx];
-  __syncthreads();
 
   // tiles: 32-pair tiles in all (the last one holds last_pairs pairs)
   const int gw = blockIdx.x * KT_WAVES + wave;
@@ -158,7 +148,29 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
     }
   };
 
-  fetch(gw, f);
+  // ---- weights and start values -> LDS: the device copy of the weights is the LDS image
+  // itself (padded rows, then the biases), so the copy is flat: each thread has up to 16
+  // of its 16-byte chunks in flight before it stores any (at c_z = 128, hidden 256: all
+  // of them, one round trip), in a few dozen instructions. The first tile's z loads go
+  // out after the weight loads: loads retire in order, and the weights are needed first.
+  {
+    chunk_t* const lds = (chunk_t*)smem;
+    for (int base = 0; base < image_chunks; base += 16 * KT_THREADS) {
+      chunk_t v[16];
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int idx = base + k * KT_THREADS + tid;
+        if (idx < image_chunks) v[k] = image[idx];
+      }
+      if (base == 0) fetch(gw, f);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        const int idx = base + k * KT_THREADS + tid;
+        if (idx < image_chunks) lds[idx] = v[k];
+      }
+    }
+  }
+  __syncthreads();
   prepare();
   const int groups = hp / KG;
   for (int t = gw; t < tiles; t += nw) {
@@ -240,6 +252,7 @@ static hipError_t launch_kt(const TransitionArgs& a, hipStream_t st) {
   constexpr int E = Traits<T>::E;
   (void)E;
   const size_t lds = transition_lds_bytes(a.cz, a.hp, sizeof(T));
+  if (lds != a.image_bytes || lds % 16) return hipErrorInvalidValue;
   auto fn = pair_transition_kernel<T, KZ>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
@@ -255,7 +268,7 @@ static hipError_t launch_kt(const TransitionArgs& a, hipStream_t st) {
   const int blocks = (int)(need < cap ? need : cap);
   if (blocks <= 0) return hipSuccess;
   hipLaunchKernelGGL(fn, dim3(blocks), dim3(KT_THREADS), lds, st, (const T*)a.z,
-                     (const T*)a.mask, (T*)a.out, (const T*)a.w1, (const T*)a.w2, a.b1, a.b2,
+                     (const T*)a.mask, (T*)a.out, (const chunk_t*)a.image, (int)(lds / 16),
                      (int)tiles, (int)(a.pairs - (tiles - 1) * KT_TW), a.hp, a.mask_all);
   return hipGetLastError();
 }

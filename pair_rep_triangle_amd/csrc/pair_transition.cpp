@@ -16,9 +16,9 @@
 struct pair_transition_handle {
   int c_z, hidden, hp, dtype, device, num_cus;
   bool bf16;
-  void* block;  // w1 | w2 | b1 | b2 | one
-  const void *w1, *w2, *one;
-  const float *b1, *b2;
+  void* block;  // LDS image of the weights | one
+  const void *image, *one;
+  size_t image_bytes;
 };
 
 namespace {
@@ -62,16 +62,19 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
   int rc = check_device(&dev, &cus);
   if (rc != TRI_MUL_OK) return rc;
 
+  // the kernel's LDS image: W_1' [hp][c_z + pad] | W_2 [c_z][hp + pad] | b_1' [hp] | b_2 [c_z]
+  // (pad: one 16-byte chunk of zeros per row), then the one-element mask `one`
   const size_t esz = bf16 ? 2 : 4;
-  const size_t w1b = align256((size_t)hp * c_z * esz), w2b = align256((size_t)c_z * hp * esz);
-  const size_t b1b = align256((size_t)hp * 4), b2b = align256((size_t)c_z * 4), oneb = 256;
-  const size_t total = w1b + w2b + b1b + b2b + oneb;
+  const size_t pad = 16 / esz;
+  const size_t rs1 = (size_t)c_z + pad, rs2 = (size_t)hp + pad;
+  const size_t image = trimul::transition_lds_bytes(c_z, hp, esz);
+  const size_t total = align256(image) + 256;
   std::vector<unsigned char> host(total, 0);
   unsigned char* hw1 = host.data();
-  unsigned char* hw2 = hw1 + w1b;
-  float* hb1 = (float*)(hw2 + w2b);
-  float* hb2 = (float*)((unsigned char*)hb1 + b1b);
-  unsigned char* hone = (unsigned char*)hb2 + b2b;
+  unsigned char* hw2 = hw1 + (size_t)hp * rs1 * esz;
+  float* hb1 = (float*)(hw2 + (size_t)c_z * rs2 * esz);
+  float* hb2 = hb1 + hp;
+  unsigned char* hone = host.data() + align256(image);
   store_elem(hone, 1.0f, bf16);
 
   // W_1' = W_1 diag(gamma), b_1' = W_1 beta + b_1 (sums in double); padded units stay 0
@@ -79,7 +82,7 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
     double t = w->b1 ? (double)w->b1[h] : 0.0;
     for (int k = 0; k < c_z; ++k) {
       const double wk = w->w1[(size_t)h * c_z + k];
-      store_elem(hw1 + ((size_t)h * c_z + k) * esz,
+      store_elem(hw1 + ((size_t)h * rs1 + k) * esz,
                  (float)(wk * (w->ln_gamma ? (double)w->ln_gamma[k] : 1.0)), bf16);
       if (w->ln_beta) t += wk * (double)w->ln_beta[k];
     }
@@ -92,7 +95,7 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
     for (int s = 0; s < hp; ++s) {
       const int hu = hidden_of_slot(s, bf16);
       const float v = hu < hidden ? w->w2[(size_t)ch * hidden + hu] : 0.f;
-      store_elem(hw2 + ((size_t)R * hp + s) * esz, v, bf16);
+      store_elem(hw2 + ((size_t)R * rs2 + s) * esz, v, bf16);
     }
   }
 
@@ -120,11 +123,9 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
   h->num_cus = cus;
   h->bf16 = bf16;
   h->block = dptr;
-  h->w1 = d;
-  h->w2 = d + w1b;
-  h->b1 = (const float*)(d + w1b + w2b);
-  h->b2 = (const float*)(d + w1b + w2b + b1b);
-  h->one = d + w1b + w2b + b1b + b2b;
+  h->image = d;
+  h->image_bytes = image;
+  h->one = d + align256(image);
   *out = h;
   return TRI_MUL_OK;
 }
@@ -149,10 +150,8 @@ int pair_transition_forward(pair_transition_handle* h, const void* z, const void
   a.z = z;
   a.mask = pair_mask ? pair_mask : h->one;
   a.out = out;
-  a.w1 = h->w1;
-  a.w2 = h->w2;
-  a.b1 = h->b1;
-  a.b2 = h->b2;
+  a.image = h->image;
+  a.image_bytes = h->image_bytes;
   a.pairs = (long long)pairs;
   a.cz = h->c_z;
   a.hp = h->hp;

@@ -9,10 +9,12 @@ struct TransitionArgs {
   const void* z;      // [pairs][cz]
   const void* mask;   // [pairs], or the one-element `one` when there is no mask
   void* out;          // [pairs][cz] (may be z itself)
-  const void* w1;     // [hp][cz]  W_1 diag(gamma), padded hidden rows zero
-  const void* w2;     // [cz][hp]  W_2 with rows and columns in the kernel's order
-  const float* b1;    // [hp]      W_1 beta + b_1
-  const float* b2;    // [cz]      b_2 in the kernel's row order
+  // the weights as the kernel's LDS image (transition_lds_bytes): W_1 diag(gamma)
+  // [hp][cz + pad] (padded hidden rows zero), W_2 [cz][hp + pad] with rows and columns in
+  // the kernel's order, then fp32 b_1' = W_1 beta + b_1 [hp] and b_2 [cz] (kernel order);
+  // pad = 16 bytes of zeros per row
+  const void* image;
+  size_t image_bytes;
   long long pairs;    // B * N * N
   int cz, hp, mask_all, num_cus;
 };
