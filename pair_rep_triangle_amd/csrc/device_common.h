@@ -60,6 +60,35 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc_u32(const void* base, unsigned int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
 }
+// Flat copy of `chunks` 16-byte chunks from device memory to LDS by a workgroup of NT
+// threads: whole batches of 16 chunks per thread with all 16 loads in flight before the
+// first store and no per-chunk predicate (which would put each load and store behind its
+// own branch), then the remainder one chunk per thread at a time. `after_first_loads`
+// runs once, right after the first batch's loads are issued (or before the remainder
+// when there is no whole batch): the place for other loads that may wait behind them.
+template <int NT, class F>
+__device__ __forceinline__ void copy_image(const chunk_t* __restrict__ src, chunk_t* dst,
+                                           int chunks, int tid, F after_first_loads) {
+  const int whole = chunks / (16 * NT) * (16 * NT);
+  chunk_t v[16];
+  if (whole > 0) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = src[k * NT + tid];
+  }
+  after_first_loads();  // one call site: its code appears once
+  if (whole > 0) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dst[k * NT + tid] = v[k];
+  }
+  for (int base = 16 * NT; base < whole; base += 16 * NT) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = src[base + k * NT + tid];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) dst[base + k * NT + tid] = v[k];
+  }
+  for (int idx = whole + tid; idx < chunks; idx += NT) dst[idx] = src[idx];
+}
+
 // Bytes left of an extent `bytes` after skipping `skip` (both below 2^31), at least 0. A
 // signed max: the unsigned "a > b ? a - b : 0" becomes a saturating subtract, which has
 // only a vector form, and a resource field in a vector register turns every load through

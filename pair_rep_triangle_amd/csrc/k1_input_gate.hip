@@ -20,6 +20,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "k1w_layout.h"
 
 namespace trimul {
 
@@ -291,15 +292,11 @@ __device__ __forceinline__ void progress_priority(int level) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-constexpr int K1W_WAVES = 8;
-constexpr int K1W_THREADS = 64 * K1W_WAVES;
-constexpr int K1W_TP = 64;  // pairs per wave tile
-
 template <class T>
 __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     const T* __restrict__ z, const T* __restrict__ mask, T* __restrict__ a_out,
-    T* __restrict__ b_out, const T* __restrict__ w1, const float* __restrict__ t1, int n, int np,
-    int cz, int c, int incoming, int mask_all, int ug, int total_tiles) {
+    T* __restrict__ b_out, const chunk_t* __restrict__ image, int n, int np, int cz, int c,
+    int incoming, int mask_all, int ug, int total_tiles) {
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int KZ = 4;               // chunk groups along c_z
@@ -307,6 +304,7 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   constexpr int ST = K1W_TP / 16;     // 16-pair subtiles per tile
   constexpr int NOUT = 16 / E;        // 16-byte stores per lane and unit (16 pairs)
   static_assert(RC == 16, "chunk count the swizzle assumes");
+  static_assert(KZ * KG * sizeof(T) == K1W_ROW_BYTES, "row size of the weight image");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int czp = KZ * KG;
   const int rows = ug * 32;  // gate and projection rows of this group's units
@@ -375,30 +373,15 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   const int gw = blockIdx.x * K1W_WAVES + wave;
   const int nw = gridDim.x * K1W_WAVES;
   Pre f;
-  fetch(gw, f);  // the first tile's z is in flight while the weights go to LDS
-
-  // ---- the group's weight rows and start values -> LDS (all loads issued first) ----
-  // LDS row lr = 32*uu + 16*gp + r holds device row (2*uq + gp)*c + ucb + r of unit u0+uu
-  auto dev_row = [&](int lr) {
-    const int uu = lr >> 5, gp = (lr >> 4) & 1, r = lr & 15;
-    const int u = u0 + uu, uq = u / cblocks, ucb = (u - uq * cblocks) * 16;
-    return (2 * uq + gp) * c + ucb + r;
-  };
+  // ---- the group's weights -> LDS. The handle keeps each group's weights as the LDS
+  // image itself (swizzled rows, then their start values), so the copy is flat: each
+  // thread has up to 16 of its 16-byte chunks in flight before it stores any. The first
+  // tile's z loads go out after the first weight loads (loads retire in order, and the
+  // weights are needed first) and land while the weights are stored. ----
   {
-    constexpr int NW = (16 * 32 * RC + K1W_THREADS - 1) / K1W_THREADS;  // at most 16 units
-    chunk_t v[NW];
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
-      v[k] = ld16(w1 + (size_t)dev_row(lr < rows ? lr : 0) * czp + cc * E);
-    }
-    const float tv = tid < rows ? t1[dev_row(tid)] : 0.f;
-#pragma unroll
-    for (int k = 0; k < NW; ++k) {
-      const int idx = tid + K1W_THREADS * k, lr = idx / RC, cc = idx - lr * RC;
-      if (lr < rows) st16(wl + lr * czp + ((cc ^ (lr & 15)) * E), v[k]);
-    }
-    if (tid < rows) tl[tid] = tv;
+    const int chunks = (int)(k1w_image_bytes(ug) / 16);
+    const chunk_t* const src = image + (size_t)blockIdx.y * chunks;
+    copy_image<K1W_THREADS>(src, (chunk_t*)smem, chunks, tid, [&]() { fetch(gw, f); });
   }
   __syncthreads();
 
@@ -586,13 +569,6 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   }
 }
 
-template <class T>
-static size_t k1w_lds(int ug) {
-  constexpr int czp = 4 * Traits<T>::KG;
-  return (size_t)ug * 32 * czp * sizeof(T) + (size_t)ug * 32 * sizeof(float) +
-         (size_t)K1W_WAVES * K1W_TP * sizeof(float);
-}
-
 // Launches the wave-independent form if the units split into groups that fit LDS;
 // *done = false leaves the launch to the tile-shared form.
 template <class T>
@@ -600,19 +576,15 @@ static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
   *done = false;
   // the per-lane z offsets are 32-bit byte offsets within one batch item's z
   if ((size_t)a.n * a.n * a.cz * sizeof(T) >= 0x80000000ull) return hipSuccess;
+  // the handle's weight images are built for this group size (units go in pairs)
   const int units = 2 * (a.c / 16);
-  int ug = 0;
-  for (int g = units < 16 ? units : 16; g >= 2; g -= 2)  // even: units go in pairs
-    if (units % g == 0 && k1w_lds<T>(g) <= LDS_PER_CU) {
-      ug = g;
-      break;
-    }
+  const int ug = a.k1w_image ? k1w_group_units(a.c) : 0;
   if (ug == 0) return hipSuccess;
   // each wave pays the weight copy and its first tile's loads up front: with fewer than
   // two tiles per wave of a full grid the tile-shared form is faster
   const int total = a.batch * a.np * (a.np / K1W_TP);
   if (total < 2 * a.num_cus * K1W_WAVES) return hipSuccess;
-  const size_t lds = k1w_lds<T>(ug);
+  const size_t lds = k1w_lds_bytes(ug);
   auto fn = k1_input_gate_waves<T>;
   static std::atomic<int> granted{0};
   hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
@@ -626,8 +598,9 @@ static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
   const int blocks = need < cap ? need : cap;
   const int mask_all = a.mask == nullptr;
   hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K1W_THREADS), lds, st, (const T*)a.z,
-                     (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b, (const T*)a.w1,
-                     a.t1, a.n, a.np, a.cz, a.c, a.incoming, mask_all, ug, total);
+                     (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b,
+                     (const chunk_t*)a.k1w_image, a.n, a.np, a.cz, a.c, a.incoming, mask_all, ug,
+                     total);
   *done = true;
   return hipGetLastError();
 }

@@ -154,21 +154,7 @@ __global__ __launch_bounds__(KT_THREADS) void pair_transition_kernel(
   // of them, one round trip), in a few dozen instructions. The first tile's z loads go
   // out after the weight loads: loads retire in order, and the weights are needed first.
   {
-    chunk_t* const lds = (chunk_t*)smem;
-    for (int base = 0; base < image_chunks; base += 16 * KT_THREADS) {
-      chunk_t v[16];
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int idx = base + k * KT_THREADS + tid;
-        if (idx < image_chunks) v[k] = image[idx];
-      }
-      if (base == 0) fetch(gw, f);
-#pragma unroll
-      for (int k = 0; k < 16; ++k) {
-        const int idx = base + k * KT_THREADS + tid;
-        if (idx < image_chunks) lds[idx] = v[k];
-      }
-    }
+    copy_image<KT_THREADS>(image, (chunk_t*)smem, image_chunks, tid, [&]() { fetch(gw, f); });
   }
   __syncthreads();
   prepare();

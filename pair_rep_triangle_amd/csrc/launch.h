@@ -26,6 +26,8 @@ struct StageArgs {
   const void* wg;    // [cz][czp]    W_g diag(gamma_in) times -log2(e)
   const float* tg;   // [cz]         (W_g beta_in + b_g) times -log2(e)
   const void* one;   // one element of value 1 in the storage type (stands in for no mask)
+  const void* k1w_image;  // the wave-independent input gate's weights, one LDS image per
+                          // unit group (k1w_layout.h), or nullptr when that form is unused
   int batch, n, np, cz, czp, c, cp, incoming, num_cus;
   int residual;      // stage 3 writes z + update instead of the update (out may be z)
 };

@@ -12,6 +12,7 @@
 #include <vector>
 
 #include "host_common.h"
+#include "k1w_layout.h"
 #include "launch.h"
 
 struct tri_mul_handle {
@@ -49,6 +50,31 @@ void fold(const float* W, const float* gamma, const float* beta, const float* bi
     }
     t[r] = (float)(scale * trow);
   }
+}
+
+// The wave-independent input gate's weights as its LDS images, one per group of ug units
+// (k1w_layout.h): image row lr = 32 uu + 16 gp + r of group g is the stored row
+// (2 uq + gp) c + 16 cb + r of unit u = g ug + uu (uq = u / (c / 16): a or b; cb = its
+// 16-channel block; gp: gate or projection row), its 16-byte chunk k at position
+// k ^ (lr & 15); the rows' start values follow the rows. w1 rows are 256 bytes here.
+void build_k1w_images(const unsigned char* w1, const float* t1, int c, int ug, int groups,
+                      int esz, unsigned char* dst) {
+  if (ug == 0) return;
+  const int cblocks = c / 16, rows = ug * 32;
+  const size_t rb = trimul::K1W_ROW_BYTES;
+  for (int g = 0; g < groups; ++g) {
+    unsigned char* img = dst + (size_t)g * trimul::k1w_image_bytes(ug);
+    float* timg = (float*)(img + (size_t)rows * rb);
+    for (int lr = 0; lr < rows; ++lr) {
+      const int uu = lr >> 5, gp = (lr >> 4) & 1, r = lr & 15;
+      const int u = g * ug + uu, uq = u / cblocks, cb = u - uq * cblocks;
+      const size_t dr = (size_t)(2 * uq + gp) * c + cb * 16 + r;
+      for (int k = 0; k < 16; ++k)
+        memcpy(img + lr * rb + (size_t)(k ^ (lr & 15)) * 16, w1 + dr * rb + (size_t)k * 16, 16);
+      timg[lr] = t1[dr];
+    }
+  }
+  (void)esz;
 }
 
 struct Layout {
@@ -164,7 +190,12 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   const size_t t1b = align256((size_t)4 * c * sizeof(float));
   const size_t tob = align256((size_t)c_z * sizeof(float));
   const size_t oneb = 256;
-  const size_t total = w1b + wob + wgb + t1b + 2 * tob + oneb;
+  // the wave-independent input gate (four chunk groups along c_z) reads its weights as one
+  // LDS image per unit group
+  const int k1w_ug = czp == 4 * kg ? trimul::k1w_group_units(c) : 0;
+  const int k1w_groups = k1w_ug ? 2 * (c / 16) / k1w_ug : 0;
+  const size_t k1wb = align256((size_t)k1w_groups * (k1w_ug ? trimul::k1w_image_bytes(k1w_ug) : 0));
+  const size_t total = w1b + wob + wgb + t1b + 2 * tob + oneb + k1wb;
   std::vector<unsigned char> host(total, 0);
   unsigned char* hw1 = host.data();
   unsigned char* hwo = hw1 + w1b;
@@ -187,6 +218,8 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
          (q % 2 == 0) ? ng : 1.0, hw1 + (size_t)q * c * czp * esz, ht1 + q * c);
   fold(w->w_out, w->ln_out_gamma, w->ln_out_beta, w->b_out, c_z, c, cp, bf16, 1.0, hwo, hto);
   fold(w->w_gate, w->ln_in_gamma, w->ln_in_beta, w->b_gate, c_z, c_z, czp, bf16, ng, hwg, htg);
+  unsigned char* himg = hone + oneb;
+  build_k1w_images(hw1, ht1, c, k1w_ug, k1w_groups, esz, himg);  // rows of czp * esz = 256 bytes
 
   tri_mul_handle* h = new (std::nothrow) tri_mul_handle();
   if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
@@ -222,6 +255,7 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   a.to = (const float*)(d + ((unsigned char*)hto - hw1));
   a.tg = (const float*)(d + ((unsigned char*)htg - hw1));
   a.one = d + (hone - hw1);
+  a.k1w_image = k1w_ug ? d + (himg - hw1) : nullptr;
   a.cz = c_z;
   a.czp = czp;
   a.c = c;
