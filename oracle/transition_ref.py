@@ -24,7 +24,7 @@ What is computed (per batch item b and residue pair (i, j); float64 NumPy):
 Weights are fp32 host arrays in nn.Linear orientation ([out][in]); ``mask`` None means
 all ones.
 
-Parity pins (tests/test_oracle_pins.py, none of them reuses this code): pure-Python
+Parity pins (tests/test_transition_pins.py, none of them reuses this code): pure-Python
 loops on tiny inputs, zero second layer (out = z exactly), zero mask, the all-active
 ReLU region against the composed matrix W_2 W_1, the all-inactive region (update =
 b_2), LayerNorm invariance to a per-pair affine change of z, and pair permutation.
