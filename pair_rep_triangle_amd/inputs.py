@@ -90,6 +90,30 @@ def make_transition_weights(rng, c_z, hidden, random_affine=False):
     return out
 
 
+def attention_weight_shapes(c_z, heads, d):
+    hd = heads * d
+    return {"ln_gamma": (c_z,), "ln_beta": (c_z,), "w_q": (hd, c_z), "w_k": (hd, c_z),
+            "w_v": (hd, c_z), "w_b": (heads, c_z), "w_g": (hd, c_z), "b_g": (hd,),
+            "w_o": (c_z, hd), "b_o": (c_z,)}
+
+
+def make_attention_weights(rng, c_z, heads, d, random_affine=False):
+    """float32 triangular-attention weights (nn.Linear orientation, heads stacked along
+    the output rows). Matrices N(0, 1/fan_in); LayerNorm gamma 1 / beta 0 and zero
+    biases unless random_affine."""
+    out = {}
+    for name, shape in attention_weight_shapes(c_z, heads, d).items():
+        if name.startswith("w_"):
+            out[name] = (rng.standard_normal(shape) / np.sqrt(shape[1])).astype(np.float32)
+        elif name == "ln_gamma":
+            out[name] = (1.0 + 0.2 * rng.standard_normal(shape) if random_affine
+                         else np.ones(shape)).astype(np.float32)
+        else:
+            out[name] = (0.2 * rng.standard_normal(shape) if random_affine
+                         else np.zeros(shape)).astype(np.float32)
+    return out
+
+
 def block_mask(batch, n, lengths):
     """1 on the leading L x L block of each item, 0 on padding."""
     m = np.zeros((batch, n, n), dtype=np.float32)
