@@ -8,5 +8,5 @@ from .transition_ref import (  # noqa: F401
     TRANSITION_FIELDS, pair_transition_ref, pair_transition_update, transition_shapes,
 )
 from .attention_ref import (  # noqa: F401
-    ATTENTION_FIELDS, NODES, attention_shapes, tri_attention_ref,
+    ATTENTION_FIELDS, NODES, attention_shapes, tri_attention_ref, tri_attention_ref_lines,
 )

@@ -100,7 +100,8 @@ def _masked_softmax(s, valid):
 
 
 def _attend(q, k, v, bias, mask, node, chunk):
-    """Attention output per head, [B, N, N, H, d], before the gate."""
+    """Attention output per head, [B, N, N, H, d], before the gate. Around the starting
+    node q, k, v and mask may hold a subset of the rows (the bias stays whole)."""
     B, N, _, H, d = q.shape
     out = np.zeros_like(q)
     scale = 1.0 / np.sqrt(d)
@@ -142,3 +143,25 @@ def tri_attention_ref(z, mask, w, node, chunk=64):
     q, k, v, g, bias = _projections(z, w)
     o = g * _attend(q, k, v, bias, mask, node, chunk)
     return o.reshape(B, N, N, -1) @ _f64(w["w_o"]).T + _f64(w["b_o"])
+
+
+def tri_attention_ref_lines(z, mask, w, node, lines, chunk=64):
+    """The output restricted to some query lines: rows i (starting node) or columns j
+    (ending node) in `lines`; returns [B, len(lines), N, c_z] with [b, t, u] the pair
+    (lines[t], u) around the starting node and (u, lines[t]) around the ending node.
+    Each line only needs its own queries, keys and values plus the pair bias, so this is
+    the same computation as tri_attention_ref on fewer lines."""
+    if node not in NODES:
+        raise ValueError(f"node must be one of {NODES}")
+    z = _f64(z)
+    B, N = z.shape[0], z.shape[1]
+    mask = np.ones((B, N, N)) if mask is None else _f64(mask)
+    lines = np.asarray(lines)
+    q, k, v, g, bias = _projections(z, w)
+    if node == "ending":  # the ending node is the starting node on the transposed grid
+        q, k, v, g = (np.swapaxes(t, 1, 2) for t in (q, k, v, g))
+        bias = np.swapaxes(bias, 2, 3)
+        mask = np.swapaxes(mask, 1, 2)
+    sel = _attend(q[:, lines], k[:, lines], v[:, lines], bias, mask[:, lines], "starting", chunk)
+    o = g[:, lines] * sel
+    return o.reshape(B, len(lines), N, -1) @ _f64(w["w_o"]).T + _f64(w["b_o"])

@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtrimul.so")
 SOURCES = ("k1_input_gate.hip", "k2_contract.hip", "k3_output_gate.hip", "kt_transition.hip",
-           "tri_mul.cpp", "pair_transition.cpp")
+           "ka_attention.hip", "tri_mul.cpp", "pair_transition.cpp", "tri_attention.cpp")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -1,0 +1,74 @@
+// Launch interface of the triangular-attention kernels (host code in tri_attention.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace trimul {
+
+constexpr int ATT_D = 32;      // head width the kernels are compiled for
+constexpr int ATT_PAD = 64;    // the stored pair grid is padded to a multiple of this
+
+// Storage of the projections ("stored coordinates" (r, c): (i, j) around the starting
+// node, (j, i) around the ending node, so both nodes attend along stored rows):
+//   q, k, g  [B][Np][H][Np][d]   bf16   (g already through the sigmoid)
+//   vt       [B][Np][H][d][Np]   bf16   (v transposed: keys contiguous)
+//   bias     [B][H][Np][Np]      fp32   (the pair bias of stored pair (r, c), base 2)
+//   ms       [B][Np][Np]         bf16   (the pair mask in stored coordinates, 0 on padding)
+struct AttnWorkspace {
+  size_t q, k, g, vt, bias, ms, total;
+};
+inline size_t att_align(size_t v) { return (v + 255) / 256 * 256; }
+inline int att_np(int n) { return (n + ATT_PAD - 1) / ATT_PAD * ATT_PAD; }
+inline AttnWorkspace att_workspace(int batch, int n, int heads) {
+  const size_t np = (size_t)att_np(n);
+  const size_t plane = (size_t)batch * np * np;
+  AttnWorkspace w;
+  const size_t qkv = att_align(plane * heads * ATT_D * 2);
+  w.q = 0;
+  w.k = w.q + qkv;
+  w.g = w.k + qkv;
+  w.vt = w.g + qkv;
+  w.bias = w.vt + qkv;
+  w.ms = w.bias + att_align(plane * heads * 4);
+  w.total = w.ms + att_align(plane * 2);
+  return w;
+}
+
+// Projection weights as the projection kernel's LDS image: rows [q | k | g | v] (H*d each)
+// then 16 bias rows (H used), each c_z + 8 bf16 (one 16-byte chunk of padding); then the
+// fp32 start value of every row (W beta, plus b_g for the gate rows).
+inline int att_proj_rows(int heads) { return 4 * heads * ATT_D + 16; }
+inline size_t att_proj_image_bytes(int cz, int heads) {
+  const size_t rows = (size_t)att_proj_rows(heads);
+  return rows * (cz + 8) * 2 + rows * 4;
+}
+// Output weights as the attention kernel's LDS image: W_o [c_z][H*d + 8] bf16, then b_o
+// [c_z] fp32; the attention kernel adds its staging rows [64][H*d + 8] bf16 after them.
+inline size_t att_out_image_bytes(int cz, int heads) {
+  return (size_t)cz * (heads * ATT_D + 8) * 2 + (size_t)cz * 4;
+}
+inline size_t att_core_lds_bytes(int cz, int heads) {
+  return att_out_image_bytes(cz, heads) + (size_t)64 * (heads * ATT_D + 8) * 2;
+}
+
+struct AttnArgs {
+  const void* z;      // [B][N][N][c_z] bf16
+  const void* mask;   // [B][N][N] bf16, or the one-element `one` when there is no mask
+  void* out;          // [B][N][N][c_z] bf16
+  void* ws;           // workspace base (att_workspace layout)
+  const void* proj_image;
+  const void* out_image;
+  int batch, n, cz, heads, node, mask_all, num_cus;
+};
+
+inline bool attention_supported(int cz, int heads, int d) {
+  if (d != ATT_D || heads < 1 || heads > 8) return false;
+  if (cz % 32 || cz < 32 || cz > 128) return false;
+  return att_proj_image_bytes(cz, heads) <= 160 * 1024 &&
+         att_core_lds_bytes(cz, heads) <= 160 * 1024;
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+
+}  // namespace trimul

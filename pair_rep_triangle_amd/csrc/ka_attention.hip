@@ -1,0 +1,410 @@
+// Triangular attention (starting and ending node), two kernels:
+//   ka_project: LayerNorm of z and every projection (q, k, gate, v, per-head pair bias)
+//               with MFMAs, written in stored coordinates;
+//   ka_core:    per stored row, flash attention for every head over 32-key tiles, the
+//               gate, and the output projection, written to out.
+// Definition and sources: include/tri_attention.h (yage.ai summary of the
+// biomolecular-software report: triangular attention as a pair operation of cubic cost
+// with a fused kernel; OpenFold-TRT summary: triangular attention among the pair
+// kernels). Stored coordinates (r, c) are (i, j) around the starting node and (j, i)
+// around the ending node: both nodes then attend along a stored row, keys indexed by the
+// stored column, and the pair bias of query column qc and key column kc is the bias of
+// stored pair (qc, kc).
+
+#include "attention_launch.h"
+#include "device_common.h"
+
+namespace trimul {
+
+typedef __attribute__((ext_vector_type(2))) unsigned int u32x2;
+
+constexpr int KA_WAVES = 8;                  // projection kernel
+constexpr int KA_THREADS = 64 * KA_WAVES;
+constexpr int KA_TW = 32;                    // pairs per projection wave tile
+constexpr int KC_WAVES = 4;                  // attention kernel
+constexpr int KC_THREADS = 64 * KC_WAVES;
+constexpr int KC_QT = 64;                    // queries per attention tile
+constexpr int KC_KT = 32;                    // keys per attention step
+
+// ---------------------------------------------------------------------------------------
+// ka_project. A wave tile is 32 consecutive stored columns (two 16-pair subtiles) of one
+// stored row. z arrives in MFMA operand layout (lane (p, q): chunk ks*4 + q of pair p),
+// is normalised in registers and is the B operand of the q, k and gate units (W rows as
+// A: lane (p, q) ends with outputs 4q..4q+3 of pair p, four consecutive head channels)
+// and the A operand of the v and bias units (W rows as B: lane (p, q) ends with pairs
+// 4q..4q+3 of output p, four consecutive stored columns of v^T and of the bias plane).
+// The weights (LDS image, rows padded by 16 bytes) are loaded once per workgroup.
+template <int KZ>
+__global__ __launch_bounds__(KA_THREADS) void ka_project(
+    const bf16* __restrict__ z, const bf16* __restrict__ mask, const chunk_t* __restrict__ image,
+    int image_chunks, bf16* __restrict__ qo, bf16* __restrict__ ko, bf16* __restrict__ go,
+    bf16* __restrict__ vto, float* __restrict__ bo, bf16* __restrict__ mso, int batch, int n,
+    int np, int heads, int ending, int mask_all) {
+  constexpr int E = 8, KG = 32, CZ = KZ * KG, RS = CZ + 8;  // LDS row stride (elements)
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int hd = heads * ATT_D;
+  const int rows = 4 * hd + 16;
+  const bf16* const wl = (const bf16*)smem;
+  const float* const tl = (const float*)(smem + (size_t)rows * RS * 2);  // start values
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int p = lane & 15, q = lane >> 4;
+  const int ctiles = np / KA_TW;
+  const int tiles = batch * np * ctiles;
+  const int gw = blockIdx.x * KA_WAVES + wave, nw = gridDim.x * KA_WAVES;
+  // stored (r, c) -> z pair (x, y); consecutive stored columns are 1 (starting) or n
+  // (ending) z pairs apart
+  const size_t pstride = ending ? (size_t)n : 1;
+
+  struct Pre {
+    chunk_t zv[2][KZ];
+    bf16 m[2];
+  };
+  auto coords = [&](int t, int& b, int& r, int& c0) {
+    b = t / (np * ctiles);
+    const int rem = t - b * np * ctiles;
+    r = rem / ctiles;
+    c0 = (rem - r * ctiles) * KA_TW;
+  };
+  // Pairs outside n x n read as zero (their resource extent ends at the last real pair of
+  // the subtile's run; rows past n get an empty extent).
+  auto fetch = [&](int t, Pre& f) {
+    int b, r, c0;
+    coords(t < tiles ? t : tiles - 1, b, r, c0);
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int cs = c0 + 16 * st;
+      const bool ok = r < n && cs < n;
+      const size_t x = ending ? (size_t)cs : (size_t)r, y = ending ? (size_t)r : (size_t)cs;
+      const size_t p0 = ok ? ((size_t)b * n + x) * n + y : 0;
+      // pairs from the subtile's first to the last real one of its run
+      const size_t span = ok ? (size_t)(n - 1 - cs) * pstride + 1 : 0;
+      const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(z + p0 * CZ, span * CZ * 2);
+      const __amdgpu_buffer_rsrc_t rm =
+          mask_all ? buffer_rsrc(mask, 2) : buffer_rsrc(mask + p0, span * 2);
+      const unsigned int zoff = (unsigned int)(((size_t)p * pstride * CZ + q * E) * 2);
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) f.zv[st][ks] = load16(rz, zoff + ks * KG * 2, 0);
+      f.m[st] = load_elem(rm, mask_all ? 0u : (unsigned int)(p * pstride * 2), 0, bf16());
+    }
+  };
+
+  Pre f;
+  copy_image<KA_THREADS>(image, (chunk_t*)smem, image_chunks, tid, [&]() { fetch(gw, f); });
+  __syncthreads();
+
+  for (int t = gw; t < tiles; t += nw) {
+    int b, r, c0;
+    coords(t, b, r, c0);
+    chunk_t za[2][KZ];
+    float mv[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      mv[st] = (r < n && c0 + 16 * st + p < n) ? to_f32(f.m[st]) : 0.f;
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) za[st][ks] = f.zv[st][ks];
+      normalize_operand_row<KZ>(za[st], CZ, lane, bf16());
+    }
+    fetch(t + nw, f);  // the next tile's loads have this tile's MFMAs to land
+
+    const size_t rowbase = ((size_t)b * np + r) * heads;  // [b][r][h] of q, k, g, v^T
+    int opaque;  // keeps the loop-invariant LDS reads inside the tile loop
+    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+
+    // q, k and gate units: W rows as A. Output row o = 16u + 4q + rr of the block's
+    // projection (h = o / d, channel o % d), pair c0 + 16 st + p.
+    auto unit_a = [&](int row0, int which, bf16* dst) {
+      const bf16* const wrow = wl + (row0 + p) * RS + q * E + opaque;
+      chunk_t wa[KZ];
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) wa[ks] = ld16(wrow + ks * KG);
+      const f32x4 t0 = ld16f(tl + row0 + 4 * q + opaque);
+      const int o = row0 - which * hd + 4 * q;  // first of this lane's four outputs
+      const int h = o / ATT_D, dd = o - h * ATT_D;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        f32x4 acc = t0;
+#pragma unroll
+        for (int ks = 0; ks < KZ; ++ks) acc = mma16(acc, wa[ks], za[st][ks], bf16());
+        if (which == 2) {  // gate: rows scaled by -log2(e), sigmoid = 1 / (1 + 2^acc)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_rcpf(1.f + exp2f(acc[e]));
+        }
+        const int c = c0 + 16 * st + p;
+        store4(dst + ((rowbase + h) * np + c) * ATT_D + dd, acc[0], acc[1], acc[2], acc[3]);
+      }
+    };
+    // v and bias units: W rows as B. Lane (p, q): pairs c0 + 16 st + 4q .. +3, output
+    // 16u' + p of the block.
+    auto unit_b = [&](int row0, bool bias) {
+      const bf16* const wrow = wl + (row0 + p) * RS + q * E + opaque;
+      chunk_t wb[KZ];
+#pragma unroll
+      for (int ks = 0; ks < KZ; ++ks) wb[ks] = ld16(wrow + ks * KG);
+      const float t0 = tl[row0 + p + opaque];
+      const int o = bias ? p : row0 - 3 * hd + p;
+      const int h = o / ATT_D, dd = o - h * ATT_D;
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        f32x4 acc = {t0, t0, t0, t0};
+#pragma unroll
+        for (int ks = 0; ks < KZ; ++ks) acc = mma16(acc, za[st][ks], wb[ks], bf16());
+        const int c = c0 + 16 * st + 4 * q;
+        if (bias) {
+          if (p < heads)
+            store4(bo + (((size_t)b * heads + p) * np + r) * np + c, acc[0], acc[1], acc[2],
+                   acc[3]);
+        } else {
+          store4(vto + ((rowbase + h) * ATT_D + dd) * np + c, acc[0], acc[1], acc[2], acc[3]);
+        }
+      }
+    };
+#pragma unroll 1
+    for (int u = 0; u < hd / 16; ++u) unit_a(16 * u, 0, qo);
+#pragma unroll 1
+    for (int u = 0; u < hd / 16; ++u) unit_a(hd + 16 * u, 1, ko);
+#pragma unroll 1
+    for (int u = 0; u < hd / 16; ++u) unit_a(2 * hd + 16 * u, 2, go);
+#pragma unroll 1
+    for (int u = 0; u < hd / 16; ++u) unit_b(3 * hd + 16 * u, false);
+    unit_b(4 * hd, true);
+    // mask in stored coordinates (0 on padding): lanes q = 0 write their pair's value
+    if (q == 0) {
+#pragma unroll
+      for (int st = 0; st < 2; ++st)
+        mso[((size_t)b * np + r) * np + c0 + 16 * st + p] = (bf16)mv[st];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// ka_core. One workgroup per stored row r; its four waves take the heads (wave w: heads
+// w, w + 4). Per tile of 64 query columns and head, a wave runs the keys in steps of 32:
+//   S^T = K Q^T (key rows, query columns) with the pair bias as the accumulator start:
+//     lane (p, q) holds keys 16 kb + 4q + rr of query 16 qb + p;
+//   online softmax per query in base 2 (log2(e) / sqrt(d) is folded into W_q and
+//     log2(e) into the bias rows), masked keys left out; the four lanes p, p^16, p^32,
+//     p^48 hold all keys of a query, so the running maximum is reduced across them and
+//     the sum is kept per lane until the end;
+//   O^T += V^T P^T: the lane's eight probabilities of a query (keys 4q..4q+3 and
+//     16+4q..16+4q+3 of the step) ARE its B-operand chunk once V^T's A chunk holds the
+//     same keys in the same order, read as two 8-byte runs of the transposed v.
+// Then o = O^T / l * gate goes to LDS as [query][h*d + channel]; after a barrier the
+// waves split the output channels: out^T = W_o o^T + b_o with W_o rows from LDS as A.
+template <int KZ>
+__global__ __launch_bounds__(KC_THREADS) void ka_core(
+    const bf16* __restrict__ qi, const bf16* __restrict__ ki, const bf16* __restrict__ gi,
+    const bf16* __restrict__ vti, const float* __restrict__ bi, const bf16* __restrict__ msi,
+    const chunk_t* __restrict__ image, int image_chunks, bf16* __restrict__ out, int n, int np,
+    int heads, int ending) {
+  constexpr int CZ = KZ * 32;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int hd = heads * ATT_D, os_stride = hd + 8;
+  const bf16* const wo = (const bf16*)smem;                                 // [CZ][hd + 8]
+  const float* const bo = (const float*)(smem + (size_t)CZ * os_stride * 2);  // [CZ]
+  bf16* const os = (bf16*)(smem + (size_t)CZ * os_stride * 2 + CZ * 4);       // [64][hd + 8]
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int p = lane & 15, q = lane >> 4;
+  const int b = blockIdx.x / n, r = blockIdx.x - b * n;
+  copy_image<KC_THREADS>(image, (chunk_t*)smem, image_chunks, tid, []() {});
+  __syncthreads();
+
+  const int ksteps = (n + KC_KT - 1) / KC_KT;  // key steps past n would be all masked
+  const bf16* const msrow = msi + ((size_t)b * np + r) * np;
+  const float NEG = -__builtin_huge_valf();
+
+  for (int qt = 0; qt < np / KC_QT; ++qt) {
+    const int qc0 = qt * KC_QT;
+    for (int h = wave; h < heads; h += KC_WAVES) {
+      const size_t rh = ((size_t)b * np + r) * heads + h;
+      const bf16* const qrow = qi + rh * np * ATT_D;
+      const bf16* const krow = ki + rh * np * ATT_D;
+      const bf16* const vrow = vti + rh * ATT_D * np;
+      const float* const brow = bi + ((size_t)b * heads + h) * np * np;
+      chunk_t qf[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) qf[qb] = ld16(qrow + (size_t)(qc0 + 16 * qb + p) * ATT_D + 8 * q);
+      f32x4 o[2][4];
+      float mrun[4], lsum[4];
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        mrun[qb] = NEG;
+        lsum[qb] = 0.f;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll 1
+      for (int ks = 0; ks < ksteps; ++ks) {
+        const int k0 = ks * KC_KT;
+        chunk_t kf[2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) kf[kb] = ld16(krow + (size_t)(k0 + 16 * kb + p) * ATT_D + 8 * q);
+        bool valid[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const u32x2 mk = *(const u32x2*)(msrow + k0 + 16 * kb + 4 * q);
+          valid[kb][0] = (mk[0] & 0x7fffu) != 0;  // nonzero bf16 (either sign of zero is 0)
+          valid[kb][1] = (mk[0] & 0x7fff0000u) != 0;
+          valid[kb][2] = (mk[1] & 0x7fffu) != 0;
+          valid[kb][3] = (mk[1] & 0x7fff0000u) != 0;
+        }
+        f32x4 s[2][4];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb)
+            s[kb][qb] = ld16f(brow + (size_t)(qc0 + 16 * qb + p) * np + k0 + 16 * kb + 4 * q);
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) s[kb][qb] = mma16(s[kb][qb], kf[kb], qf[qb], bf16());
+        // V^T chunks of the step: rows d = 16 db + p, keys 4q..4q+3 and 16+4q..16+4q+3
+        chunk_t vf[2];
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const bf16* const vp = vrow + (size_t)(16 * db + p) * np + k0 + 4 * q;
+          const u32x2 lo = *(const u32x2*)vp, hi = *(const u32x2*)(vp + 16);
+          vf[db] = chunk_t{lo[0], lo[1], hi[0], hi[1]};
+        }
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) {
+          float tmax = NEG;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, valid[kb][e] ? s[kb][qb][e] : NEG);
+          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 16));
+          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 32));
+          const float mnew = fmaxf(mrun[qb], tmax);
+          const bool any = mnew != NEG;  // same in the four lanes of the query
+          const float scale = any ? exp2f(mrun[qb] - mnew) : 1.f;
+          mrun[qb] = mnew;
+          float pv[8];
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              pv[4 * kb + e] = (any && valid[kb][e]) ? exp2f(s[kb][qb][e] - mnew) : 0.f;
+          float ps = 0.f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) ps += pv[e];
+          lsum[qb] = lsum[qb] * scale + ps;
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[db][qb][e] *= scale;
+          const chunk_t pb = pack(pv, bf16());
+#pragma unroll
+          for (int db = 0; db < 2; ++db) o[db][qb] = mma16(o[db][qb], vf[db], pb, bf16());
+        }
+      }
+      // normalise, gate, stage: o^T lane (p, q) reg e = channel 16 db + 4q + e of query
+      // 16 qb + p
+      const bf16* const grow = gi + rh * np * ATT_D;
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        float l = lsum[qb];
+        l += lane_value(l, lane ^ 16);
+        l += lane_value(l, lane ^ 32);
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const int qc = qc0 + 16 * qb + p;
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          float gv[4] = {0.f, 0.f, 0.f, 0.f};
+          add4(gv, grow + (size_t)qc * ATT_D + 16 * db + 4 * q);
+          store4(os + (16 * qb + p) * os_stride + h * ATT_D + 16 * db + 4 * q,
+                 o[db][qb][0] * inv * gv[0], o[db][qb][1] * inv * gv[1],
+                 o[db][qb][2] * inv * gv[2], o[db][qb][3] * inv * gv[3]);
+        }
+      }
+    }
+    __syncthreads();
+    // out^T = W_o o^T + b_o: lane (p, q) reg e = channel 16u + 4q + e of query 16 qb + p
+    for (int u = wave; u < CZ / 16; u += KC_WAVES) {
+      const f32x4 b0 = ld16f(bo + 16 * u + 4 * q);
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) {
+        f32x4 acc = b0;
+        for (int kk = 0; kk < hd / 32; ++kk)
+          acc = mma16(acc, ld16(wo + (16 * u + p) * os_stride + 32 * kk + 8 * q),
+                      ld16(os + (16 * qb + p) * os_stride + 32 * kk + 8 * q), bf16());
+        const int qc = qc0 + 16 * qb + p;
+        if (qc < n) {
+          const size_t x = ending ? (size_t)qc : (size_t)r, y = ending ? (size_t)r : (size_t)qc;
+          store4(out + (((size_t)b * n + x) * n + y) * CZ + 16 * u + 4 * q, acc[0], acc[1],
+                 acc[2], acc[3]);
+        }
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+
+template <int KZ>
+static hipError_t launch_attention_kz(const AttnArgs& a, hipStream_t st) {
+  const int np = att_np(a.n);
+  const AttnWorkspace L = att_workspace(a.batch, a.n, a.heads);
+  unsigned char* ws = (unsigned char*)a.ws;
+  bf16* q = (bf16*)(ws + L.q);
+  bf16* k = (bf16*)(ws + L.k);
+  bf16* g = (bf16*)(ws + L.g);
+  bf16* vt = (bf16*)(ws + L.vt);
+  float* bias = (float*)(ws + L.bias);
+  bf16* ms = (bf16*)(ws + L.ms);
+
+  // projection: persistent waves over 32-pair tiles of the padded stored grid
+  {
+    const size_t lds = att_proj_image_bytes(a.cz, a.heads);
+    if (lds % 16) return hipErrorInvalidValue;
+    auto fn = ka_project<KZ>;
+    static std::atomic<int> granted{0};
+    hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
+    if (e != hipSuccess) return e;
+    static std::atomic<int> occ{0};
+    static std::atomic<size_t> occ_lds{0};
+    const int per_cu = resident_blocks((const void*)fn, KA_THREADS, lds, occ, occ_lds);
+    const long long tiles = (long long)a.batch * np * (np / KA_TW);
+    if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
+    const long long need = (tiles + KA_WAVES - 1) / KA_WAVES;
+    const long long cap = (long long)a.num_cus * per_cu;
+    const int blocks = (int)(need < cap ? need : cap);
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(KA_THREADS), lds, st, (const bf16*)a.z,
+                       (const bf16*)a.mask, (const chunk_t*)a.proj_image, (int)(lds / 16), q, k,
+                       g, vt, bias, ms, a.batch, a.n, np, a.heads, a.node, a.mask_all);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // attention: one workgroup per stored row
+  {
+    const size_t img = att_out_image_bytes(a.cz, a.heads);
+    const size_t lds = att_core_lds_bytes(a.cz, a.heads);
+    if (img % 16) return hipErrorInvalidValue;
+    auto fn = ka_core<KZ>;
+    static std::atomic<int> granted{0};
+    hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
+    if (e != hipSuccess) return e;
+    const long long rows = (long long)a.batch * a.n;
+    if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned int)rows), dim3(KC_THREADS), lds, st, q, k, g, vt,
+                       bias, ms, (const chunk_t*)a.out_image, (int)(img / 16), (bf16*)a.out,
+                       a.n, np, a.heads, a.node);
+    return hipGetLastError();
+  }
+}
+
+hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+  switch (a.cz / 32) {
+    case 1: return launch_attention_kz<1>(a, st);
+    case 2: return launch_attention_kz<2>(a, st);
+    case 3: return launch_attention_kz<3>(a, st);
+    case 4: return launch_attention_kz<4>(a, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace trimul

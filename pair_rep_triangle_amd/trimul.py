@@ -15,6 +15,9 @@ import numpy as np
 from .inputs import WEIGHT_FIELDS
 
 TRANSITION_FIELDS = ("ln_gamma", "ln_beta", "w1", "b1", "w2", "b2")
+ATTENTION_FIELDS = ("ln_gamma", "ln_beta", "w_q", "w_k", "w_v", "w_b", "w_g", "b_g", "w_o",
+                    "b_o")
+NODES = {"starting": 0, "ending": 1}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libtrimul.so")
@@ -31,6 +34,8 @@ EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layou
            "tri_mul_destroy", "tri_mul_strerror", "tri_mul_last_hip_error")
 TRANSITION_EXPORTS = ("pair_transition_create", "pair_transition_forward",
                       "pair_transition_destroy")
+ATTENTION_EXPORTS = ("tri_attn_create", "tri_attn_workspace_bytes", "tri_attn_forward",
+                     "tri_attn_destroy")
 
 
 class TriMulError(RuntimeError):
@@ -46,6 +51,10 @@ class Weights(ctypes.Structure):
 
 class TransitionWeights(ctypes.Structure):
     _fields_ = [(name, ctypes.POINTER(ctypes.c_float)) for name in TRANSITION_FIELDS]
+
+
+class AttentionWeights(ctypes.Structure):
+    _fields_ = [(name, ctypes.POINTER(ctypes.c_float)) for name in ATTENTION_FIELDS]
 
 
 class Layout(ctypes.Structure):
@@ -83,6 +92,12 @@ def load_library(path=LIB_PATH):
                                            ctypes.POINTER(vp)]
     lib.pair_transition_forward.argtypes = [vp, vp, vp, vp, i, i, vp]
     lib.pair_transition_destroy.argtypes = [vp]
+    lib.tri_attn_create.argtypes = [ctypes.POINTER(AttentionWeights), i, i, i, i,
+                                    ctypes.POINTER(vp)]
+    lib.tri_attn_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
+    lib.tri_attn_forward.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+    lib.tri_attn_destroy.argtypes = [vp]
+    lib.tri_attn_destroy.restype = None
     lib.pair_transition_destroy.restype = None
     for name in ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
                  "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage",
@@ -278,6 +293,84 @@ class PairTransition:
     def close(self):
         if getattr(self, "_h", None):
             self.lib.pair_transition_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+class TriAttention:
+    """Triangular attention around the starting or ending node (one weight set; bf16).
+
+    weights: mapping with the tri_attn_weights field names, fp32 host arrays in nn.Linear
+    orientation, heads stacked along the output rows (missing gamma -> ones, missing
+    beta / b_g / b_o -> zeros).
+    """
+
+    def __init__(self, weights, c_z, heads, head_dim=32, dtype="bf16"):
+        self.lib = load_library()
+        self.c_z, self.heads, self.head_dim, self.dtype = int(c_z), int(heads), int(head_dim), dtype
+        if dtype not in DTYPES:
+            raise ValueError(f"dtype must be one of {sorted(DTYPES)}")
+        keep = {}
+        ws = AttentionWeights()
+        for name in ATTENTION_FIELDS:
+            v = weights.get(name) if hasattr(weights, "get") else None
+            if v is None:
+                continue
+            keep[name] = _host_f32(v)
+            setattr(ws, name, keep[name].ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        h = ctypes.c_void_p()
+        _check(self.lib.tri_attn_create(ctypes.byref(ws), self.c_z, self.heads, self.head_dim,
+                                        DTYPES[dtype], ctypes.byref(h)), "tri_attn_create")
+        self._h = h
+
+    def workspace_bytes(self, batch, n):
+        out = ctypes.c_size_t()
+        _check(self.lib.tri_attn_workspace_bytes(self._h, int(batch), int(n), ctypes.byref(out)),
+               "tri_attn_workspace_bytes")
+        return out.value
+
+    def new_workspace(self, batch, n, device="cuda"):
+        import torch
+        return torch.empty(self.workspace_bytes(batch, n), dtype=torch.uint8, device=device)
+
+    def forward(self, z, mask=None, out=None, node="starting", workspace=None, stream=None):
+        """out = triangular attention of z around `node` ("starting" or "ending")."""
+        import torch
+        if node not in NODES:
+            raise ValueError(f"node must be one of {sorted(NODES)}")
+        if z.dim() != 4 or z.shape[1] != z.shape[2] or z.shape[3] != self.c_z:
+            raise ValueError(f"z must be [B, N, N, {self.c_z}], got {tuple(z.shape)}")
+        if z.dtype != torch.bfloat16 or not z.is_cuda or not z.is_contiguous():
+            raise ValueError("z must be a contiguous bfloat16 CUDA tensor")
+        batch, n = int(z.shape[0]), int(z.shape[1])
+        if mask is not None and (tuple(mask.shape) != (batch, n, n) or mask.dtype != z.dtype
+                                 or not mask.is_contiguous()):
+            raise ValueError("mask must be a contiguous [B, N, N] tensor of z's dtype")
+        if out is None:
+            out = torch.empty_like(z)
+        elif out.shape != z.shape or out.dtype != z.dtype or not out.is_contiguous():
+            raise ValueError("out must be a contiguous tensor shaped like z")
+        if workspace is None:
+            workspace = self.new_workspace(batch, n, z.device)
+        if stream is None:
+            stream = torch.cuda.current_stream(z.device).cuda_stream
+        _check(self.lib.tri_attn_forward(self._h, z.data_ptr(),
+                                         None if mask is None else mask.data_ptr(),
+                                         out.data_ptr(), batch, n, NODES[node],
+                                         workspace.data_ptr(), workspace.numel(), stream),
+               "tri_attn_forward")
+        return out
+
+    __call__ = forward
+
+    def close(self):
+        if getattr(self, "_h", None):
+            self.lib.tri_attn_destroy(self._h)
             self._h = None
 
     def __del__(self):

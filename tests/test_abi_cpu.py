@@ -1,6 +1,6 @@
 """C-ABI contract checks that need no GPU: the library loads, exports every
-symbol include/tri_mul.h and include/pair_transition.h declare, and rejects bad
-create arguments before any HIP call."""
+symbol include/tri_mul.h, include/pair_transition.h and include/tri_attention.h
+declare, and rejects bad create arguments before any HIP call."""
 
 import ctypes
 import os
@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 
 from pair_rep_triangle_amd import trimul as tm
-from pair_rep_triangle_amd.inputs import make_transition_weights, make_weights
+from pair_rep_triangle_amd.inputs import (make_attention_weights, make_transition_weights,
+                                          make_weights)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -35,8 +36,13 @@ def test_transition_header_declares_the_entry_points():
     assert _declared_functions("pair_transition.h", "pair_transition_") == sorted(tm.TRANSITION_EXPORTS)
 
 
+def test_attention_header_declares_the_entry_points():
+    assert _declared_functions("tri_attention.h", "tri_attn_") == sorted(tm.ATTENTION_EXPORTS)
+
+
 def test_library_exports_every_declared_symbol(lib):
-    for name in _declared_functions() + _declared_functions("pair_transition.h", "pair_transition_"):
+    for name in (_declared_functions() + _declared_functions("pair_transition.h", "pair_transition_")
+                 + _declared_functions("tri_attention.h", "tri_attn_")):
         assert hasattr(lib, name), name
 
 
@@ -124,3 +130,39 @@ def test_transition_null_arguments(lib):
     assert lib.pair_transition_create(ctypes.byref(s), 64, 128, tm.TRI_MUL_BF16, ctypes.byref(h)) == -1
     assert lib.pair_transition_forward(None, 16, None, 32, 1, 8, None) == -1
     lib.pair_transition_destroy(None)  # no-op
+
+
+def _attention_struct(w):
+    keep = {k: np.ascontiguousarray(v, dtype=np.float32) for k, v in w.items()}
+    s = tm.AttentionWeights()
+    for k, v in keep.items():
+        setattr(s, k, v.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+    return s, keep
+
+
+@pytest.mark.parametrize("c_z,heads,d,dtype,code", [
+    (48, 4, 32, tm.TRI_MUL_BF16, -2), (160, 4, 32, tm.TRI_MUL_BF16, -2),
+    (128, 8, 32, tm.TRI_MUL_BF16, -2), (64, 9, 32, tm.TRI_MUL_BF16, -2),
+    (128, 4, 16, tm.TRI_MUL_BF16, -2), (128, 4, 32, tm.TRI_MUL_FP32, -2),
+    (0, 4, 32, tm.TRI_MUL_BF16, -1), (64, 0, 32, tm.TRI_MUL_BF16, -1),
+])
+def test_attention_create_rejects_bad_shapes(lib, c_z, heads, d, dtype, code):
+    w = make_attention_weights(np.random.default_rng(0), max(c_z, 1), max(heads, 1), max(d, 1))
+    s, keep = _attention_struct(w)
+    h = ctypes.c_void_p(1)
+    assert lib.tri_attn_create(ctypes.byref(s), c_z, heads, d, dtype, ctypes.byref(h)) == code
+    assert h.value is None
+
+
+def test_attention_null_arguments(lib):
+    w = make_attention_weights(np.random.default_rng(0), 64, 2, 32)
+    s, keep = _attention_struct(w)
+    h = ctypes.c_void_p()
+    assert lib.tri_attn_create(None, 64, 2, 32, tm.TRI_MUL_BF16, ctypes.byref(h)) == -1
+    assert lib.tri_attn_create(ctypes.byref(s), 64, 2, 32, tm.TRI_MUL_BF16, None) == -1
+    s.w_o = None
+    assert lib.tri_attn_create(ctypes.byref(s), 64, 2, 32, tm.TRI_MUL_BF16, ctypes.byref(h)) == -1
+    n = ctypes.c_size_t()
+    assert lib.tri_attn_workspace_bytes(None, 1, 8, ctypes.byref(n)) == -1
+    assert lib.tri_attn_forward(None, 16, None, 32, 1, 8, 0, 48, 1 << 20, None) == -1
+    lib.tri_attn_destroy(None)  # no-op

@@ -361,3 +361,15 @@ def test_attention_planted_mistake_is_caught(mutant, monkeypatch):
     name, fn = MUTANTS[mutant]
     monkeypatch.setattr(aref, name, fn)
     assert not _pins_pass(), f"planted mistake {mutant!r} slipped through the pins"
+
+
+@pytest.mark.parametrize("node", aref.NODES)
+def test_line_restricted_oracle_equals_the_full_evaluation(node):
+    """tri_attention_ref_lines (used for sampled parity at large N) returns exactly the
+    chosen rows (starting) or columns (ending) of the full output."""
+    z, m, w = _case(B=2, N=9, c_z=8, heads=2, d=4, seed=14, mask="rowpad")
+    lines = [0, 2, 5, 8]
+    full = aref.tri_attention_ref(z, m, w, node)
+    sub = aref.tri_attention_ref_lines(z, m, w, node, lines)
+    want = full[:, lines] if node == "starting" else np.swapaxes(full[:, :, lines], 1, 2)
+    assert np.array_equal(sub, want)

@@ -1,0 +1,118 @@
+"""GPU parity of triangular attention (tri_attn_forward) against the fp64 oracle, both
+nodes. Tolerance: max |gpu - ref| / max |ref| <= 2e-2 (bf16 storage of z, out and the
+projections; fp32 accumulation and softmax)."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tri_attention_ref, tri_attention_ref_lines
+from pair_rep_triangle_amd.inputs import make_attention_weights, make_random, make_workload
+from pair_rep_triangle_amd.trimul import TriAttention, TriMulError
+from tests.gpu_util import TOL, note, rel_err, to_device
+
+pytestmark = pytest.mark.gpu
+
+NODES = ("starting", "ending")
+
+
+def _run(B, n, c_z, heads, mask, seed, node, use_mask=True):
+    d = make_random(B, n, c_z, 16, seed=seed, mask=mask)
+    w = make_attention_weights(np.random.default_rng(seed + 100), c_z, heads, 32,
+                               random_affine=True)
+    z, m, z_host, m_host = to_device(d, "bf16")
+    if not use_mask:
+        m, m_host = None, None
+    mod = TriAttention(w, c_z, heads)
+    out = mod.forward(z, m, node=node)
+    torch.cuda.synchronize()
+    return out, z, m, z_host, m_host, w, mod
+
+
+@pytest.mark.parametrize("node", NODES)
+@pytest.mark.parametrize("B,n,c_z,heads,mask", [
+    (1, 40, 64, 2, "random_pairs"),
+    (2, 33, 128, 4, "block"),            # ragged n, two items, the widest supported
+    (1, 70, 32, 1, "random_residues"),   # fully padded residues: queries with no valid key
+    (1, 64, 96, 3, "ones"),              # three heads (a wave of the workgroup idles)
+    (1, 129, 64, 8, "random_pairs"),     # eight heads: each wave runs two
+])
+def test_attention_full_output(node, B, n, c_z, heads, mask):
+    note(f"attention {node} B={B} n={n} cz={c_z} heads={heads} {mask}")
+    out, z, m, z_host, m_host, w, _ = _run(B, n, c_z, heads, mask, seed=n + c_z, node=node)
+    got = out.to(torch.float64).cpu().numpy()
+    want = tri_attention_ref(z_host, m_host, w, node)
+    assert np.isfinite(got).all()
+    assert rel_err(got, want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("node", NODES)
+def test_attention_null_mask_means_all_ones(node):
+    note(f"attention null mask {node}")
+    out, z, _, z_host, _, w, mod = _run(1, 45, 64, 2, "ones", seed=5, node=node, use_mask=False)
+    ones = torch.ones(z.shape[:3], dtype=z.dtype, device=z.device)
+    assert torch.equal(mod.forward(z, ones, node=node), out)
+    want = tri_attention_ref(z_host, None, w, node)
+    assert rel_err(out.to(torch.float64).cpu().numpy(), want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("node", NODES)
+def test_attention_repeatable(node):
+    """Two runs give the same bytes (no race between waves or workgroups)."""
+    note(f"attention repeat {node}")
+    out, z, m, _, _, _, mod = _run(1, 96, 128, 4, "random_pairs", seed=6, node=node)
+    again = mod.forward(z, m, node=node)
+    torch.cuda.synchronize()
+    assert torch.equal(out, again)
+
+
+def test_attention_writes_nothing_past_the_output():
+    note("attention guard band")
+    d = make_random(1, 37, 64, 16, seed=7, mask="block")
+    w = make_attention_weights(np.random.default_rng(7), 64, 2, 32, random_affine=True)
+    z, m, z_host, m_host = to_device(d, "bf16")
+    mod = TriAttention(w, 64, 2)
+    count = z.numel()
+    big = torch.full((count + 4096,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = big[:count].view_as(z)
+    for node in NODES:
+        mod.forward(z, m, out=out, node=node)
+        torch.cuda.synchronize()
+        assert torch.all(big[count:] == 7.0)
+        assert rel_err(out.to(torch.float64).cpu().numpy(),
+                       tri_attention_ref(z_host, m_host, w, node)) <= TOL["bf16"]
+
+
+def test_attention_rejects_small_workspace_and_overlap():
+    d = make_random(1, 24, 64, 16, seed=8)
+    w = make_attention_weights(np.random.default_rng(8), 64, 2, 32)
+    z, m, _, _ = to_device(d, "bf16")
+    mod = TriAttention(w, 64, 2)
+    small = torch.empty(mod.workspace_bytes(1, 24) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(TriMulError) as ei:
+        mod.forward(z, m, workspace=small)
+    assert ei.value.name == "WORKSPACE_TOO_SMALL"
+    with pytest.raises(TriMulError) as ei:
+        mod.forward(z, m, out=z)
+    assert ei.value.name == "ALIAS"
+
+
+@pytest.mark.parametrize("node", NODES)
+def test_attention_headline_shape_sampled(node):
+    """N = 512, c_z = 128, 4 heads of 32, bf16, the block mask of the headline workload
+    (valid length 493): full device output, oracle on sampled query lines (the first and
+    last lines, lines around the valid length, padded lines, random ones)."""
+    note(f"attention headline {node}")
+    d = make_workload("n512_cz128_c128_bf16_masked", seed=0)
+    w = make_attention_weights(np.random.default_rng(2), 128, 4, 32, random_affine=True)
+    z, m, z_host, m_host = to_device(d, "bf16")
+    mod = TriAttention(w, 128, 4)
+    out = mod.forward(z, m, node=node)
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy()
+    assert np.isfinite(got).all()
+    L = d["meta"]["valid_length"]
+    lines = sorted({0, 1, L - 2, L - 1, L, 511} | set(np.random.default_rng(9).integers(0, 512, 4).tolist()))
+    want = tri_attention_ref_lines(z_host, m_host, w, node, lines)
+    sel = got[:, lines] if node == "starting" else np.swapaxes(got[:, :, lines], 1, 2)
+    assert rel_err(sel, want) <= TOL["bf16"]
