@@ -17,6 +17,9 @@ The timed steps launch their six kernels one by one; --launch graph captures the
 step once in a HIP graph and times replays of it instead (the eager step time is
 reported in both cases). The per-kernel region always launches eagerly.
 
+With --op attention the step is triangular attention around the starting node, then
+around the ending node (each with its own weights, 4 heads of width 32) on the same
+workload's z and mask; per-kernel events time its two kernels (projection, attention).
 With --op transition the step is the pair transition instead (one kernel: LayerNorm,
 c_z -> 2 c_z -> c_z with ReLU, masked residual) on the same workload's z and mask; its
 line reports pair-updates/s with the same roofline and cpu_baseline objects.
@@ -36,6 +39,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "triangle-mult-update TFLOP/s & pair-updates/s at N=512,c_z=128 bf16 (1 GPU)"
 TRANSITION_METRIC = "pair-transition pair-updates/s (expansion 2, masked residual, 1 GPU)"
+ATTENTION_METRIC = "triangular-attention pair-updates/s (starting+ending node, 4 heads of 32, 1 GPU)"
 KERNELS = ("k1_input_gate", "k2_contract", "k3_output_gate")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
 # A bounded spin on the GPU queued ahead of each per-kernel event region, so the host has
@@ -56,8 +60,9 @@ def parse():
     p.add_argument("--launch", choices=("eager", "graph"), default="eager",
                    help="timed steps launch their kernels one by one (default) or replay one "
                         "captured HIP graph of the step")
-    p.add_argument("--op", choices=("trimul", "transition"), default="trimul",
-                   help="time the triangle multiplicative update (default) or the pair transition")
+    p.add_argument("--op", choices=("trimul", "transition", "attention"), default="trimul",
+                   help="time the triangle multiplicative update (default), the pair transition "
+                        "or triangular attention")
     p.add_argument("--seed", type=int, default=0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
@@ -250,6 +255,127 @@ def bench_transition(args):
     print(json.dumps(rec), flush=True)
 
 
+def bench_attention(args):
+    """Triangular attention around both nodes (4 heads of 32) on the workload's z and mask."""
+    import numpy as np
+    import torch
+    from pair_rep_triangle_amd.inputs import HEADLINE, WORKLOADS, make_attention_weights, make_workload
+    from pair_rep_triangle_amd.metrics import MI355X_EXP_PER_S, MI355X_PEAK, attention_work
+    from pair_rep_triangle_amd.trimul import TriAttention
+
+    name = args.workload or HEADLINE
+    spec = WORKLOADS[name]
+    d = make_workload(name, seed=args.seed)
+    B, n, c_z, dtype = spec["batch"], spec["n"], spec["c_z"], spec["dtype"]
+    heads, hdim = 4, 32
+    if dtype != "bf16":
+        print("bench.py: triangular attention runs in bf16 only", file=sys.stderr)
+        sys.exit(2)
+    ws_nodes = {node: make_attention_weights(np.random.default_rng(args.seed + 3 + i), c_z, heads,
+                                             hdim, random_affine=True)
+                for i, node in enumerate(("starting", "ending"))}
+    dev = torch.device("cuda:0")
+    z = torch.from_numpy(d["z"]).to(torch.bfloat16).to(dev)
+    mask = torch.from_numpy(d["mask"]).to(torch.bfloat16).to(dev)
+    mods = {node: TriAttention(w, c_z, heads, hdim) for node, w in ws_nodes.items()}
+    ws = mods["starting"].new_workspace(B, n, dev)
+    outs = {node: torch.empty_like(z) for node in mods}
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        for node, mod in mods.items():
+            mod.forward(z, mask, out=outs[node], node=node, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    copy_calibration(args.copy_calibration_mb, dev)
+    ms_eager, wall = timed_steps(step, args.steps, stream)
+    ms_step, launch = ms_eager, "eager"
+    if args.launch == "graph":
+        graph = graph_of(step, dev)
+        ms_step, wall = timed_steps(graph.replay, args.steps, stream)
+        launch = "hipgraph"
+
+    pairs = B * n * n
+    work = attention_work(n, c_z, heads, hdim, 2)
+    kernels, roofline = {}, None
+    if not args.no_kernel_events:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+        torch.cuda._sleep(HOST_AHEAD_CYCLES)
+        for k in range(args.steps):
+            evs[k][0].record(stream)
+            e = 1
+            for node, mod in mods.items():
+                for st in (1, 2):
+                    mod.stage(st, z, mask, out=outs[node], node=node, workspace=ws)
+                    evs[k][e].record(stream)
+                    e += 1
+        torch.cuda.synchronize()
+        per = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(4)]
+                        for k in range(args.steps)])
+        for idx, kname in enumerate(("ka_project", "ka_core")):
+            samples = np.concatenate([per[:, idx], per[:, idx + 2]])  # both nodes
+            avg_ms = float(samples.mean())
+            wk = work[kname]
+            gbps = wk["bytes"] * pairs / (avg_ms * 1e-3) / 1e9
+            tfl = wk["flops"] * pairs / (avg_ms * 1e-3) / 1e12
+            kd = {"avg_us": round(avg_ms * 1e3, 3), "median_us": round(float(np.median(samples)) * 1e3, 3),
+                  "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1),
+                  "hbm_frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4),
+                  "mfma_frac": round(tfl / MI355X_PEAK["bf16_TFLOPs"], 4),
+                  "bytes_per_launch": wk["bytes"] * pairs, "flops_per_launch": wk["flops"] * pairs}
+            if "exps" in wk:
+                ges = wk["exps"] * pairs / (avg_ms * 1e-3) / 1e9
+                kd["Gexp_per_s"] = round(ges, 1)
+                kd["exp_frac"] = round(ges * 1e9 / MI355X_EXP_PER_S, 4)
+            kernels[kname] = kd
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+        kd = kernels[dom]
+        traffic = measured_traffic(name, dom)
+        if dom == "ka_core":
+            roofline = {"kernel": dom, "bound": "alu", "achieved": kd["Gexp_per_s"],
+                        "peak": round(MI355X_EXP_PER_S / 1e9, 1), "unit": "Gexp/s",
+                        "frac": kd["exp_frac"], "traffic": traffic}
+        else:
+            roofline = {"kernel": dom, "bound": "hbm", "achieved": kd["GBps"],
+                        "peak": MI355X_PEAK["hbm_GBps"], "unit": "GB/s",
+                        "frac": kd["hbm_frac"], "traffic": traffic}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        from threadpoolctl import threadpool_limits
+        from oracle import tri_attention_ref
+        threads = min(16, len(os.sched_getaffinity(0)))
+        zh = torch.from_numpy(d["z"]).to(torch.bfloat16).to(torch.float64).numpy()
+        with threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            tri_attention_ref(zh, d["mask"], ws_nodes["starting"], "starting")
+            dt = time.perf_counter() - t0
+        cpu = {"value": round(pairs / dt, 1), "unit": "pair-updates/s", "cores": threads,
+               "kind": "oracle", "seconds_per_pass": round(dt, 2),
+               "sample": f"the starting node over the whole workload {name}, fp64 NumPy "
+                         f"oracle (BLAS on {threads} threads), one pass"}
+
+    flops_pair = work["ka_project"]["flops"] + work["ka_core"]["flops"]
+    rec = {
+        "metric": ATTENTION_METRIC, "value": round(2 * pairs / (ms_step * 1e-3), 1),
+        "unit": "pair-updates/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4), "ms_per_step_eager": round(ms_eager, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": f"triangular_attention_{name}", "batch": B, "n": n, "c_z": c_z,
+                   "heads": heads, "head_dim": hdim, "nodes": "starting+ending",
+                   "mask": spec["mask"], "launch": launch},
+        "tflops": round(2 * flops_pair * pairs / (ms_step * 1e-3) / 1e12, 2),
+        "wall_s": round(wall, 3),
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -258,6 +384,9 @@ def main():
         sys.exit(2)
     if args.op == "transition":
         bench_transition(args)
+        return
+    if args.op == "attention":
+        bench_attention(args)
         return
 
     import numpy as np

@@ -64,7 +64,7 @@ int tri_attn_create(const tri_attn_weights* w, int c_z, int heads, int head_dim,
                     tri_attn_handle** out);
 
 /* Bytes of the caller-owned workspace a forward call over batch x n x n needs: the
- * per-head q, k, gate and transposed v, the fp32 pair bias and the mask, each over the
+ * per-head q, k, gate and transposed v, the pair bias and the mask, each over the
  * pair grid padded to a multiple of 64 per side. */
 int tri_attn_workspace_bytes(const tri_attn_handle* h, int batch, int n, size_t* bytes);
 
@@ -78,6 +78,15 @@ int tri_attn_workspace_bytes(const tri_attn_handle* h, int batch, int n, size_t*
 int tri_attn_forward(tri_attn_handle* h, const void* z, const void* pair_mask, void* out,
                      int batch, int n, int node, void* workspace, size_t ws_bytes,
                      void* stream);
+
+/* One of the two kernels of tri_attn_forward alone, with the same arguments: stage 1 =
+ * the projection (LayerNorm, q, k, gate, v, pair bias and mask into the workspace),
+ * stage 2 = the attention and output projection (reads the workspace stage 1 wrote for
+ * the same z, mask and node). For tests and per-kernel timing. Errors as
+ * tri_attn_forward, INVALID_ARG for another stage. */
+int tri_attn_forward_stage(tri_attn_handle* h, int stage, const void* z, const void* pair_mask,
+                           void* out, int batch, int n, int node, void* workspace,
+                           size_t ws_bytes, void* stream);
 
 /* Release the handle's device weights (NULL is ignored). */
 void tri_attn_destroy(tri_attn_handle* h);

@@ -28,6 +28,12 @@ COMMON = [
 ]
 
 
+# Per-source additions. The attention kernels feed every MFMA result to vector ALU work
+# (softmax, rescaling); the MFMA forms that write vector registers avoid a copy out of the
+# accumulation registers for each use.
+EXTRA = {"ka_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
+
 def _run(cmd):
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
@@ -44,7 +50,7 @@ def build(verbose=True):
     os.makedirs(objdir, exist_ok=True)
     from concurrent.futures import ThreadPoolExecutor
     objs = [os.path.join(objdir, src + ".o") for src in SOURCES]
-    jobs = [[HIPCC, *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
+    jobs = [[HIPCC, *COMMON, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
             for src, obj in zip(SOURCES, objs)]
     with ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1, 8)) as ex:
         list(ex.map(_run, jobs))

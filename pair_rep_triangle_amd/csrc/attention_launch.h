@@ -13,7 +13,7 @@ constexpr int ATT_PAD = 64;    // the stored pair grid is padded to a multiple o
 // node, (j, i) around the ending node, so both nodes attend along stored rows):
 //   q, k, g  [B][Np][H][Np][d]   bf16   (g already through the sigmoid)
 //   vt       [B][Np][H][d][Np]   bf16   (v transposed: keys contiguous)
-//   bias     [B][H][Np][Np]      fp32   (the pair bias of stored pair (r, c), base 2)
+//   bias     [B][H][Np][Np]      bf16   (the pair bias of stored pair (r, c), base 2)
 //   ms       [B][Np][Np]         bf16   (the pair mask in stored coordinates, 0 on padding)
 struct AttnWorkspace {
   size_t q, k, g, vt, bias, ms, total;
@@ -30,7 +30,7 @@ inline AttnWorkspace att_workspace(int batch, int n, int heads) {
   w.g = w.k + qkv;
   w.vt = w.g + qkv;
   w.bias = w.vt + qkv;
-  w.ms = w.bias + att_align(plane * heads * 4);
+  w.ms = w.bias + att_align(plane * heads * 2);
   w.total = w.ms + att_align(plane * 2);
   return w;
 }
@@ -69,6 +69,7 @@ inline bool attention_supported(int cz, int heads, int d) {
          att_core_lds_bytes(cz, heads) <= 160 * 1024;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st);
+// stages: 1 = projection, 2 = attention and output, 3 = both
+hipError_t launch_attention(const AttnArgs& a, int stages, hipStream_t st);
 
 }  // namespace trimul

@@ -11,6 +11,8 @@
 // stored column, and the pair bias of query column qc and key column kc is the bias of
 // stored pair (qc, kc).
 
+#include <type_traits>
+
 #include "attention_launch.h"
 #include "device_common.h"
 
@@ -23,7 +25,7 @@ constexpr int KA_THREADS = 64 * KA_WAVES;
 constexpr int KA_TW = 32;                    // pairs per projection wave tile
 constexpr int KC_WAVES = 4;                  // attention kernel
 constexpr int KC_THREADS = 64 * KC_WAVES;
-constexpr int KC_QT = 64;                    // queries per attention tile
+constexpr int KC_QB = 4;                     // 16-query blocks per attention tile
 constexpr int KC_KT = 32;                    // keys per attention step
 
 // ---------------------------------------------------------------------------------------
@@ -38,7 +40,7 @@ template <int KZ>
 __global__ __launch_bounds__(KA_THREADS) void ka_project(
     const bf16* __restrict__ z, const bf16* __restrict__ mask, const chunk_t* __restrict__ image,
     int image_chunks, bf16* __restrict__ qo, bf16* __restrict__ ko, bf16* __restrict__ go,
-    bf16* __restrict__ vto, float* __restrict__ bo, bf16* __restrict__ mso, int batch, int n,
+    bf16* __restrict__ vto, bf16* __restrict__ bo, bf16* __restrict__ mso, int batch, int n,
     int np, int heads, int ending, int mask_all) {
   constexpr int E = 8, KG = 32, CZ = KZ * KG, RS = CZ + 8;  // LDS row stride (elements)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -192,13 +194,14 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 //     same keys in the same order, read as two 8-byte runs of the transposed v.
 // Then o = O^T / l * gate goes to LDS as [query][h*d + channel]; after a barrier the
 // waves split the output channels: out^T = W_o o^T + b_o with W_o rows from LDS as A.
-template <int KZ>
+template <int KZ, int QB>
 __global__ __launch_bounds__(KC_THREADS) void ka_core(
     const bf16* __restrict__ qi, const bf16* __restrict__ ki, const bf16* __restrict__ gi,
-    const bf16* __restrict__ vti, const float* __restrict__ bi, const bf16* __restrict__ msi,
+    const bf16* __restrict__ vti, const bf16* __restrict__ bi, const bf16* __restrict__ msi,
     const chunk_t* __restrict__ image, int image_chunks, bf16* __restrict__ out, int n, int np,
     int heads, int ending) {
   constexpr int CZ = KZ * 32;
+  constexpr int QT = 16 * QB;  // queries per tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int hd = heads * ATT_D, os_stride = hd + 8;
   const bf16* const wo = (const bf16*)smem;                                 // [CZ][hd + 8]
@@ -208,7 +211,7 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = lane & 15, q = lane >> 4;
-  const int b = blockIdx.x / n, r = blockIdx.x - b * n;
+  const int b = blockIdx.x / n, r = blockIdx.x - b * n;  // blockIdx.y: this row's share
   copy_image<KC_THREADS>(image, (chunk_t*)smem, image_chunks, tid, []() {});
   __syncthreads();
 
@@ -216,96 +219,138 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
   const bf16* const msrow = msi + ((size_t)b * np + r) * np;
   const float NEG = -__builtin_huge_valf();
 
-  for (int qt = 0; qt < np / KC_QT; ++qt) {
-    const int qc0 = qt * KC_QT;
+  for (int qt = blockIdx.y; qt < np / QT; qt += gridDim.y) {
+    const int qc0 = qt * QT;
     for (int h = wave; h < heads; h += KC_WAVES) {
       const size_t rh = ((size_t)b * np + r) * heads + h;
       const bf16* const qrow = qi + rh * np * ATT_D;
       const bf16* const krow = ki + rh * np * ATT_D;
       const bf16* const vrow = vti + rh * ATT_D * np;
-      const float* const brow = bi + ((size_t)b * heads + h) * np * np;
-      chunk_t qf[4];
+      const bf16* const brow = bi + ((size_t)b * heads + h) * np * np;
+      chunk_t qf[QB];
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) qf[qb] = ld16(qrow + (size_t)(qc0 + 16 * qb + p) * ATT_D + 8 * q);
-      f32x4 o[2][4];
-      float mrun[4], lsum[4];
+      for (int qb = 0; qb < QB; ++qb) qf[qb] = ld16(qrow + (size_t)(qc0 + 16 * qb + p) * ATT_D + 8 * q);
+      f32x4 o[2][QB];
+      float mrun[QB], lsum[QB];
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         mrun[qb] = NEG;
         lsum[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < 2; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-#pragma unroll 1
-      for (int ks = 0; ks < ksteps; ++ks) {
-        const int k0 = ks * KC_KT;
-        chunk_t kf[2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) kf[kb] = ld16(krow + (size_t)(k0 + 16 * kb + p) * ATT_D + 8 * q);
-        bool valid[2][4];
+      // One key step's operands: K chunks, the bias tiles (the accumulator start of
+      // S^T), the key mask and V^T chunks. Each is reloaded for the next step right after
+      // its last use in this one (bias and K after the S^T MFMAs, the mask after its
+      // flags, V^T after the O^T MFMAs), so the loads run a step ahead with no copies.
+      chunk_t kf[2], vf[2];
+      u32x2 sb[2][QB];  // four bf16 bias values per tile and lane
+      u32x2 mk[2];
+      auto load_kbm = [&](int ks) {
+        const int k0 = (ks < ksteps ? ks : ksteps - 1) * KC_KT;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const u32x2 mk = *(const u32x2*)(msrow + k0 + 16 * kb + 4 * q);
-          valid[kb][0] = (mk[0] & 0x7fffu) != 0;  // nonzero bf16 (either sign of zero is 0)
-          valid[kb][1] = (mk[0] & 0x7fff0000u) != 0;
-          valid[kb][2] = (mk[1] & 0x7fffu) != 0;
-          valid[kb][3] = (mk[1] & 0x7fff0000u) != 0;
+          kf[kb] = ld16(krow + (size_t)(k0 + 16 * kb + p) * ATT_D + 8 * q);
+          mk[kb] = *(const u32x2*)(msrow + k0 + 16 * kb + 4 * q);
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            sb[kb][qb] = *(const u32x2*)(brow + (size_t)(qc0 + 16 * qb + p) * np + k0 + 16 * kb + 4 * q);
         }
-        f32x4 s[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < 4; ++qb)
-            s[kb][qb] = ld16f(brow + (size_t)(qc0 + 16 * qb + p) * np + k0 + 16 * kb + 4 * q);
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int qb = 0; qb < 4; ++qb) s[kb][qb] = mma16(s[kb][qb], kf[kb], qf[qb], bf16());
-        // V^T chunks of the step: rows d = 16 db + p, keys 4q..4q+3 and 16+4q..16+4q+3
-        chunk_t vf[2];
+      };
+      // V^T rows d = 16 db + p, keys 4q..4q+3 and 16+4q..16+4q+3 of the step
+      auto load_v = [&](int ks) {
+        const int k0 = (ks < ksteps ? ks : ksteps - 1) * KC_KT;
 #pragma unroll
         for (int db = 0; db < 2; ++db) {
           const bf16* const vp = vrow + (size_t)(16 * db + p) * np + k0 + 4 * q;
           const u32x2 lo = *(const u32x2*)vp, hi = *(const u32x2*)(vp + 16);
           vf[db] = chunk_t{lo[0], lo[1], hi[0], hi[1]};
         }
+      };
+      load_kbm(0);
+      load_v(0);
+#pragma unroll 1
+      for (int ks = 0; ks < ksteps; ++ks) {
+        f32x4 s[2][QB];
 #pragma unroll
-        for (int qb = 0; qb < 4; ++qb) {
-          float tmax = NEG;
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
+          for (int qb = 0; qb < QB; ++qb) {
+            const u32x2 bv = sb[kb][qb];
+            const f32x4 b0 = {__uint_as_float(bv[0] << 16), __uint_as_float(bv[0] & 0xffff0000u),
+                              __uint_as_float(bv[1] << 16), __uint_as_float(bv[1] & 0xffff0000u)};
+            s[kb][qb] = mma16(b0, kf[kb], qf[qb], bf16());
+          }
+        bool valid[2][4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tmax = fmaxf(tmax, valid[kb][e] ? s[kb][qb][e] : NEG);
-          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 16));
-          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 32));
-          const float mnew = fmaxf(mrun[qb], tmax);
-          const bool any = mnew != NEG;  // same in the four lanes of the query
-          const float scale = any ? exp2f(mrun[qb] - mnew) : 1.f;
-          mrun[qb] = mnew;
-          float pv[8];
-#pragma unroll
-          for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              pv[4 * kb + e] = (any && valid[kb][e]) ? exp2f(s[kb][qb][e] - mnew) : 0.f;
-          float ps = 0.f;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) ps += pv[e];
-          lsum[qb] = lsum[qb] * scale + ps;
-#pragma unroll
-          for (int db = 0; db < 2; ++db)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[db][qb][e] *= scale;
-          const chunk_t pb = pack(pv, bf16());
-#pragma unroll
-          for (int db = 0; db < 2; ++db) o[db][qb] = mma16(o[db][qb], vf[db], pb, bf16());
+        for (int kb = 0; kb < 2; ++kb) {
+          valid[kb][0] = (mk[kb][0] & 0x7fffu) != 0;  // nonzero bf16 (either sign of 0 is 0)
+          valid[kb][1] = (mk[kb][0] & 0x7fff0000u) != 0;
+          valid[kb][2] = (mk[kb][1] & 0x7fffu) != 0;
+          valid[kb][3] = (mk[kb][1] & 0x7fff0000u) != 0;
         }
+        load_kbm(ks + 1);  // the last step reloads itself (unused)
+        bool all = true;
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) all = all && valid[kb][e];
+        // The common case (every key of the step valid) runs without selects; the
+        // probabilities use the raw base-2 exponential (results below 2^-126 flush to 0).
+        chunk_t pb[QB];
+        auto softmax_step = [&](auto masked) {
+          constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb) {
+            float tmax = NEG;
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                tmax = fmaxf(tmax, (!MASKED || valid[kb][e]) ? s[kb][qb][e] : NEG);
+            tmax = fmaxf(tmax, lane_value(tmax, lane ^ 16));
+            tmax = fmaxf(tmax, lane_value(tmax, lane ^ 32));
+            const float mnew = fmaxf(mrun[qb], tmax);
+            const float msafe = mnew == NEG ? 0.f : mnew;  // no valid key yet: every p is 0
+            // the accumulated sums follow the new maximum: 2^(old - new), 1 when it did not
+            // grow, 0 before the first valid key (old = -inf); no branch, no copies
+            const float scale = __builtin_amdgcn_exp2f(mrun[qb] - msafe);
+            lsum[qb] *= scale;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[db][qb][e] *= scale;
+            mrun[qb] = mnew;
+            float pv[8];
+#pragma unroll
+            for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                const float ex = __builtin_amdgcn_exp2f(s[kb][qb][e] - msafe);
+                pv[4 * kb + e] = (!MASKED || valid[kb][e]) ? ex : 0.f;
+              }
+            float ps = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ps += pv[e];
+            lsum[qb] += ps;
+            pb[qb] = pack(pv, bf16());
+          }
+        };
+        if (__all(all))
+          softmax_step(std::false_type());
+        else
+          softmax_step(std::true_type());
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+          for (int db = 0; db < 2; ++db) o[db][qb] = mma16(o[db][qb], vf[db], pb[qb], bf16());
+        load_v(ks + 1);
       }
       // normalise, gate, stage: o^T lane (p, q) reg e = channel 16 db + 4q + e of query
       // 16 qb + p
       const bf16* const grow = gi + rh * np * ATT_D;
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         float l = lsum[qb];
         l += lane_value(l, lane ^ 16);
         l += lane_value(l, lane ^ 32);
@@ -326,7 +371,7 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
     for (int u = wave; u < CZ / 16; u += KC_WAVES) {
       const f32x4 b0 = ld16f(bo + 16 * u + 4 * q);
 #pragma unroll
-      for (int qb = 0; qb < 4; ++qb) {
+      for (int qb = 0; qb < QB; ++qb) {
         f32x4 acc = b0;
         for (int kk = 0; kk < hd / 32; ++kk)
           acc = mma16(acc, ld16(wo + (16 * u + p) * os_stride + 32 * kk + 8 * q),
@@ -346,7 +391,7 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
 // ---------------------------------------------------------------------------------------
 
 template <int KZ>
-static hipError_t launch_attention_kz(const AttnArgs& a, hipStream_t st) {
+static hipError_t launch_attention_kz(const AttnArgs& a, int stages, hipStream_t st) {
   const int np = att_np(a.n);
   const AttnWorkspace L = att_workspace(a.batch, a.n, a.heads);
   unsigned char* ws = (unsigned char*)a.ws;
@@ -354,11 +399,11 @@ static hipError_t launch_attention_kz(const AttnArgs& a, hipStream_t st) {
   bf16* k = (bf16*)(ws + L.k);
   bf16* g = (bf16*)(ws + L.g);
   bf16* vt = (bf16*)(ws + L.vt);
-  float* bias = (float*)(ws + L.bias);
+  bf16* bias = (bf16*)(ws + L.bias);
   bf16* ms = (bf16*)(ws + L.ms);
 
   // projection: persistent waves over 32-pair tiles of the padded stored grid
-  {
+  if (stages & 1) {
     const size_t lds = att_proj_image_bytes(a.cz, a.heads);
     if (lds % 16) return hipErrorInvalidValue;
     auto fn = ka_project<KZ>;
@@ -380,29 +425,36 @@ static hipError_t launch_attention_kz(const AttnArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e;
   }
   // attention: one workgroup per stored row
-  {
+  if (stages & 2) {
     const size_t img = att_out_image_bytes(a.cz, a.heads);
     const size_t lds = att_core_lds_bytes(a.cz, a.heads);
     if (img % 16) return hipErrorInvalidValue;
-    auto fn = ka_core<KZ>;
+    constexpr int QB = KC_QB;
+    auto fn = ka_core<KZ, QB>;
     static std::atomic<int> granted{0};
     hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.batch * a.n;
     if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(fn, dim3((unsigned int)rows), dim3(KC_THREADS), lds, st, q, k, g, vt,
+    // a row's query tiles are shared by `split` workgroups, enough for four per CU
+    const int qtiles = np / (16 * QB);
+    const long long want = ((long long)a.num_cus * 4 + rows - 1) / rows;
+    const int split = (int)(want < 1 ? 1 : (want > qtiles ? qtiles : want));
+    hipLaunchKernelGGL(fn, dim3((unsigned int)rows, split), dim3(KC_THREADS), lds, st, q, k, g, vt,
                        bias, ms, (const chunk_t*)a.out_image, (int)(img / 16), (bf16*)a.out,
                        a.n, np, a.heads, a.node);
-    return hipGetLastError();
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  return hipSuccess;
 }
 
-hipError_t launch_attention(const AttnArgs& a, hipStream_t st) {
+hipError_t launch_attention(const AttnArgs& a, int stages, hipStream_t st) {
   switch (a.cz / 32) {
-    case 1: return launch_attention_kz<1>(a, st);
-    case 2: return launch_attention_kz<2>(a, st);
-    case 3: return launch_attention_kz<3>(a, st);
-    case 4: return launch_attention_kz<4>(a, st);
+    case 1: return launch_attention_kz<1>(a, stages, st);
+    case 2: return launch_attention_kz<2>(a, stages, st);
+    case 3: return launch_attention_kz<3>(a, stages, st);
+    case 4: return launch_attention_kz<4>(a, stages, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -129,9 +129,13 @@ int tri_attn_workspace_bytes(const tri_attn_handle* h, int batch, int n, size_t*
   return TRI_MUL_OK;
 }
 
-int tri_attn_forward(tri_attn_handle* h, const void* z, const void* pair_mask, void* out,
-                     int batch, int n, int node, void* workspace, size_t ws_bytes,
-                     void* stream) {
+}  // extern "C"
+
+namespace {
+
+int attn_forward(tri_attn_handle* h, int stages, const void* z, const void* pair_mask,
+                 void* out, int batch, int n, int node, void* workspace, size_t ws_bytes,
+                 void* stream) {
   if (!h || !z || !out || !workspace) return TRI_MUL_ERR_INVALID_ARG;
   if (batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N) return TRI_MUL_ERR_INVALID_ARG;
   if (node != TRI_ATTN_STARTING && node != TRI_ATTN_ENDING) return TRI_MUL_ERR_INVALID_ARG;
@@ -163,9 +167,26 @@ int tri_attn_forward(tri_attn_handle* h, const void* z, const void* pair_mask, v
   a.node = node;
   a.mask_all = pair_mask ? 0 : 1;
   a.num_cus = h->num_cus;
-  e = trimul::launch_attention(a, (hipStream_t)stream);
+  e = trimul::launch_attention(a, stages, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "launch triangular attention");
   return TRI_MUL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int tri_attn_forward(tri_attn_handle* h, const void* z, const void* pair_mask, void* out,
+                     int batch, int n, int node, void* workspace, size_t ws_bytes,
+                     void* stream) {
+  return attn_forward(h, 3, z, pair_mask, out, batch, n, node, workspace, ws_bytes, stream);
+}
+
+int tri_attn_forward_stage(tri_attn_handle* h, int stage, const void* z, const void* pair_mask,
+                           void* out, int batch, int n, int node, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  if (stage != 1 && stage != 2) return TRI_MUL_ERR_INVALID_ARG;
+  return attn_forward(h, stage, z, pair_mask, out, batch, n, node, workspace, ws_bytes, stream);
 }
 
 void tri_attn_destroy(tri_attn_handle* h) {

@@ -11,6 +11,14 @@ Per pair (b, i, j), storage element size `esz` (2 for bf16, 4 for fp32):
 and of the pair transition (one kernel), per pair:
   pair_transition reads z (c_z) and the mask (1), writes out (c_z)
                   flops: c_z -> hidden and hidden -> c_z linears, 4 c_z hidden
+and of triangular attention (H heads of width d, per pair and node):
+  ka_project      reads z (c_z) and the mask (1); writes q, k, gate, v (4 H d) in the
+                  storage type, the pair bias (H) and the mask (1)
+                  flops: LayerNorm'd z times 4 H d + H projection rows, 2 c_z (4 H d + H)
+  ka_core         reads q, gate, k, v (4 H d; k and v of a row once) and the mask (1),
+                  the pair bias once per item (H); writes out (c_z)
+                  flops: q.k and p.v over N keys per head, 4 N H d, plus the output
+                  projection 2 H d c_z; one exponential per (query, key, head): N H
 """
 
 MI355X_PEAK = {
@@ -35,3 +43,18 @@ def flops_per_pair(n, c_z, c):
 
 def transition_work(c_z, hidden, esz):
     return {"bytes": esz * (2 * c_z + 1), "flops": 4 * c_z * hidden}
+
+
+def attention_work(n, c_z, heads, d, esz):
+    hd = heads * d
+    return {
+        "ka_project": {"bytes": esz * (c_z + 1 + 4 * hd + heads + 1),
+                       "flops": 2 * c_z * (4 * hd + heads)},
+        "ka_core": {"bytes": esz * (4 * hd + 1 + heads + c_z),
+                    "flops": 4 * n * hd + 2 * hd * c_z, "exps": n * heads},
+    }
+
+
+# transcendental rate of the chip: 256 CUs x 4 SIMDs, each 16 lanes at a quarter of the
+# plain VALU rate (4 results per cycle), at the 2.4 GHz peak engine clock
+MI355X_EXP_PER_S = 256 * 4 * 4 * 2.4e9

@@ -19,7 +19,8 @@ import hashlib
 import os
 
 KERNELS = {"k1_input_gate": "k1_input_gate.hip", "k2_contract": "k2_contract.hip",
-           "k3_output_gate": "k3_output_gate.hip", "pair_transition": "kt_transition.hip"}
+           "k3_output_gate": "k3_output_gate.hip", "pair_transition": "kt_transition.hip",
+           "ka_project": "ka_attention.hip", "ka_core": "ka_attention.hip"}
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 

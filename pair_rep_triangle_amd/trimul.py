@@ -35,7 +35,7 @@ EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layou
 TRANSITION_EXPORTS = ("pair_transition_create", "pair_transition_forward",
                       "pair_transition_destroy")
 ATTENTION_EXPORTS = ("tri_attn_create", "tri_attn_workspace_bytes", "tri_attn_forward",
-                     "tri_attn_destroy")
+                     "tri_attn_forward_stage", "tri_attn_destroy")
 
 
 class TriMulError(RuntimeError):
@@ -96,6 +96,7 @@ def load_library(path=LIB_PATH):
                                     ctypes.POINTER(vp)]
     lib.tri_attn_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.tri_attn_forward.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+    lib.tri_attn_forward_stage.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_attn_destroy.argtypes = [vp]
     lib.tri_attn_destroy.restype = None
     lib.pair_transition_destroy.restype = None
@@ -340,6 +341,14 @@ class TriAttention:
 
     def forward(self, z, mask=None, out=None, node="starting", workspace=None, stream=None):
         """out = triangular attention of z around `node` ("starting" or "ending")."""
+        return self._call(0, z, mask, out, node, workspace, stream)
+
+    def stage(self, stage, z, mask=None, out=None, node="starting", workspace=None, stream=None):
+        """One kernel of forward alone: 1 = projection into the workspace, 2 = attention
+        and output projection from it."""
+        return self._call(int(stage), z, mask, out, node, workspace, stream)
+
+    def _call(self, stage, z, mask, out, node, workspace, stream):
         import torch
         if node not in NODES:
             raise ValueError(f"node must be one of {sorted(NODES)}")
@@ -359,11 +368,12 @@ class TriAttention:
             workspace = self.new_workspace(batch, n, z.device)
         if stream is None:
             stream = torch.cuda.current_stream(z.device).cuda_stream
-        _check(self.lib.tri_attn_forward(self._h, z.data_ptr(),
-                                         None if mask is None else mask.data_ptr(),
-                                         out.data_ptr(), batch, n, NODES[node],
-                                         workspace.data_ptr(), workspace.numel(), stream),
-               "tri_attn_forward")
+        args = (z.data_ptr(), None if mask is None else mask.data_ptr(), out.data_ptr(), batch, n,
+                NODES[node], workspace.data_ptr(), workspace.numel(), stream)
+        if stage == 0:
+            _check(self.lib.tri_attn_forward(self._h, *args), "tri_attn_forward")
+        else:
+            _check(self.lib.tri_attn_forward_stage(self._h, stage, *args), "tri_attn_forward_stage")
         return out
 
     __call__ = forward

@@ -112,7 +112,21 @@ def test_attention_headline_shape_sampled(node):
     got = out.to(torch.float64).cpu().numpy()
     assert np.isfinite(got).all()
     L = d["meta"]["valid_length"]
-    lines = sorted({0, 1, L - 2, L - 1, L, 511} | set(np.random.default_rng(9).integers(0, 512, 4).tolist()))
+    extra = np.random.default_rng(9).integers(0, 512, 4).tolist()
+    lines = sorted({0, 1, L - 2, L - 1, L, 511} | set(extra))
     want = tri_attention_ref_lines(z_host, m_host, w, node, lines)
     sel = got[:, lines] if node == "starting" else np.swapaxes(got[:, :, lines], 1, 2)
     assert rel_err(sel, want) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("node", NODES)
+def test_attention_stages_compose_to_forward(node):
+    """Stage 1 (projection) then stage 2 (attention) gives forward's bytes."""
+    note(f"attention stages {node}")
+    out, z, m, _, _, _, mod = _run(1, 50, 64, 2, "random_pairs", seed=10, node=node)
+    ws = mod.new_workspace(1, 50)
+    staged = torch.empty_like(out)
+    mod.stage(1, z, m, out=staged, node=node, workspace=ws)
+    mod.stage(2, z, m, out=staged, node=node, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(staged, out)
