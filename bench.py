@@ -324,7 +324,7 @@ def bench_attention(args):
                   "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1),
                   "hbm_frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4),
                   "mfma_frac": round(tfl / MI355X_PEAK["bf16_TFLOPs"], 4),
-                  "bytes_per_launch": wk["bytes"] * pairs, "flops_per_launch": wk["flops"] * pairs}
+                  "bytes_per_launch": int(wk["bytes"] * pairs), "flops_per_launch": wk["flops"] * pairs}
             if "exps" in wk:
                 ges = wk["exps"] * pairs / (avg_ms * 1e-3) / 1e9
                 kd["Gexp_per_s"] = round(ges, 1)

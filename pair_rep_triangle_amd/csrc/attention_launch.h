@@ -14,7 +14,8 @@ constexpr int ATT_PAD = 64;    // the stored pair grid is padded to a multiple o
 //   q, k, g  [B][Np][H][Np][d]   bf16   (g already through the sigmoid)
 //   vt       [B][Np][H][d][Np]   bf16   (v transposed: keys contiguous)
 //   bias     [B][H][Np][Np]      bf16   (the pair bias of stored pair (r, c), base 2)
-//   ms       [B][Np][Np]         bf16   (the pair mask in stored coordinates, 0 on padding)
+//   ms       [B][Np][Np / 32]    u32    (key-valid bits of the stored row: bit k of word w is
+//                                        stored column 32 w + k; 0 on padding)
 struct AttnWorkspace {
   size_t q, k, g, vt, bias, ms, total;
 };
@@ -31,7 +32,7 @@ inline AttnWorkspace att_workspace(int batch, int n, int heads) {
   w.vt = w.g + qkv;
   w.bias = w.vt + qkv;
   w.ms = w.bias + att_align(plane * heads * 2);
-  w.total = w.ms + att_align(plane * 2);
+  w.total = w.ms + att_align(plane / 8);
   return w;
 }
 

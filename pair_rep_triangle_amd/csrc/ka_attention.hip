@@ -27,6 +27,7 @@ constexpr int KC_WAVES = 4;                  // attention kernel
 constexpr int KC_THREADS = 64 * KC_WAVES;
 constexpr int KC_QB = 4;                     // 16-query blocks per attention tile
 constexpr int KC_KT = 32;                    // keys per attention step
+constexpr int KC_MIN_SPLIT = 4;              // workgroups per stored row, at least
 
 // ---------------------------------------------------------------------------------------
 // ka_project. A wave tile is 32 consecutive stored columns (two 16-pair subtiles) of one
@@ -40,7 +41,7 @@ template <int KZ>
 __global__ __launch_bounds__(KA_THREADS) void ka_project(
     const bf16* __restrict__ z, const bf16* __restrict__ mask, const chunk_t* __restrict__ image,
     int image_chunks, bf16* __restrict__ qo, bf16* __restrict__ ko, bf16* __restrict__ go,
-    bf16* __restrict__ vto, bf16* __restrict__ bo, bf16* __restrict__ mso, int batch, int n,
+    bf16* __restrict__ vto, bf16* __restrict__ bo, unsigned int* __restrict__ mwo, int batch, int n,
     int np, int heads, int ending, int mask_all) {
   constexpr int E = 8, KG = 32, CZ = KZ * KG, RS = CZ + 8;  // LDS row stride (elements)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -171,17 +172,20 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 #pragma unroll 1
     for (int u = 0; u < hd / 16; ++u) unit_b(3 * hd + 16 * u, false);
     unit_b(4 * hd, true);
-    // mask in stored coordinates (0 on padding): lanes q = 0 write their pair's value
-    if (q == 0) {
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        mso[((size_t)b * np + r) * np + c0 + 16 * st + p] = (bf16)mv[st];
-    }
+    // key-valid bits in stored coordinates (0 on padding): bit k of word c0 / 32 of
+    // stored row r is column c0 + k (nonzero mask value); lanes q = 0 hold the tile's
+    // 32 values
+    const unsigned long long v0 = __ballot(q == 0 && mv[0] != 0.f);
+    const unsigned long long v1 = __ballot(q == 0 && mv[1] != 0.f);
+    if (lane == 0)
+      mwo[((size_t)b * np + r) * (np / 32) + c0 / 32] =
+          (unsigned int)(v0 & 0xffffu) | ((unsigned int)(v1 & 0xffffu) << 16);
   }
 }
 
 // ---------------------------------------------------------------------------------------
-// ka_core. One workgroup per stored row r; its four waves take the heads (wave w: heads
+// ka_core. Stored row r is shared by `split` workgroups (query tiles share, share +
+// split, ...); the four waves of a workgroup take the heads (wave w: heads
 // w, w + 4). Per tile of 64 query columns and head, a wave runs the keys in steps of 32:
 //   S^T = K Q^T (key rows, query columns) with the pair bias as the accumulator start:
 //     lane (p, q) holds keys 16 kb + 4q + rr of query 16 qb + p;
@@ -197,9 +201,9 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 template <int KZ, int QB>
 __global__ __launch_bounds__(KC_THREADS) void ka_core(
     const bf16* __restrict__ qi, const bf16* __restrict__ ki, const bf16* __restrict__ gi,
-    const bf16* __restrict__ vti, const bf16* __restrict__ bi, const bf16* __restrict__ msi,
+    const bf16* __restrict__ vti, const bf16* __restrict__ bi, const unsigned int* __restrict__ mwi,
     const chunk_t* __restrict__ image, int image_chunks, bf16* __restrict__ out, int n, int np,
-    int heads, int ending) {
+    int heads, int ending, int rows, int split) {
   constexpr int CZ = KZ * 32;
   constexpr int QT = 16 * QB;  // queries per tile
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -211,15 +215,26 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int p = lane & 15, q = lane >> 4;
-  const int b = blockIdx.x / n, r = blockIdx.x - b * n;  // blockIdx.y: this row's share
+  // XCD-aware order: workgroup ids are dealt to the eight XCDs in turn. The `split`
+  // workgroups of stored row `row` get ids equal mod 8 and within 8 * split of each other,
+  // so they run together on one XCD and read the row's K and V^T through its L2 once.
+  const int grp = blockIdx.x / (8 * split), w8 = blockIdx.x - grp * 8 * split;
+  const int share = w8 >> 3, row = grp * 8 + (w8 & 7);
+  if (row >= rows) return;  // the last group of eight may be partial (whole workgroup)
+  const int b = row / n, r = row - b * n;
   copy_image<KC_THREADS>(image, (chunk_t*)smem, image_chunks, tid, []() {});
   __syncthreads();
 
   const int ksteps = (n + KC_KT - 1) / KC_KT;  // key steps past n would be all masked
-  const bf16* const msrow = msi + ((size_t)b * np + r) * np;
+  const unsigned int* const mwrow = mwi + ((size_t)b * np + r) * (np / 32);
+  // a row without any valid key (a padded residue) adds nothing: its queries get a zero
+  // attention output without running the key steps
+  unsigned int anyv = 0;
+  for (int t = lane; t < np / 32; t += 64) anyv |= mwrow[t];
+  const int kend = __any(anyv != 0u) ? ksteps : 0;
   const float NEG = -__builtin_huge_valf();
 
-  for (int qt = blockIdx.y; qt < np / QT; qt += gridDim.y) {
+  for (int qt = share; qt < np / QT; qt += split) {
     const int qc0 = qt * QT;
     for (int h = wave; h < heads; h += KC_WAVES) {
       const size_t rh = ((size_t)b * np + r) * heads + h;
@@ -245,13 +260,13 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
       // flags, V^T after the O^T MFMAs), so the loads run a step ahead with no copies.
       chunk_t kf[2], vf[2];
       u32x2 sb[2][QB];  // four bf16 bias values per tile and lane
-      u32x2 mk[2];
+      unsigned int mw;  // the step's key-valid bits (bit k: key k0 + k), wave-uniform
       auto load_kbm = [&](int ks) {
         const int k0 = (ks < ksteps ? ks : ksteps - 1) * KC_KT;
+        mw = __builtin_amdgcn_readfirstlane(mwrow[k0 / KC_KT]);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           kf[kb] = ld16(krow + (size_t)(k0 + 16 * kb + p) * ATT_D + 8 * q);
-          mk[kb] = *(const u32x2*)(msrow + k0 + 16 * kb + 4 * q);
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
             sb[kb][qb] = *(const u32x2*)(brow + (size_t)(qc0 + 16 * qb + p) * np + k0 + 16 * kb + 4 * q);
@@ -270,7 +285,8 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
       load_kbm(0);
       load_v(0);
 #pragma unroll 1
-      for (int ks = 0; ks < ksteps; ++ks) {
+      for (int ks = 0; ks < kend; ++ks) {
+        const unsigned int w = mw;
         f32x4 s[2][QB];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
@@ -281,20 +297,13 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
                               __uint_as_float(bv[1] << 16), __uint_as_float(bv[1] & 0xffff0000u)};
             s[kb][qb] = mma16(b0, kf[kb], qf[qb], bf16());
           }
-        bool valid[2][4];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          valid[kb][0] = (mk[kb][0] & 0x7fffu) != 0;  // nonzero bf16 (either sign of 0 is 0)
-          valid[kb][1] = (mk[kb][0] & 0x7fff0000u) != 0;
-          valid[kb][2] = (mk[kb][1] & 0x7fffu) != 0;
-          valid[kb][3] = (mk[kb][1] & 0x7fff0000u) != 0;
-        }
-        load_kbm(ks + 1);  // the last step reloads itself (unused)
-        bool all = true;
+        bool valid[2][4];  // keys 16 kb + 4q + e (read on the masked path only)
+        const unsigned int wl = w >> (4 * q);
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) all = all && valid[kb][e];
+          for (int e = 0; e < 4; ++e) valid[kb][e] = (wl >> (16 * kb + e)) & 1u;
+        load_kbm(ks + 1);  // the last step reloads itself (unused)
         // The common case (every key of the step valid) runs without selects; the
         // probabilities use the raw base-2 exponential (results below 2^-126 flush to 0).
         chunk_t pb[QB];
@@ -336,7 +345,7 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
             pb[qb] = pack(pv, bf16());
           }
         };
-        if (__all(all))
+        if (w == 0xffffffffu)
           softmax_step(std::false_type());
         else
           softmax_step(std::true_type());
@@ -400,7 +409,7 @@ static hipError_t launch_attention_kz(const AttnArgs& a, int stages, hipStream_t
   bf16* g = (bf16*)(ws + L.g);
   bf16* vt = (bf16*)(ws + L.vt);
   bf16* bias = (bf16*)(ws + L.bias);
-  bf16* ms = (bf16*)(ws + L.ms);
+  unsigned int* mw = (unsigned int*)(ws + L.ms);
 
   // projection: persistent waves over 32-pair tiles of the padded stored grid
   if (stages & 1) {
@@ -420,7 +429,7 @@ static hipError_t launch_attention_kz(const AttnArgs& a, int stages, hipStream_t
     const int blocks = (int)(need < cap ? need : cap);
     hipLaunchKernelGGL(fn, dim3(blocks), dim3(KA_THREADS), lds, st, (const bf16*)a.z,
                        (const bf16*)a.mask, (const chunk_t*)a.proj_image, (int)(lds / 16), q, k,
-                       g, vt, bias, ms, a.batch, a.n, np, a.heads, a.node, a.mask_all);
+                       g, vt, bias, mw, a.batch, a.n, np, a.heads, a.node, a.mask_all);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -436,13 +445,18 @@ static hipError_t launch_attention_kz(const AttnArgs& a, int stages, hipStream_t
     if (e != hipSuccess) return e;
     const long long rows = (long long)a.batch * a.n;
     if (rows > 0x7fffffffLL) return hipErrorInvalidValue;
-    // a row's query tiles are shared by `split` workgroups, enough for four per CU
+    // a row's query tiles are shared by `split` workgroups on one XCD: at least
+    // KC_MIN_SPLIT (they share the row's K and V^T through L2), enough for four per CU
     const int qtiles = np / (16 * QB);
-    const long long want = ((long long)a.num_cus * 4 + rows - 1) / rows;
-    const int split = (int)(want < 1 ? 1 : (want > qtiles ? qtiles : want));
-    hipLaunchKernelGGL(fn, dim3((unsigned int)rows, split), dim3(KC_THREADS), lds, st, q, k, g, vt,
-                       bias, ms, (const chunk_t*)a.out_image, (int)(img / 16), (bf16*)a.out,
-                       a.n, np, a.heads, a.node);
+    const long long rows8 = (rows + 7) / 8 * 8;
+    long long split = ((long long)a.num_cus * 4 + rows - 1) / rows;
+    if (split < KC_MIN_SPLIT) split = KC_MIN_SPLIT;
+    if (split > qtiles) split = qtiles;
+    while (split > 1 && rows8 * split > 0x7fffffffLL) --split;
+    if (rows8 * split > 0x7fffffffLL) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(fn, dim3((unsigned int)(rows8 * split)), dim3(KC_THREADS), lds, st, q, k,
+                       g, vt, bias, mw, (const chunk_t*)a.out_image, (int)(img / 16),
+                       (bf16*)a.out, a.n, np, a.heads, a.node, (int)rows, (int)split);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

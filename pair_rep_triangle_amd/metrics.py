@@ -46,11 +46,13 @@ def transition_work(c_z, hidden, esz):
 
 
 def attention_work(n, c_z, heads, d, esz):
+    """Per pair. ka_project reads z and the mask and writes q, k, gate, v, the per-head
+    bias and one key-valid bit; ka_core reads all of those once and writes out."""
     hd = heads * d
     return {
-        "ka_project": {"bytes": esz * (c_z + 1 + 4 * hd + heads + 1),
+        "ka_project": {"bytes": esz * (c_z + 1 + 4 * hd + heads) + 0.125,
                        "flops": 2 * c_z * (4 * hd + heads)},
-        "ka_core": {"bytes": esz * (4 * hd + 1 + heads + c_z),
+        "ka_core": {"bytes": esz * (4 * hd + heads + c_z) + 0.125,
                     "flops": 4 * n * hd + 2 * hd * c_z, "exps": n * heads},
     }
 
