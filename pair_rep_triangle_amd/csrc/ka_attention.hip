@@ -26,7 +26,7 @@ constexpr int KA_TW = 32;                    // pairs per projection wave tile
 constexpr int KC_WAVES = 4;                  // attention kernel
 constexpr int KC_THREADS = 64 * KC_WAVES;
 constexpr int KC_QB = 4;                     // 16-query blocks per attention tile
-constexpr int KC_KT = 32;                    // keys per attention step
+constexpr int KC_KB = 2;                     // 16-key blocks per attention step (2 or 4)
 constexpr int KC_MIN_SPLIT = 4;              // workgroups per stored row, at least
 
 // ---------------------------------------------------------------------------------------
@@ -186,19 +186,21 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 // ---------------------------------------------------------------------------------------
 // ka_core. Stored row r is shared by `split` workgroups (query tiles share, share +
 // split, ...); the four waves of a workgroup take the heads (wave w: heads
-// w, w + 4). Per tile of 64 query columns and head, a wave runs the keys in steps of 32:
+// w, w + 4). Per tile of 16 QB query columns and head, a wave runs the keys in steps of
+// 16 KB, with the step's keys permuted so that lane q owns 4 KB consecutive ones:
 //   S^T = K Q^T (key rows, query columns) with the pair bias as the accumulator start:
-//     lane (p, q) holds keys 16 kb + 4q + rr of query 16 qb + p;
+//     lane (p, q) of block kb holds keys 4 KB q + 4 kb + e (e < 4) of query 16 qb + p
+//     (the K operand's row p is key 4 KB (p / 4) + 4 kb + p % 4);
 //   online softmax per query in base 2 (log2(e) / sqrt(d) is folded into W_q and
 //     log2(e) into the bias rows), masked keys left out; the four lanes p, p^16, p^32,
 //     p^48 hold all keys of a query, so the running maximum is reduced across them and
 //     the sum is kept per lane until the end;
-//   O^T += V^T P^T: the lane's eight probabilities of a query (keys 4q..4q+3 and
-//     16+4q..16+4q+3 of the step) ARE its B-operand chunk once V^T's A chunk holds the
-//     same keys in the same order, read as two 8-byte runs of the transposed v.
+//   O^T += V^T P^T: each run of eight of the lane's probabilities of a query ARE its
+//     B-operand chunk once V^T's A chunk holds the same eight keys, one 16-byte run of
+//     the transposed v.
 // Then o = O^T / l * gate goes to LDS as [query][h*d + channel]; after a barrier the
 // waves split the output channels: out^T = W_o o^T + b_o with W_o rows from LDS as A.
-template <int KZ, int QB>
+template <int KZ, int QB, int KB>
 __global__ __launch_bounds__(KC_THREADS) void ka_core(
     const bf16* __restrict__ qi, const bf16* __restrict__ ki, const bf16* __restrict__ gi,
     const bf16* __restrict__ vti, const bf16* __restrict__ bi, const unsigned int* __restrict__ mwi,
@@ -225,7 +227,8 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
   copy_image<KC_THREADS>(image, (chunk_t*)smem, image_chunks, tid, []() {});
   __syncthreads();
 
-  const int ksteps = (n + KC_KT - 1) / KC_KT;  // key steps past n would be all masked
+  constexpr int KT = 16 * KB;  // keys per step
+  const int ksteps = (n + KT - 1) / KT;  // key steps past n would be all masked
   const unsigned int* const mwrow = mwi + ((size_t)b * np + r) * (np / 32);
   // a row without any valid key (a padded residue) adds nothing: its queries get a zero
   // attention output without running the key steps
@@ -254,69 +257,82 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
 #pragma unroll
         for (int db = 0; db < 2; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
-      // One key step's operands: K chunks, the bias tiles (the accumulator start of
-      // S^T), the key mask and V^T chunks. Each is reloaded for the next step right after
-      // its last use in this one (bias and K after the S^T MFMAs, the mask after its
-      // flags, V^T after the O^T MFMAs), so the loads run a step ahead with no copies.
-      chunk_t kf[2], vf[2];
-      u32x2 sb[2][QB];  // four bf16 bias values per tile and lane
-      unsigned int mw;  // the step's key-valid bits (bit k: key k0 + k), wave-uniform
+      // One key step's operands (KB blocks of 16 keys): K chunks, the bias tiles (the
+      // accumulator start of S^T), the key-valid bits and V^T chunks. Each is reloaded for
+      // the next step right after its last use in this one (bias, K and the bits after the
+      // S^T MFMAs, V^T after the O^T MFMAs), so the loads run a step ahead with no copies.
+      // Key order: lane q of a step owns the 4 KB consecutive keys 4 KB q .. 4 KB q + 4 KB - 1
+      // (row 4q + e of S^T block kb is key 4 KB q + 4 kb + e), so its bias values and its
+      // V^T chunks are whole 16-byte runs.
+      chunk_t kf[KB], vf[KB / 2][2];
+      chunk_t sb[KB / 2][QB];  // eight bf16 bias values per chunk and lane
+      unsigned long long mw;  // the step's key-valid bits (bit k: key k0 + k), wave-uniform
       auto load_kbm = [&](int ks) {
-        const int k0 = (ks < ksteps ? ks : ksteps - 1) * KC_KT;
-        mw = __builtin_amdgcn_readfirstlane(mwrow[k0 / KC_KT]);
+        const int k0 = (ks < ksteps ? ks : ksteps - 1) * KT;
+        if constexpr (KB == 2) {
+          mw = __builtin_amdgcn_readfirstlane(mwrow[k0 / 32]);
+        } else {
+          const u32x2 w2 = *(const u32x2*)(mwrow + k0 / 32);
+          mw = (unsigned long long)__builtin_amdgcn_readfirstlane(w2[0]) |
+               ((unsigned long long)__builtin_amdgcn_readfirstlane(w2[1]) << 32);
+        }
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          kf[kb] = ld16(krow + (size_t)(k0 + 16 * kb + p) * ATT_D + 8 * q);
+        for (int kb = 0; kb < KB; ++kb) {
+          // A row p of block kb: key 4 KB (p / 4) + 4 kb + p % 4
+          kf[kb] = ld16(krow + (size_t)(k0 + 4 * KB * (p >> 2) + 4 * kb + (p & 3)) * ATT_D + 8 * q);
+        }
+#pragma unroll
+        for (int j = 0; j < KB / 2; ++j)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            sb[kb][qb] = *(const u32x2*)(brow + (size_t)(qc0 + 16 * qb + p) * np + k0 + 16 * kb + 4 * q);
-        }
+            sb[j][qb] = ld16(brow + (size_t)(qc0 + 16 * qb + p) * np + k0 + 4 * KB * q + 8 * j);
       };
-      // V^T rows d = 16 db + p, keys 4q..4q+3 and 16+4q..16+4q+3 of the step
+      // V^T rows d = 16 db + p; half kh of the step: keys 4 KB q + 8 kh .. + 7 (the keys
+      // of the lane's probabilities pv[8 kh .. 8 kh + 7])
       auto load_v = [&](int ks) {
-        const int k0 = (ks < ksteps ? ks : ksteps - 1) * KC_KT;
+        const int k0 = (ks < ksteps ? ks : ksteps - 1) * KT;
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          const bf16* const vp = vrow + (size_t)(16 * db + p) * np + k0 + 4 * q;
-          const u32x2 lo = *(const u32x2*)vp, hi = *(const u32x2*)(vp + 16);
-          vf[db] = chunk_t{lo[0], lo[1], hi[0], hi[1]};
-        }
+        for (int kh = 0; kh < KB / 2; ++kh)
+#pragma unroll
+          for (int db = 0; db < 2; ++db)
+            vf[kh][db] = ld16(vrow + (size_t)(16 * db + p) * np + k0 + 4 * KB * q + 8 * kh);
       };
       load_kbm(0);
       load_v(0);
 #pragma unroll 1
       for (int ks = 0; ks < kend; ++ks) {
-        const unsigned int w = mw;
-        f32x4 s[2][QB];
+        const unsigned long long w = mw;
+        f32x4 s[KB][QB];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            const u32x2 bv = sb[kb][qb];
-            const f32x4 b0 = {__uint_as_float(bv[0] << 16), __uint_as_float(bv[0] & 0xffff0000u),
-                              __uint_as_float(bv[1] << 16), __uint_as_float(bv[1] & 0xffff0000u)};
+            const unsigned int b01 = sb[kb >> 1][qb][2 * (kb & 1)];
+            const unsigned int b23 = sb[kb >> 1][qb][2 * (kb & 1) + 1];
+            const f32x4 b0 = {__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u),
+                              __uint_as_float(b23 << 16), __uint_as_float(b23 & 0xffff0000u)};
             s[kb][qb] = mma16(b0, kf[kb], qf[qb], bf16());
           }
-        bool valid[2][4];  // keys 16 kb + 4q + e (read on the masked path only)
-        const unsigned int wl = w >> (4 * q);
+        bool valid[KB][4];  // keys 4 KB q + 4 kb + e (read on the masked path only)
+        const unsigned long long wl = w >> (4 * KB * q);
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) valid[kb][e] = (wl >> (16 * kb + e)) & 1u;
+          for (int e = 0; e < 4; ++e) valid[kb][e] = (wl >> (4 * kb + e)) & 1u;
         load_kbm(ks + 1);  // the last step reloads itself (unused)
         // The common case (every key of the step valid) runs without selects; the
         // probabilities use the raw base-2 exponential (results below 2^-126 flush to 0).
-        chunk_t pb[QB];
+        chunk_t pb[KB / 2][QB];
         auto softmax_step = [&](auto masked) {
           constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
-            float tmax = NEG;
+            float tmax = (!MASKED || valid[0][0]) ? s[0][qb][0] : NEG;
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                tmax = fmaxf(tmax, (!MASKED || valid[kb][e]) ? s[kb][qb][e] : NEG);
+                if (kb + e > 0) tmax = fmaxf(tmax, (!MASKED || valid[kb][e]) ? s[kb][qb][e] : NEG);
             tmax = fmaxf(tmax, lane_value(tmax, lane ^ 16));
             tmax = fmaxf(tmax, lane_value(tmax, lane ^ 32));
             const float mnew = fmaxf(mrun[qb], tmax);
@@ -330,29 +346,33 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
 #pragma unroll
               for (int e = 0; e < 4; ++e) o[db][qb][e] *= scale;
             mrun[qb] = mnew;
-            float pv[8];
+            float pv[4 * KB];
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
               for (int e = 0; e < 4; ++e) {
                 const float ex = __builtin_amdgcn_exp2f(s[kb][qb][e] - msafe);
                 pv[4 * kb + e] = (!MASKED || valid[kb][e]) ? ex : 0.f;
               }
-            float ps = 0.f;
+            float ps = pv[0];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) ps += pv[e];
+            for (int e = 1; e < 4 * KB; ++e) ps += pv[e];
             lsum[qb] += ps;
-            pb[qb] = pack(pv, bf16());
+#pragma unroll
+            for (int kh = 0; kh < KB / 2; ++kh) pb[kh][qb] = pack(pv + 8 * kh, bf16());
           }
         };
-        if (w == 0xffffffffu)
+        if (w == (KB == 2 ? 0xffffffffull : ~0ull))
           softmax_step(std::false_type());
         else
           softmax_step(std::true_type());
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb)
+        for (int kh = 0; kh < KB / 2; ++kh)
 #pragma unroll
-          for (int db = 0; db < 2; ++db) o[db][qb] = mma16(o[db][qb], vf[db], pb[qb], bf16());
+          for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+              o[db][qb] = mma16(o[db][qb], vf[kh][db], pb[kh][qb], bf16());
         load_v(ks + 1);
       }
       // normalise, gate, stage: o^T lane (p, q) reg e = channel 16 db + 4q + e of query
@@ -439,7 +459,8 @@ static hipError_t launch_attention_kz(const AttnArgs& a, int stages, hipStream_t
     const size_t lds = att_core_lds_bytes(a.cz, a.heads);
     if (img % 16) return hipErrorInvalidValue;
     constexpr int QB = KC_QB;
-    auto fn = ka_core<KZ, QB>;
+    static_assert(KC_KB == 2 || KC_KB == 4, "a step is 32 or 64 keys");
+    auto fn = ka_core<KZ, QB, KC_KB>;
     static std::atomic<int> granted{0};
     hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
     if (e != hipSuccess) return e;
