@@ -14,6 +14,8 @@ constexpr int ATT_PAD = 64;    // the stored pair grid is padded to a multiple o
 //   q, k, g  [B][Np][H][Np][d]   bf16   (g already through the sigmoid)
 //   vt       [B][Np][H][d][Np]   bf16   (v transposed: keys contiguous)
 //   bias     [B][H][Np][Np]      bf16   (the pair bias of stored pair (r, c), base 2)
+//   (the vt planes [d][Np] and the bias planes [Np][Np] in tiles of 16 rows x 32 columns,
+//   row-major inside the tile, tiles row-major: one 1 KB run per tile)
 //   ms       [B][Np][Np / 32]    u32    (key-valid bits of the stored row: bit k of word w is
 //                                        stored column 32 w + k; 0 on padding)
 struct AttnWorkspace {

@@ -29,6 +29,13 @@ constexpr int KC_QB = 4;                     // 16-query blocks per attention ti
 constexpr int KC_KB = 2;                     // 16-key blocks per attention step (2 or 4)
 constexpr int KC_MIN_SPLIT = 4;              // workgroups per stored row, at least
 
+// The bias planes and the v^T planes are stored in tiles of 16 rows x 32 columns (1 KB in
+// bf16, row-major inside the tile): element (row, col) of a plane with np columns sits at
+// tile_off(row, col, np). A wave's 16 rows x 32 keys of a key step are then one 1 KB run.
+__device__ __forceinline__ size_t tile_off(int row, int col, int np) {
+  return ((size_t)(row >> 4) * (np >> 5) + (col >> 5)) * 512 + (row & 15) * 32 + (col & 31);
+}
+
 // ---------------------------------------------------------------------------------------
 // ka_project. A wave tile is 32 consecutive stored columns (two 16-pair subtiles) of one
 // stored row. z arrives in MFMA operand layout (lane (p, q): chunk ks*4 + q of pair p),
@@ -156,10 +163,11 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
         const int c = c0 + 16 * st + 4 * q;
         if (bias) {
           if (p < heads)
-            store4(bo + (((size_t)b * heads + p) * np + r) * np + c, acc[0], acc[1], acc[2],
-                   acc[3]);
+            store4(bo + ((size_t)b * heads + p) * np * np + tile_off(r, c, np), acc[0], acc[1],
+                   acc[2], acc[3]);
         } else {
-          store4(vto + ((rowbase + h) * ATT_D + dd) * np + c, acc[0], acc[1], acc[2], acc[3]);
+          store4(vto + (rowbase + h) * ATT_D * np + tile_off(dd, c, np), acc[0], acc[1], acc[2],
+                 acc[3]);
         }
       }
     };
@@ -285,7 +293,7 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
         for (int j = 0; j < KB / 2; ++j)
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            sb[j][qb] = ld16(brow + (size_t)(qc0 + 16 * qb + p) * np + k0 + 4 * KB * q + 8 * j);
+            sb[j][qb] = ld16(brow + tile_off(qc0 + 16 * qb + p, k0 + 4 * KB * q + 8 * j, np));
       };
       // V^T rows d = 16 db + p; half kh of the step: keys 4 KB q + 8 kh .. + 7 (the keys
       // of the lane's probabilities pv[8 kh .. 8 kh + 7])
@@ -295,7 +303,7 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
         for (int kh = 0; kh < KB / 2; ++kh)
 #pragma unroll
           for (int db = 0; db < 2; ++db)
-            vf[kh][db] = ld16(vrow + (size_t)(16 * db + p) * np + k0 + 4 * KB * q + 8 * kh);
+            vf[kh][db] = ld16(vrow + tile_off(16 * db + p, k0 + 4 * KB * q + 8 * kh, np));
       };
       load_kbm(0);
       load_v(0);
