@@ -52,7 +52,9 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=10)
+    # the GPU's clocks settle only after some 100 ms of sustained work: 200 untimed steps
+    # (about 60 ms of the headline step, more for attention) before the timed region
+    p.add_argument("--warmup", type=int, default=200)
     p.add_argument("--workload", default=None)
     p.add_argument("--chained", action="store_true",
                    help="time the pair update in model order instead: outgoing with its residual "
