@@ -57,6 +57,8 @@ def attention_work(n, c_z, heads, d, esz):
     }
 
 
-# transcendental rate of the chip: 256 CUs x 4 SIMDs, each 16 lanes at a quarter of the
-# plain VALU rate (4 results per cycle), at the 2.4 GHz peak engine clock
-MI355X_EXP_PER_S = 256 * 4 * 4 * 2.4e9
+# transcendental rate of the chip: 256 CUs x 4 SIMDs, each 8 v_exp_f32 results per cycle
+# (half the 16-lane rate of plain fp32 VALU; CDNA 4 doubled the transcendental rate), at
+# the 2.4 GHz peak engine clock. A one-SIMD probe measured 5.4 ns per 64-lane exp2 at about
+# 2.0 GHz (1.2e13/s over the chip), above what a quarter rate would allow.
+MI355X_EXP_PER_S = 256 * 4 * 8 * 2.4e9
