@@ -122,27 +122,38 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
     int opaque;  // keeps the loop-invariant LDS reads inside the tile loop
     asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
 
-    // q, k and gate units: W rows as A. Output row o = 16u + 4q + rr of the block's
-    // projection (h = o / d, channel o % d), pair c0 + 16 st + p.
-    auto unit_a = [&](int row0, int which, bf16* dst) {
-      const bf16* const wrow = wl + (row0 + p) * RS + q * E + opaque;
-      chunk_t wa[KZ];
+    // q, k and gate: one head (two 16-row halves, W rows as A) at a time. The handle
+    // stores a head's 32 rows permuted: row 4q + rr of half hf is channel 8q + 4 hf + rr,
+    // so after both halves lane (p, q) holds channels 8q .. 8q + 7 of the head for pair
+    // c0 + 16 st + p, and one 16-byte store per lane writes the pair's whole 64-byte row.
+    auto head_a = [&](int row0, int which, bf16* dst) {
+      const int h = (row0 - which * hd) / ATT_D;
+      f32x4 acc[2][2];  // [half][st]
 #pragma unroll
-      for (int ks = 0; ks < KZ; ++ks) wa[ks] = ld16(wrow + ks * KG);
-      const f32x4 t0 = ld16f(tl + row0 + 4 * q + opaque);
-      const int o = row0 - which * hd + 4 * q;  // first of this lane's four outputs
-      const int h = o / ATT_D, dd = o - h * ATT_D;
+      for (int hf = 0; hf < 2; ++hf) {
+        const bf16* const wrow = wl + (row0 + 16 * hf + p) * RS + q * E + opaque;
+        chunk_t wa[KZ];
+#pragma unroll
+        for (int ks = 0; ks < KZ; ++ks) wa[ks] = ld16(wrow + ks * KG);
+        const f32x4 t0 = ld16f(tl + row0 + 16 * hf + 4 * q + opaque);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          acc[hf][st] = t0;
+#pragma unroll
+          for (int ks = 0; ks < KZ; ++ks) acc[hf][st] = mma16(acc[hf][st], wa[ks], za[st][ks], bf16());
+        }
+      }
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
-        f32x4 acc = t0;
+        float v[8];
 #pragma unroll
-        for (int ks = 0; ks < KZ; ++ks) acc = mma16(acc, wa[ks], za[st][ks], bf16());
-        if (which == 2) {  // gate: rows scaled by -log2(e), sigmoid = 1 / (1 + 2^acc)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[e] = __builtin_amdgcn_rcpf(1.f + exp2f(acc[e]));
+        for (int e = 0; e < 8; ++e) {
+          v[e] = acc[e >> 2][st][e & 3];
+          // gate: rows scaled by -log2(e), sigmoid = 1 / (1 + 2^acc)
+          if (which == 2) v[e] = __builtin_amdgcn_rcpf(1.f + exp2f(v[e]));
         }
         const int c = c0 + 16 * st + p;
-        store4(dst + ((rowbase + h) * np + c) * ATT_D + dd, acc[0], acc[1], acc[2], acc[3]);
+        st16(dst + ((rowbase + h) * np + c) * ATT_D + 8 * q, pack(v, bf16()));
       }
     };
     // v and bias units: W rows as B. Lane (p, q): pairs c0 + 16 st + 4q .. +3, output
@@ -172,11 +183,11 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
       }
     };
 #pragma unroll 1
-    for (int u = 0; u < hd / 16; ++u) unit_a(16 * u, 0, qo);
+    for (int hh = 0; hh < heads; ++hh) head_a(ATT_D * hh, 0, qo);
 #pragma unroll 1
-    for (int u = 0; u < hd / 16; ++u) unit_a(hd + 16 * u, 1, ko);
+    for (int hh = 0; hh < heads; ++hh) head_a(hd + ATT_D * hh, 1, ko);
 #pragma unroll 1
-    for (int u = 0; u < hd / 16; ++u) unit_a(2 * hd + 16 * u, 2, go);
+    for (int hh = 0; hh < heads; ++hh) head_a(2 * hd + ATT_D * hh, 2, go);
 #pragma unroll 1
     for (int u = 0; u < hd / 16; ++u) unit_b(3 * hd + 16 * u, false);
     unit_b(4 * hd, true);

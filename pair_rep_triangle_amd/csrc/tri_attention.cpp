@@ -74,13 +74,18 @@ int tri_attn_create(const tri_attn_weights* w, int c_z, int heads, int head_dim,
   // (scaled by log2(e)); bias rows past `heads` stay zero
   const double qs = kLog2e / sqrt((double)head_dim);
   for (int o = 0; o < hd; ++o) {
-    const size_t W = (size_t)o * c_z;
+    // q, k and gate rows per head in the projection kernel's order: image row 16 hf + i
+    // of a head (half hf, MFMA row i = 4q + rr) is channel 8q + 4 hf + rr of the head
+    const int i = o % 16, hf = (o / 16) % 2;
+    const int src = o / head_dim * head_dim + 8 * (i >> 2) + 4 * hf + (i & 3);
+    const size_t W = (size_t)src * c_z;
     fold_row(w->w_q + W, w->ln_gamma, w->ln_beta, 0.0, c_z, qs, hp + (size_t)o * rs * 2, hpt + o);
     fold_row(w->w_k + W, w->ln_gamma, w->ln_beta, 0.0, c_z, 1.0, hp + (size_t)(hd + o) * rs * 2,
              hpt + hd + o);
-    fold_row(w->w_g + W, w->ln_gamma, w->ln_beta, w->b_g ? (double)w->b_g[o] : 0.0, c_z, -kLog2e,
-             hp + (size_t)(2 * hd + o) * rs * 2, hpt + 2 * hd + o);
-    fold_row(w->w_v + W, w->ln_gamma, w->ln_beta, 0.0, c_z, 1.0,
+    fold_row(w->w_g + W, w->ln_gamma, w->ln_beta, w->b_g ? (double)w->b_g[src] : 0.0, c_z,
+             -kLog2e, hp + (size_t)(2 * hd + o) * rs * 2, hpt + 2 * hd + o);
+    // v rows in channel order (the v^T unit stores one channel per lane)
+    fold_row(w->w_v + (size_t)o * c_z, w->ln_gamma, w->ln_beta, 0.0, c_z, 1.0,
              hp + (size_t)(3 * hd + o) * rs * 2, hpt + 3 * hd + o);
   }
   for (int h = 0; h < heads; ++h)
