@@ -77,26 +77,29 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
     r = rem / ctiles;
     c0 = (rem - r * ctiles) * KA_TW;
   };
-  // Pairs outside n x n read as zero (their resource extent ends at the last real pair of
-  // the subtile's run; rows past n get an empty extent).
+  // Row p of subtile st is the tile's pair pp(st) = 8 (p / 4) + 4 st + p % 4, so that the
+  // v^T and bias units end with eight consecutive pairs per lane. Pairs outside n x n read
+  // as zero (the resource extent ends at the last real pair of the tile's run; rows past
+  // n get an empty extent).
+  auto pair_of = [&](int st) { return 8 * (p >> 2) + 4 * st + (p & 3); };
   auto fetch = [&](int t, Pre& f) {
     int b, r, c0;
     coords(t < tiles ? t : tiles - 1, b, r, c0);
+    const bool ok = r < n && c0 < n;
+    const size_t x = ending ? (size_t)c0 : (size_t)r, y = ending ? (size_t)r : (size_t)c0;
+    const size_t p0 = ok ? ((size_t)b * n + x) * n + y : 0;
+    // pairs from the tile's first to the last real one of its run
+    const size_t span = ok ? (size_t)(n - 1 - c0) * pstride + 1 : 0;
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(z + p0 * CZ, span * CZ * 2);
+    const __amdgpu_buffer_rsrc_t rm =
+        mask_all ? buffer_rsrc(mask, 2) : buffer_rsrc(mask + p0, span * 2);
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int cs = c0 + 16 * st;
-      const bool ok = r < n && cs < n;
-      const size_t x = ending ? (size_t)cs : (size_t)r, y = ending ? (size_t)r : (size_t)cs;
-      const size_t p0 = ok ? ((size_t)b * n + x) * n + y : 0;
-      // pairs from the subtile's first to the last real one of its run
-      const size_t span = ok ? (size_t)(n - 1 - cs) * pstride + 1 : 0;
-      const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(z + p0 * CZ, span * CZ * 2);
-      const __amdgpu_buffer_rsrc_t rm =
-          mask_all ? buffer_rsrc(mask, 2) : buffer_rsrc(mask + p0, span * 2);
-      const unsigned int zoff = (unsigned int)(((size_t)p * pstride * CZ + q * E) * 2);
+      const unsigned int zoff = (unsigned int)(((size_t)pair_of(st) * pstride * CZ + q * E) * 2);
 #pragma unroll
       for (int ks = 0; ks < KZ; ++ks) f.zv[st][ks] = load16(rz, zoff + ks * KG * 2, 0);
-      f.m[st] = load_elem(rm, mask_all ? 0u : (unsigned int)(p * pstride * 2), 0, bf16());
+      f.m[st] = load_elem(rm, mask_all ? 0u : (unsigned int)(pair_of(st) * pstride * 2), 0,
+                          bf16());
     }
   };
 
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
     float mv[2];
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      mv[st] = (r < n && c0 + 16 * st + p < n) ? to_f32(f.m[st]) : 0.f;
+      mv[st] = (r < n && c0 + pair_of(st) < n) ? to_f32(f.m[st]) : 0.f;
 #pragma unroll
       for (int ks = 0; ks < KZ; ++ks) za[st][ks] = f.zv[st][ks];
       normalize_operand_row<KZ>(za[st], CZ, lane, bf16());
@@ -152,12 +155,13 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
           // gate: rows scaled by -log2(e), sigmoid = 1 / (1 + 2^acc)
           if (which == 2) v[e] = __builtin_amdgcn_rcpf(1.f + exp2f(v[e]));
         }
-        const int c = c0 + 16 * st + p;
+        const int c = c0 + pair_of(st);
         st16(dst + ((rowbase + h) * np + c) * ATT_D + 8 * q, pack(v, bf16()));
       }
     };
-    // v and bias units: W rows as B. Lane (p, q): pairs c0 + 16 st + 4q .. +3, output
-    // 16u' + p of the block.
+    // v and bias units: W rows as B. Lane (p, q): pairs c0 + 8q + 4 st .. +3 (rows 4q .. 4q
+    // + 3 of subtile st), output 16u' + p of the block; the two subtiles leave as one
+    // 16-byte store of pairs c0 + 8q .. c0 + 8q + 7.
     auto unit_b = [&](int row0, bool bias) {
       const bf16* const wrow = wl + (row0 + p) * RS + q * E + opaque;
       chunk_t wb[KZ];
@@ -166,20 +170,21 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
       const float t0 = tl[row0 + p + opaque];
       const int o = bias ? p : row0 - 3 * hd + p;
       const int h = o / ATT_D, dd = o - h * ATT_D;
+      float v[8];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         f32x4 acc = {t0, t0, t0, t0};
 #pragma unroll
         for (int ks = 0; ks < KZ; ++ks) acc = mma16(acc, za[st][ks], wb[ks], bf16());
-        const int c = c0 + 16 * st + 4 * q;
-        if (bias) {
-          if (p < heads)
-            store4(bo + ((size_t)b * heads + p) * np * np + tile_off(r, c, np), acc[0], acc[1],
-                   acc[2], acc[3]);
-        } else {
-          store4(vto + (rowbase + h) * ATT_D * np + tile_off(dd, c, np), acc[0], acc[1], acc[2],
-                 acc[3]);
-        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[4 * st + e] = acc[e];
+      }
+      const int c = c0 + 8 * q;
+      if (bias) {
+        if (p < heads)
+          st16(bo + ((size_t)b * heads + p) * np * np + tile_off(r, c, np), pack(v, bf16()));
+      } else {
+        st16(vto + (rowbase + h) * ATT_D * np + tile_off(dd, c, np), pack(v, bf16()));
       }
     };
 #pragma unroll 1
@@ -194,11 +199,16 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
     // key-valid bits in stored coordinates (0 on padding): bit k of word c0 / 32 of
     // stored row r is column c0 + k (nonzero mask value); lanes q = 0 hold the tile's
     // 32 values
+    // (lane p of subtile st holds pair 8 (p / 4) + 4 st + p % 4: nibble g of a ballot
+    // goes to bits 8g + 4 st)
     const unsigned long long v0 = __ballot(q == 0 && mv[0] != 0.f);
     const unsigned long long v1 = __ballot(q == 0 && mv[1] != 0.f);
-    if (lane == 0)
-      mwo[((size_t)b * np + r) * (np / 32) + c0 / 32] =
-          (unsigned int)(v0 & 0xffffu) | ((unsigned int)(v1 & 0xffffu) << 16);
+    unsigned int word = 0;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+      word |= (unsigned int)((v0 >> (4 * g)) & 0xfu) << (8 * g) |
+              (unsigned int)((v1 >> (4 * g)) & 0xfu) << (8 * g + 4);
+    if (lane == 0) mwo[((size_t)b * np + r) * (np / 32) + c0 / 32] = word;
   }
 }
 
