@@ -38,11 +38,12 @@ __device__ __forceinline__ size_t tile_off(int row, int col, int np) {
 
 // ---------------------------------------------------------------------------------------
 // ka_project. A wave tile is 32 consecutive stored columns (two 16-pair subtiles) of one
-// stored row. z arrives in MFMA operand layout (lane (p, q): chunk ks*4 + q of pair p),
-// is normalised in registers and is the B operand of the q, k and gate units (W rows as
-// A: lane (p, q) ends with outputs 4q..4q+3 of pair p, four consecutive head channels)
-// and the A operand of the v and bias units (W rows as B: lane (p, q) ends with pairs
-// 4q..4q+3 of output p, four consecutive stored columns of v^T and of the bias plane).
+// stored row; row p of subtile st is the tile's pair 8 (p / 4) + 4 st + p % 4. z arrives
+// in MFMA operand layout (lane (p, q): chunk ks*4 + q of that pair), is normalised in
+// registers and is the B operand of the q, k and gate heads (W rows as A, stored
+// permuted per head: lane (p, q) ends with channels 8q..8q+7 of its pair) and the A
+// operand of the v and bias units (W rows as B: lane (p, q) ends with stored columns
+// 8q..8q+7 of output p). Every result leaves as one 16-byte store per lane.
 // The weights (LDS image, rows padded by 16 bytes) are loaded once per workgroup.
 template <int KZ>
 __global__ __launch_bounds__(KA_THREADS) void ka_project(
