@@ -426,20 +426,29 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
       }
     }
     __syncthreads();
-    // out^T = W_o o^T + b_o: lane (p, q) reg e = channel 16u + 4q + e of query 16 qb + p
-    for (int u = wave; u < CZ / 16; u += KC_WAVES) {
-      const f32x4 b0 = ld16f(bo + 16 * u + 4 * q);
+    // out^T = W_o o^T + b_o per group of 32 output channels, as two 16-row halves. The
+    // handle stores W_o's rows (and b_o) permuted per group: row 4q + rr of half hf is
+    // channel 8q + 4 hf + rr, so lane (p, q) ends with channels 32g + 8q .. + 7 of query
+    // 16 qb + p and writes them as one 16-byte store.
+    for (int g = wave; g < CZ / 32; g += KC_WAVES) {
+#pragma unroll 1
+      for (int qb = 0; qb < QB; ++qb) {  // one query block at a time: few live registers
+        f32x4 acc[2];
 #pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        f32x4 acc = b0;
-        for (int kk = 0; kk < hd / 32; ++kk)
-          acc = mma16(acc, ld16(wo + (16 * u + p) * os_stride + 32 * kk + 8 * q),
-                      ld16(os + (16 * qb + p) * os_stride + 32 * kk + 8 * q), bf16());
+        for (int hf = 0; hf < 2; ++hf) {
+          const int u = 2 * g + hf;
+          acc[hf] = ld16f(bo + 16 * u + 4 * q);
+          for (int kk = 0; kk < hd / 32; ++kk)
+            acc[hf] = mma16(acc[hf], ld16(wo + (16 * u + p) * os_stride + 32 * kk + 8 * q),
+                            ld16(os + (16 * qb + p) * os_stride + 32 * kk + 8 * q), bf16());
+        }
         const int qc = qc0 + 16 * qb + p;
         if (qc < n) {
+          float v[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v[e] = acc[e >> 2][e & 3];
           const size_t x = ending ? (size_t)qc : (size_t)r, y = ending ? (size_t)r : (size_t)qc;
-          store4(out + (((size_t)b * n + x) * n + y) * CZ + 16 * u + 4 * q, acc[0], acc[1],
-                 acc[2], acc[3]);
+          st16(out + (((size_t)b * n + x) * n + y) * CZ + 32 * g + 8 * q, pack(v, bf16()));
         }
       }
     }

@@ -91,11 +91,15 @@ int tri_attn_create(const tri_attn_weights* w, int c_z, int heads, int head_dim,
   for (int h = 0; h < heads; ++h)
     fold_row(w->w_b + (size_t)h * c_z, w->ln_gamma, w->ln_beta, 0.0, c_z, kLog2e,
              hp + (size_t)(4 * hd + h) * rs * 2, hpt + 4 * hd + h);
-  // output image: W_o [c_z][hd] rows, b_o
+  // output image: W_o [c_z][hd] rows and b_o, permuted per group of 32 output channels
+  // as the attention kernel's output projection reads them: image row 16 hf + i of a
+  // group (half hf, MFMA row i = 4q + rr) is channel 8q + 4 hf + rr of the group
   for (int c = 0; c < c_z; ++c) {
+    const int i = c % 16, hf = (c / 16) % 2;
+    const int src = c / 32 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
     for (int k = 0; k < hd; ++k)
-      store_elem(ho + ((size_t)c * ors + k) * 2, w->w_o[(size_t)c * hd + k], true);
-    hob[c] = w->b_o ? w->b_o[c] : 0.f;
+      store_elem(ho + ((size_t)c * ors + k) * 2, w->w_o[(size_t)src * hd + k], true);
+    hob[c] = w->b_o ? w->b_o[src] : 0.f;
   }
 
   tri_attn_handle* h = new (std::nothrow) tri_attn_handle();
