@@ -317,15 +317,18 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
           for (int qb = 0; qb < QB; ++qb)
             sb[j][qb] = ld16(brow + tile_off(qc0 + 16 * qb + p, k0 + 4 * KB * q + 8 * j, np));
       };
-      // V^T rows d = 16 db + p; half kh of the step: keys 4 KB q + 8 kh .. + 7 (the keys
-      // of the lane's probabilities pv[8 kh .. 8 kh + 7])
+      // V^T row p of block db is channel 8 (p / 4) + 4 db + p % 4, so that O^T lane (p, q)
+      // ends with channels 8q .. 8q + 7 of its query across the two blocks (one 16-byte
+      // gate load and one 16-byte staging store); half kh of the step: keys 4 KB q + 8 kh
+      // .. + 7 (the keys of the lane's probabilities pv[8 kh .. 8 kh + 7])
       auto load_v = [&](int ks) {
         const int k0 = (ks < ksteps ? ks : ksteps - 1) * KT;
 #pragma unroll
         for (int kh = 0; kh < KB / 2; ++kh)
 #pragma unroll
           for (int db = 0; db < 2; ++db)
-            vf[kh][db] = ld16(vrow + tile_off(16 * db + p, k0 + 4 * KB * q + 8 * kh, np));
+            vf[kh][db] = ld16(vrow + tile_off(8 * (p >> 2) + 4 * db + (p & 3),
+                                              k0 + 4 * KB * q + 8 * kh, np));
       };
       load_kbm(0);
       load_v(0);
@@ -405,8 +408,8 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
               o[db][qb] = mma16(o[db][qb], vf[kh][db], pb[kh][qb], bf16());
         load_v(ks + 1);
       }
-      // normalise, gate, stage: o^T lane (p, q) reg e = channel 16 db + 4q + e of query
-      // 16 qb + p
+      // normalise, gate, stage: o^T lane (p, q) reg e of block db = channel 8q + 4 db + e
+      // of query 16 qb + p
       const bf16* const grow = gi + rh * np * ATT_D;
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
@@ -415,14 +418,11 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
         l += lane_value(l, lane ^ 32);
         const float inv = l > 0.f ? 1.f / l : 0.f;
         const int qc = qc0 + 16 * qb + p;
+        float gv[8], ov[8];
+        unpack(ld16(grow + (size_t)qc * ATT_D + 8 * q), gv, bf16());
 #pragma unroll
-        for (int db = 0; db < 2; ++db) {
-          float gv[4] = {0.f, 0.f, 0.f, 0.f};
-          add4(gv, grow + (size_t)qc * ATT_D + 16 * db + 4 * q);
-          store4(os + (16 * qb + p) * os_stride + h * ATT_D + 16 * db + 4 * q,
-                 o[db][qb][0] * inv * gv[0], o[db][qb][1] * inv * gv[1],
-                 o[db][qb][2] * inv * gv[2], o[db][qb][3] * inv * gv[3]);
-        }
+        for (int e = 0; e < 8; ++e) ov[e] = o[e >> 2][qb][e & 3] * inv * gv[e];
+        st16(os + (16 * qb + p) * os_stride + h * ATT_D + 8 * q, pack(ov, bf16()));
       }
     }
     __syncthreads();
