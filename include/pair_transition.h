@@ -6,8 +6,9 @@
  *
  * RFProteína architecture page: "Inside the velocity network" (each pair update ends
  * with a pair transition, applied as a masked residual) and, under "Kernel support",
- * the pair-transition paragraph of "Dispatch and fallback" (both linears, the ReLU, the mask and the residual in
- * one launch, the hidden activation kept on chip; the released pair width uses an
+ * the pair-transition paragraph of "Dispatch and fallback" (both linears, the ReLU,
+ * the mask and the residual in one launch, the hidden activation kept on chip; the
+ * released pair width uses an
  * expansion of 2, hidden = 2 c_z). The LayerNorm over c_z (biased variance, epsilon
  * TRI_MUL_LN_EPS) is the pre-norm the pages run as a separate norm kernel; here it is
  * folded into W_1 and b_1.

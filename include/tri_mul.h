@@ -86,7 +86,8 @@ typedef struct tri_mul_layout {
 } tri_mul_layout;
 
 /* Build a handle: checks c_z, c (multiples of 16; at most TRI_MUL_MAX_WIDTH for
- * bf16, TRI_MUL_MAX_WIDTH_FP32_CZ / _C for fp32) and dtype, checks that the current device is gfx950, folds both LayerNorm
+ * bf16, TRI_MUL_MAX_WIDTH_FP32_CZ / _C for fp32) and dtype, checks that the current
+ * device is gfx950, folds both LayerNorm
  * affines into the projection weights (in double precision), converts them to
  * `dtype` and copies them to the current device. The only call that allocates.
  * On error *out is set to NULL. */
