@@ -567,6 +567,9 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
       goff[k] = (row0 + pr) * cz + ch0 + cc * E;
       soff[k] = pr * sst + cc * E;
     }
+    // The output is the last thing the update writes and nothing in the update reads it
+    // again: non-temporal stores keep it from displacing x and z in the caches (K3 took
+    // 52.7 instead of 55.2 us at N = 512, c_z = c = 128).
     if constexpr (RESID) {
       // out = z + update. Every z chunk is read before any chunk is written, so the
       // duplicate stores past the row end also add the update to the original z (out may
@@ -575,10 +578,13 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
 #pragma unroll
       for (int k = 0; k < NOUT; ++k) zr[k] = ld16(z + goff[k]);
 #pragma unroll
-      for (int k = 0; k < NOUT; ++k) st16(out + goff[k], add_chunks(ld16(stg + soff[k]), zr[k], T()));
+      for (int k = 0; k < NOUT; ++k)
+        __builtin_nontemporal_store(add_chunks(ld16(stg + soff[k]), zr[k], T()),
+                                    (chunk_t*)(out + goff[k]));
     } else {
 #pragma unroll
-      for (int k = 0; k < NOUT; ++k) st16(out + goff[k], ld16(stg + soff[k]));
+      for (int k = 0; k < NOUT; ++k)
+        __builtin_nontemporal_store(ld16(stg + soff[k]), (chunk_t*)(out + goff[k]));
     }
   }
 }

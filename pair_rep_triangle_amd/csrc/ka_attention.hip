@@ -448,7 +448,10 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
 #pragma unroll
           for (int e = 0; e < 8; ++e) v[e] = acc[e >> 2][e & 3];
           const size_t x = ending ? (size_t)qc : (size_t)r, y = ending ? (size_t)r : (size_t)qc;
-          st16(out + (((size_t)b * n + x) * n + y) * CZ + 32 * g + 8 * q, pack(v, bf16()));
+          // non-temporal: the output is not read again here and would only displace
+          // K, V^T and the bias from the caches (ka_core 235 -> 229 us)
+          __builtin_nontemporal_store(
+              pack(v, bf16()), (chunk_t*)(out + (((size_t)b * n + x) * n + y) * CZ + 32 * g + 8 * q));
         }
       }
     }
