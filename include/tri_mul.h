@@ -85,6 +85,18 @@ typedef struct tri_mul_layout {
   int elem_bytes;                      /* 2 (bf16) or 4 (fp32)          */
 } tri_mul_layout;
 
+/* Which kernel forms a call of (batch, n) takes (tri_mul_query_plan). The input and the
+ * output kernel each come in a wave-independent form (weights in LDS, every wave runs its
+ * own tiles) and a tile-shared form (weights in registers, tiles shared through LDS); the
+ * choice depends on the widths and on the size of one batch item's operands. */
+typedef struct tri_mul_plan {
+  int input_form;    /* 0 wave-independent, 1 tile-shared                        */
+  int output_form;   /* 0 wave-independent, 1 tile-shared                        */
+  int output_groups; /* output-channel groups the output kernel splits c_z into  */
+  int in_place_ok;   /* 1 when tri_mul_forward_residual may take z_out == z      */
+  int n_pad;         /* padded side of the workspace planes                      */
+} tri_mul_plan;
+
 /* Build a handle: checks c_z, c (multiples of 16; at most TRI_MUL_MAX_WIDTH for
  * bf16, TRI_MUL_MAX_WIDTH_FP32_CZ / _C for fp32) and dtype, checks that the current
  * device is gfx950, folds both LayerNorm
@@ -99,6 +111,10 @@ int tri_mul_workspace_bytes(const tri_mul_handle* h, int batch, int n, size_t* b
 
 /* Offsets of a, b and x inside the workspace (see tri_mul_layout). */
 int tri_mul_workspace_layout(const tri_mul_handle* h, int batch, int n, tri_mul_layout* out);
+
+/* The kernel forms a forward call of (batch, n) takes (see tri_mul_plan). Enqueues nothing.
+ * Errors: INVALID_ARG for a NULL handle or output, batch or n out of range. */
+int tri_mul_query_plan(const tri_mul_handle* h, int batch, int n, tri_mul_plan* out);
 
 /* The whole update for one direction: enqueues the three kernels on `stream`.
  *   z          [batch][n][n][c_z]  contiguous, handle dtype, 16-byte aligned
@@ -121,6 +137,11 @@ int tri_mul_forward(tri_mul_handle* h, const void* z, const void* pair_mask, voi
  * ("Inside the velocity network": outgoing, then incoming triangle multiplication).
  *   z_out  [batch][n][n][c_z], handle dtype, 16-byte aligned; either z itself (in
  *          place) or a buffer that does not overlap z, pair_mask or the workspace.
+ *          In place needs the output kernel to produce every channel of a pair in one
+ *          workgroup (tri_mul_plan.in_place_ok: always for bf16 c_z <= 128 and
+ *          fp32 c_z <= 64, for wider shapes only where the plan says so); otherwise z_out == z returns
+ *          TRI_MUL_ERR_ALIAS, because one channel group could overwrite z before
+ *          another has read it.
  * The sum is taken in fp32 and rounded once to the handle dtype. Other arguments and
  * errors as for tri_mul_forward. */
 int tri_mul_forward_residual(tri_mul_handle* h, const void* z, const void* pair_mask,

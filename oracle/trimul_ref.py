@@ -183,6 +183,73 @@ def tri_mul_ref_pairs(z, mask, weights, direction, bidx, iidx, jidx, eps=EPS):
     return out
 
 
+def line_operands(z, mask, weights, bidx, eps=EPS, chunk=8, workers=None):
+    """Steps 1-2 for every pair of batch item `bidx`, channel-major: (a, b) as [c, N, N]
+    float64 with a[ch, i, k] = a_{bidx, i, k, ch} (same for b). Both operands are needed in
+    full for complete output lines: row i of x pairs one row of a with every row of b,
+    column j every row of a with one row of b.
+
+    Pairs are independent in these steps, so blocks of `chunk` residue rows are evaluated
+    on `workers` threads (NumPy releases the interpreter lock inside its array loops); each
+    block is the same arithmetic as `input_operands` on those rows."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    z = np.asarray(z)
+    N = z.shape[1]
+    w = {k: _f64(weights[k]) for k in WEIGHT_FIELDS}
+    c = w["w_a_gate"].shape[0]
+    m_b = np.ones((N, N)) if mask is None else _f64(np.asarray(mask)[bidx])
+    a = np.empty((c, N, N))
+    b = np.empty((c, N, N))
+
+    def block(r0):
+        r1 = min(N, r0 + chunk)
+        _, a_rows, b_rows = input_operands(_f64(z[bidx, r0:r1]), m_b[r0:r1], w, eps)
+        a[:, r0:r1, :] = np.moveaxis(a_rows, -1, 0)
+        b[:, r0:r1, :] = np.moveaxis(b_rows, -1, 0)
+
+    workers = workers or min(16, len(os.sched_getaffinity(0)))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(block, range(0, N, chunk)))
+    return a, b
+
+
+def tri_mul_ref_lines(z, mask, weights, direction, bidx, rows, cols, eps=EPS, operands=None):
+    """Complete output lines of batch item `bidx`: out[bidx, rows, :, :] as [R, N, c_z] and
+    out[bidx, :, cols, :] as [N, C, c_z], float64.
+
+    Steps 1-2 run over every pair of the batch item (`line_operands`; pass its result as
+    `operands` to reuse it for the other direction), steps 3-6 only on the listed lines.
+    For incoming, x_ij = sum_k a_ki b_kj is the outgoing pattern on the transposed
+    operand planes.
+    """
+    z = np.asarray(z)
+    N = z.shape[1]
+    w = {k: _f64(weights[k]) for k in WEIGHT_FIELDS}
+    rows = np.asarray(rows, dtype=np.int64).ravel()
+    cols = np.asarray(cols, dtype=np.int64).ravel()
+    a, b = operands if operands is not None else line_operands(z, mask, weights, bidx, eps)
+    if direction == "incoming":
+        a, b = np.swapaxes(a, 1, 2), np.swapaxes(b, 1, 2)
+    elif direction != "outgoing":
+        raise ValueError(f"direction must be 'outgoing' or 'incoming', got {direction!r}")
+    # x[ch, i, j] = sum_k a[ch, i, k] * b[ch, j, k], on the listed rows and columns
+    x_rows = np.matmul(a[:, rows, :], np.swapaxes(b, 1, 2))          # [c, R, N]
+    x_cols = np.matmul(a, np.swapaxes(b[:, cols, :], 1, 2))          # [c, N, C]
+    m_b = np.ones((N, N)) if mask is None else _f64(np.asarray(mask)[bidx])
+    zr, zc = _f64(z[bidx, rows]), _f64(z[bidx][:, cols])
+    out_rows = output_stage(np.moveaxis(x_rows, 0, -1),
+                            layer_norm(zr, w["ln_in_gamma"], w["ln_in_beta"], eps),
+                            m_b[rows], w, eps)
+    out_cols = output_stage(np.moveaxis(x_cols, 0, -1),
+                            layer_norm(zc, w["ln_in_gamma"], w["ln_in_beta"], eps),
+                            m_b[:, cols], w, eps)
+    return out_rows, out_cols
+
+
 def tri_mul_residual_ref(z, mask, weights, direction, eps=EPS):
     """z + out: the update followed by the masked residual add of the pair update
     [RFProteína architecture page, kernel table: a "masked residual" kernel follows each

@@ -584,6 +584,11 @@ static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
   // two tiles per wave of a full grid the tile-shared form is faster
   const int total = a.batch * a.np * (a.np / K1W_TP);
   if (total < 2 * a.num_cus * K1W_WAVES) return hipSuccess;
+  if (a.plan) {
+    a.plan->k1_form = 0;
+    *done = true;
+    return hipSuccess;
+  }
   const size_t lds = k1w_lds_bytes(ug);
   auto fn = k1_input_gate_waves<T>;
   static std::atomic<int> granted{0};
@@ -609,6 +614,10 @@ static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
 
 template <class T, int KMAX, int UPW, int W>
 static hipError_t launch_k1_t(const StageArgs& a, hipStream_t st) {
+  if (a.plan) {
+    a.plan->k1_form = 1;
+    return hipSuccess;
+  }
   constexpr int E = Traits<T>::E;
   auto lds_for = [&](int nb) {
     return nb * ((size_t)K1_TP * (a.czp + E) * sizeof(T) + K1_TP * sizeof(float)) +

@@ -636,6 +636,12 @@ static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
         break;
       }
     if (ug == 0) return hipSuccess;
+    if (a.plan) {
+      a.plan->k3_form = 0;
+      a.plan->k3_groups = units / ug;
+      *done = true;
+      return hipSuccess;
+    }
     const size_t lds = k3w_lds<T>(a, ug, ST, W);
     auto fn = k3_output_gate_waves<T, KXM, KZM, ST, UGM, W, XBC, RESID>;
     static std::atomic<int> granted{0};
@@ -665,6 +671,11 @@ static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
 
 template <class T, int KXM, int KZM, int XB, bool RESID>
 static hipError_t launch_k3_t(const StageArgs& a, hipStream_t st) {
+  if (a.plan) {
+    a.plan->k3_form = 1;
+    a.plan->k3_groups = (a.cz / 16 + K3_WAVES * K3_UPW - 1) / (K3_WAVES * K3_UPW);
+    return hipSuccess;
+  }
   constexpr int E = Traits<T>::E;
   auto lds_for = [&](int nb) {
     return (size_t)nb * K3_TP * ((a.cp + E) + (a.czp + E)) * sizeof(T) +

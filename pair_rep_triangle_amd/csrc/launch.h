@@ -9,6 +9,14 @@
 
 namespace trimul {
 
+// Which form of the input and output kernels a call takes (filled by a launcher instead of
+// launching when StageArgs::plan is set).
+struct KernelPlan {
+  int k1_form;    // 0 = wave-independent, weights in LDS; 1 = tile-shared, weights in registers
+  int k3_form;    // same two forms for the output kernel
+  int k3_groups;  // output-channel groups the output kernel splits c_z into (grid y)
+};
+
 // Everything one stage launch needs. Pointers are device memory; the element type
 // (bf16 or fp32) is chosen by the launcher's `bf16_storage`.
 struct StageArgs {
@@ -30,6 +38,7 @@ struct StageArgs {
                           // unit group (k1w_layout.h), or nullptr when that form is unused
   int batch, n, np, cz, czp, c, cp, incoming, num_cus;
   int residual;      // stage 3 writes z + update instead of the update (out may be z)
+  KernelPlan* plan;  // when set, the k1 / k3 launchers record their choice and launch nothing
 };
 
 // k extent of one 16x16 MFMA chunk group: 32 (bf16) or 16 (fp32).

@@ -118,28 +118,52 @@ int validate_call(const tri_mul_handle* h, int stage, const void* z, const void*
   return TRI_MUL_OK;
 }
 
-int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out, int batch, int n,
-        int direction, void* ws, size_t ws_bytes, void* stream, bool residual = false) {
-  int rc = validate_call(h, stage, z, mask, out, batch, n, direction, ws, ws_bytes, residual);
-  if (rc != TRI_MUL_OK) return rc;
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (dev != h->device) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
+// The stage arguments of a call (activation pointers may be null for a plan query).
+trimul::StageArgs stage_args(const tri_mul_handle* h, const void* z, const void* mask, void* out,
+                             int batch, int n, int direction, void* ws, bool residual) {
   const Layout L = layout_of(h, batch, n);
   trimul::StageArgs a = h->w;
   a.z = z;
   a.mask = mask;
   a.out = out;
-  a.a = (unsigned char*)ws + L.a;
-  a.b = (unsigned char*)ws + L.b;
-  a.x = (unsigned char*)ws + L.x;
+  a.a = ws ? (unsigned char*)ws + L.a : nullptr;
+  a.b = ws ? (unsigned char*)ws + L.b : nullptr;
+  a.x = ws ? (unsigned char*)ws + L.x : nullptr;
   a.batch = batch;
   a.n = n;
   a.np = L.np;
   a.incoming = direction == TRI_MUL_INCOMING;
   a.num_cus = h->num_cus;
   a.residual = residual ? 1 : 0;
+  a.plan = nullptr;
+  return a;
+}
+
+// The kernel forms a call of (batch, n) takes.
+trimul::KernelPlan plan_of(const tri_mul_handle* h, int batch, int n) {
+  trimul::KernelPlan p{};
+  trimul::StageArgs a = stage_args(h, nullptr, nullptr, nullptr, batch, n, TRI_MUL_OUTGOING,
+                                   nullptr, false);
+  a.plan = &p;
+  (void)trimul::launch_k1(h->bf16, a, nullptr);
+  (void)trimul::launch_k3(h->bf16, a, nullptr);
+  return p;
+}
+
+int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out, int batch, int n,
+        int direction, void* ws, size_t ws_bytes, void* stream, bool residual = false) {
+  int rc = validate_call(h, stage, z, mask, out, batch, n, direction, ws, ws_bytes, residual);
+  if (rc != TRI_MUL_OK) return rc;
+  // In place, each pair of z must be read (all c_z channels, for the gate's LayerNorm)
+  // before any of it is overwritten. That holds only while one workgroup produces all
+  // output channels of a pair; with several channel groups another group may already
+  // have stored its slice.
+  if (residual && out == z && plan_of(h, batch, n).k3_groups > 1) return TRI_MUL_ERR_ALIAS;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev != h->device) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
+  trimul::StageArgs a = stage_args(h, z, mask, out, batch, n, direction, ws, residual);
   hipStream_t st = (hipStream_t)stream;
   if (stage == 0 || stage == 1) {
     e = trimul::launch_k1(h->bf16, a, st);
@@ -281,6 +305,18 @@ int tri_mul_workspace_layout(const tri_mul_handle* h, int batch, int n, tri_mul_
   out->total_bytes = L.total;
   out->n_pad = L.np;
   out->elem_bytes = L.esz;
+  return TRI_MUL_OK;
+}
+
+int tri_mul_query_plan(const tri_mul_handle* h, int batch, int n, tri_mul_plan* out) {
+  if (!h || !out || batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N)
+    return TRI_MUL_ERR_INVALID_ARG;
+  const trimul::KernelPlan p = plan_of(h, batch, n);
+  out->input_form = p.k1_form;
+  out->output_form = p.k3_form;
+  out->output_groups = p.k3_groups;
+  out->in_place_ok = p.k3_groups == 1;
+  out->n_pad = layout_of(h, batch, n).np;
   return TRI_MUL_OK;
 }
 

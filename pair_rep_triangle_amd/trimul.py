@@ -30,7 +30,8 @@ ERRORS = {
     -5: "ALIAS", -6: "WORKSPACE_TOO_SMALL", -7: "HIP", -8: "OUT_OF_MEMORY",
 }
 EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
-           "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage",
+           "tri_mul_query_plan", "tri_mul_forward",
+           "tri_mul_forward_residual", "tri_mul_forward_stage",
            "tri_mul_destroy", "tri_mul_strerror", "tri_mul_last_hip_error")
 TRANSITION_EXPORTS = ("pair_transition_create", "pair_transition_forward",
                       "pair_transition_destroy")
@@ -57,6 +58,12 @@ class AttentionWeights(ctypes.Structure):
     _fields_ = [(name, ctypes.POINTER(ctypes.c_float)) for name in ATTENTION_FIELDS]
 
 
+class Plan(ctypes.Structure):
+    _fields_ = [("input_form", ctypes.c_int), ("output_form", ctypes.c_int),
+                ("output_groups", ctypes.c_int), ("in_place_ok", ctypes.c_int),
+                ("n_pad", ctypes.c_int)]
+
+
 class Layout(ctypes.Structure):
     _fields_ = [("a_offset", ctypes.c_size_t), ("b_offset", ctypes.c_size_t),
                 ("x_offset", ctypes.c_size_t), ("total_bytes", ctypes.c_size_t),
@@ -79,6 +86,7 @@ def load_library(path=LIB_PATH):
     lib.tri_mul_create.argtypes = [ctypes.POINTER(Weights), i, i, i, ctypes.POINTER(vp)]
     lib.tri_mul_workspace_bytes.argtypes = [vp, i, i, ctypes.POINTER(sz)]
     lib.tri_mul_workspace_layout.argtypes = [vp, i, i, ctypes.POINTER(Layout)]
+    lib.tri_mul_query_plan.argtypes = [vp, i, i, ctypes.POINTER(Plan)]
     lib.tri_mul_forward.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_forward_residual.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_forward_stage.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, sz, vp]
@@ -101,7 +109,8 @@ def load_library(path=LIB_PATH):
     lib.tri_attn_destroy.restype = None
     lib.pair_transition_destroy.restype = None
     for name in ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
-                 "tri_mul_forward", "tri_mul_forward_residual", "tri_mul_forward_stage",
+                 "tri_mul_query_plan", "tri_mul_forward",
+           "tri_mul_forward_residual", "tri_mul_forward_stage",
                  "pair_transition_create", "pair_transition_forward"):
         getattr(lib, name).restype = i
     _lib = lib
@@ -114,6 +123,21 @@ def _check(rc, what):
         if rc == -7:
             detail = "- " + load_library().tri_mul_last_hip_error().decode()
         raise TriMulError(rc, what, detail)
+
+
+def _check_device(name, t, z):
+    """Every buffer of a call must be device memory on z's device: a host pointer handed to
+    the kernels is a GPU page fault the C ABI cannot detect."""
+    if t is not None and (not t.is_cuda or t.device != z.device):
+        raise ValueError(f"{name} must be a CUDA tensor on {z.device}, got {t.device}")
+
+
+def _keep_for_stream(t, stream, z):
+    """A buffer allocated here on the current stream but used on `stream`: mark it used there,
+    so the caching allocator does not hand it out again before that stream's work is done."""
+    import torch
+    if stream != torch.cuda.current_stream(z.device).cuda_stream:
+        t.record_stream(torch.cuda.ExternalStream(stream, device=z.device))
 
 
 def _host_f32(v):
@@ -162,6 +186,13 @@ class TriMul:
                "tri_mul_workspace_layout")
         return lay
 
+    def plan(self, batch, n):
+        """The kernel forms a call of (batch, n) takes (tri_mul_query_plan)."""
+        p = Plan()
+        _check(self.lib.tri_mul_query_plan(self._h, int(batch), int(n), ctypes.byref(p)),
+               "tri_mul_query_plan")
+        return {name: getattr(p, name) for name, _ in Plan._fields_}
+
     def torch_dtype(self):
         import torch
         return torch.bfloat16 if self.dtype == "bf16" else torch.float32
@@ -192,16 +223,19 @@ class TriMul:
         if mask is not None:
             if tuple(mask.shape) != (batch, n, n) or mask.dtype != z.dtype or not mask.is_contiguous():
                 raise ValueError("mask must be a contiguous [B, N, N] tensor of z's dtype")
+        for name, t in (("mask", mask), ("out", out), ("workspace", workspace)):
+            _check_device(name, t, z)
+        if direction not in DIRECTIONS:
+            raise ValueError("direction must be 'outgoing' or 'incoming'")
         if out is None:
             out = torch.empty_like(z)
         elif out.shape != z.shape or out.dtype != z.dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous tensor shaped like z")
-        if workspace is None:
-            workspace = self.new_workspace(batch, n, device=z.device)
-        if direction not in DIRECTIONS:
-            raise ValueError("direction must be 'outgoing' or 'incoming'")
         if stream is None:
             stream = torch.cuda.current_stream(z.device).cuda_stream
+        if workspace is None:
+            workspace = self.new_workspace(batch, n, device=z.device)
+            _keep_for_stream(workspace, stream, z)
         return (z.data_ptr(), None if mask is None else mask.data_ptr(), out.data_ptr(),
                 batch, n, DIRECTIONS[direction], workspace.data_ptr(),
                 workspace.numel() * workspace.element_size(), stream), out, workspace
@@ -277,6 +311,8 @@ class PairTransition:
         if mask is not None and (tuple(mask.shape) != (batch, n, n) or mask.dtype != z.dtype
                                  or not mask.is_contiguous()):
             raise ValueError("mask must be a contiguous [B, N, N] tensor of z's dtype")
+        for name, t in (("mask", mask), ("out", out)):
+            _check_device(name, t, z)
         if out is None:
             out = torch.empty_like(z)
         elif out.shape != z.shape or out.dtype != z.dtype or not out.is_contiguous():
@@ -360,16 +396,19 @@ class TriAttention:
         if mask is not None and (tuple(mask.shape) != (batch, n, n) or mask.dtype != z.dtype
                                  or not mask.is_contiguous()):
             raise ValueError("mask must be a contiguous [B, N, N] tensor of z's dtype")
+        for name, t in (("mask", mask), ("out", out), ("workspace", workspace)):
+            _check_device(name, t, z)
         if out is None:
             out = torch.empty_like(z)
         elif out.shape != z.shape or out.dtype != z.dtype or not out.is_contiguous():
             raise ValueError("out must be a contiguous tensor shaped like z")
-        if workspace is None:
-            workspace = self.new_workspace(batch, n, z.device)
         if stream is None:
             stream = torch.cuda.current_stream(z.device).cuda_stream
+        if workspace is None:
+            workspace = self.new_workspace(batch, n, z.device)
+            _keep_for_stream(workspace, stream, z)
         args = (z.data_ptr(), None if mask is None else mask.data_ptr(), out.data_ptr(), batch, n,
-                NODES[node], workspace.data_ptr(), workspace.numel(), stream)
+                NODES[node], workspace.data_ptr(), workspace.numel() * workspace.element_size(), stream)
         if stage == 0:
             _check(self.lib.tri_attn_forward(self._h, *args), "tri_attn_forward")
         else:

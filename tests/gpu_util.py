@@ -40,6 +40,35 @@ def rel_err(got, want):
     return float(np.abs(got - want).max() / (scale if scale > 0 else 1.0))
 
 
+def storage_round(x, dtype):
+    """x (float64) rounded to the storage type, as float64."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float64))
+    return t.to(torch_dtype(dtype)).to(torch.float64).numpy()
+
+
+def storage_ulp(x, dtype):
+    """The spacing of the storage type at |x| (8 significand bits for bf16, 24 for fp32)."""
+    bits = 8 if dtype == "bf16" else 24
+    ax = np.maximum(np.abs(np.asarray(x, np.float64)), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - (bits - 1))
+
+
+def check_residual_update(got, z_host, upd_ref, dtype, tol=None):
+    """A residual output got = round(z + u) against the oracle's update u_ref: every element
+    within tol * max|u_ref| of round(z + u_ref), plus one unit of the storage type at
+    z + u_ref for the final rounding. This holds the computed update itself to the
+    tolerance, whatever the size of z."""
+    want = np.asarray(z_host, np.float64) + upd_ref
+    rounded = storage_round(want, dtype)
+    unit = np.maximum(storage_ulp(want, dtype), storage_ulp(rounded, dtype))
+    bound = (tol or TOL[dtype]) * np.abs(upd_ref).max() + unit
+    excess = np.abs(np.asarray(got, np.float64) - rounded) - bound
+    worst = float(excess.max())
+    assert worst <= 0, (f"update off by {worst:.3e} beyond tol * max|u_ref| + 1 ulp "
+                        f"(max|u_ref| {np.abs(upd_ref).max():.3e})")
+    return float((np.abs(got - rounded) / np.abs(upd_ref).max()).max())
+
+
 def run_full(d, dtype, direction, use_mask=True, module=None):
     z, m, z_host, m_host = to_device(d, dtype)
     c_z, c = d["z"].shape[-1], d["weights"]["w_a_gate"].shape[0]
@@ -76,4 +105,5 @@ def sample_pairs(rng, batch, n, count, valid=None):
 
 
 __all__ = ["TOL", "note", "to_device", "rel_err", "run_full", "check_full", "sample_pairs",
+           "storage_round", "storage_ulp", "check_residual_update",
            "tri_mul_ref", "tri_mul_ref_pairs", "tri_mul_intermediates", "TriMul", "torch_dtype"]

@@ -46,6 +46,11 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_query_plan_rejects_bad_arguments(lib):
+    plan = tm.Plan()
+    assert lib.tri_mul_query_plan(None, 1, 16, ctypes.byref(plan)) == -1
+
+
 def test_strerror_covers_every_code(lib):
     for code in tm.ERRORS:
         msg = lib.tri_mul_strerror(code).decode()

@@ -10,8 +10,9 @@ import pytest
 import torch
 
 from pair_rep_triangle_amd.inputs import WORKLOADS, make_random, make_workload
-from tests.gpu_util import (TOL, TriMul, check_full, note, rel_err, run_full, sample_pairs,
-                            to_device, tri_mul_intermediates, tri_mul_ref, tri_mul_ref_pairs)
+from oracle import line_operands, tri_mul_ref_lines
+from tests.gpu_util import (TOL, TriMul, check_full, check_residual_update, note, rel_err,
+                            run_full, to_device, tri_mul_intermediates, tri_mul_ref, torch_dtype)
 
 pytestmark = pytest.mark.gpu
 DIRS = ("outgoing", "incoming")
@@ -37,29 +38,84 @@ def test_workload_full_output(name, direction):
 
 
 @pytest.mark.parametrize("direction", DIRS)
-@pytest.mark.parametrize("name", ["n768_cz384_c128_b2_bf16", "n2048_cz128_c128_bf16_chains"])
-def test_workload_sampled(name, direction):
-    note(f"workload {name} {direction} sampled")
+def test_wide_pair_track_workload_full_output(direction):
+    """B = 2, N = 768, c_z = 384: every output element against the oracle (about 1.2 TFLOP
+    of fp64 work per direction on the host)."""
+    name = "n768_cz384_c128_b2_bf16"
+    note(f"workload {name} {direction} full")
     d = make_workload(name, seed=0)
-    spec = WORKLOADS[name]
-    dt = torch.bfloat16 if spec["dtype"] == "bf16" else torch.float32
+    err, _, _ = check_full(d, "bf16", direction)
+    print(f"{name} {direction}: rel err {err:.3e}")
+
+
+def _line_set(rng, n, valid=None):
+    """Complete rows and columns that pass through every 256 x 128 tile of the contraction
+    (one random row per 256 rows, one random column per 128 columns), plus the first and
+    last residue and, when padded, both sides of the valid boundary."""
+    rows = [int(rng.integers(r, min(n, r + 256))) for r in range(0, n, 256)]
+    cols = [int(rng.integers(c0, min(n, c0 + 128))) for c0 in range(0, n, 128)]
+    edge = [0, n - 1] + ([valid - 1, valid] if valid is not None and valid < n else [])
+    return sorted(set(rows + edge)), sorted(set(cols + edge))
+
+
+def _check_lines(name_or_d, spec, plan_check=None, label=""):
+    d = make_workload(name_or_d, seed=0) if isinstance(name_or_d, str) else name_or_d
+    B, n, c_z, c, dtype = spec["batch"], spec["n"], spec["c_z"], spec["c"], spec["dtype"]
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
     z = torch.from_numpy(d["z"]).to(dt)
     m = torch.from_numpy(d["mask"]).to(dt)
-    mod = TriMul(d["weights"], spec["c_z"], spec["c"], spec["dtype"])
-    out = mod.forward(z.cuda(), m.cuda(), direction=direction)
+    mod = TriMul(d["weights"], c_z, c, dtype)
+    if plan_check:
+        plan_check(mod.plan(B, n))
     rng = np.random.default_rng(7)
-    bi, ii, jj = sample_pairs(rng, spec["batch"], spec["n"], 48, d["meta"].get("valid_length"))
-    idx = [torch.as_tensor(v, device=out.device) for v in (bi, ii, jj)]
-    got = out[idx[0], idx[1], idx[2]].double().cpu().numpy()
-    finite = bool(torch.isfinite(out).all().item())
+    lines = [_line_set(rng, n, d.get("meta", {}).get("valid_length")) for _ in range(B)]
+    got = {}
+    zc, mc = z.cuda(), m.cuda()
+    ws = mod.new_workspace(B, n)
+    for direction in DIRS:
+        note(f"{label} {direction} lines")
+        out = mod.forward(zc, mc, direction=direction, workspace=ws)
+        torch.cuda.synchronize()
+        assert bool(torch.isfinite(out).all().item())
+        for b, (rows, cols) in enumerate(lines):
+            got[direction, b] = (out[b, rows].double().cpu().numpy(),
+                                 out[b][:, cols].double().cpu().numpy())
+        del out
+    del zc, mc, ws
     torch.cuda.synchronize()
-    del out
-    want = tri_mul_ref_pairs(z.double().numpy(), m.double().numpy(), d["weights"], direction,
-                             bi, ii, jj)
-    err = rel_err(got, want)
-    print(f"{name} {direction}: sampled rel err {err:.3e}")
-    assert finite
-    assert err <= TOL[spec["dtype"]]
+    zh, mh = z.double().numpy(), m.double().numpy()
+    for b, (rows, cols) in enumerate(lines):
+        ops = line_operands(zh, mh, d["weights"], b)  # both directions share a and b
+        for direction in DIRS:
+            want_r, want_c = tri_mul_ref_lines(zh, mh, d["weights"], direction, b, rows, cols,
+                                               operands=ops)
+            got_r, got_c = got[direction, b]
+            scale = max(np.abs(want_r).max(), np.abs(want_c).max())
+            err = max(np.abs(got_r - want_r).max(), np.abs(got_c - want_c).max()) / scale
+            print(f"{label} {direction} b={b}: {len(rows)} rows, {len(cols)} cols, "
+                  f"rel err {err:.3e}")
+            assert err <= TOL[dtype]
+        del ops
+
+
+def test_large_complex_workload_lines():
+    """N = 2048 (chains 900/700/448, all valid): complete output rows and columns through
+    every contraction tile, both directions, in the benchmark's launch configuration."""
+    name = "n2048_cz128_c128_bf16_chains"
+    _check_lines(name, WORKLOADS[name], label=name)
+
+
+def test_operands_over_2gib_take_the_64bit_forms():
+    """N = 2900, c_z = c = 128, bf16: one batch item's z (2.15 GB) and x plane set (2.4 GB)
+    exceed the 32-bit lane offsets of the wave-independent forms, so both projection kernels
+    run their tile-shared forms with 64-bit indexing. Complete lines, both directions."""
+    spec = {"batch": 1, "n": 2900, "c_z": 128, "c": 128, "dtype": "bf16"}
+    d = make_random(1, 2900, 128, 128, seed=29, mask="ones")
+
+    def plan_check(p):
+        assert p["input_form"] == 1 and p["output_form"] == 1, p
+
+    _check_lines(d, spec, plan_check, label="n2900 over 2 GiB")
 
 
 def test_headline_padding_is_zero():
@@ -120,6 +176,52 @@ def test_widest_fp32_full_output(direction):
     note(f"widest fp32 {direction}")
     d = make_random(1, 45, 256, 128, seed=77, mask="random_pairs", random_affine=True)
     check_full(d, "fp32", direction)
+
+
+@pytest.mark.parametrize("dtype,B,n,c_z,c,forms", [
+    ("bf16", 1, 450, 128, 128, (0, 0)),   # both projection kernels wave-independent
+    ("bf16", 1, 129, 128, 128, (1, 0)),   # tile-shared input gate, wave-independent output
+    ("bf16", 2, 70, 128, 512, (1, 1)),    # both tile-shared
+    ("fp32", 1, 450, 64, 32, (0, 0)),
+    ("fp32", 1, 45, 256, 128, (1, 1)),
+])
+def test_writes_nothing_outside_out_and_workspace(dtype, B, n, c_z, c, forms):
+    """out and the workspace sit inside larger buffers filled with a byte pattern, at a
+    ragged n (partial last tiles in every kernel): nothing before or after them may
+    change, z and the mask must be left as they were, and out must still match the
+    oracle. Both directions, with and without the residual add."""
+    d = make_random(B, n, c_z, c, seed=n + c, mask="random_pairs", random_affine=True)
+    z, m, z_host, m_host = to_device(d, dtype)
+    mod = TriMul(d["weights"], c_z, c, dtype)
+    plan = mod.plan(B, n)
+    assert (plan["input_form"], plan["output_form"]) == forms, plan
+    esz = 2 if dtype == "bf16" else 4
+    guard = 16384  # bytes on each side (keeps every buffer 16-byte aligned)
+    obytes = z.numel() * esz
+    obig = torch.full((obytes + 2 * guard,), 0x5A, dtype=torch.uint8, device="cuda")
+    out = obig[guard:guard + obytes].view(torch_dtype(dtype)).view_as(z)
+    wsb = mod.workspace_bytes(B, n)
+    wbig = torch.full((wsb + 2 * guard,), 0xA5, dtype=torch.uint8, device="cuda")
+    ws = wbig[guard:guard + wsb]
+    z0, m0 = z.clone(), m.clone()
+    for direction in DIRS:
+        want = tri_mul_ref(z_host, m_host, d["weights"], direction)
+        for residual in (False, True):
+            note(f"guard bands {dtype} B={B} n={n} c_z={c_z} c={c} {direction} "
+                 f"residual={residual}")
+            if residual:
+                mod.forward_residual(z, m, out=out, direction=direction, workspace=ws)
+            else:
+                mod.forward(z, m, out=out, direction=direction, workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.all(obig[:guard] == 0x5A) and torch.all(obig[guard + obytes:] == 0x5A)
+            assert torch.all(wbig[:guard] == 0xA5) and torch.all(wbig[guard + wsb:] == 0xA5)
+            assert torch.equal(z, z0) and torch.equal(m, m0)
+            got = out.to(torch.float64).cpu().numpy()
+            if residual:
+                check_residual_update(got, z_host, want, dtype)
+            else:
+                assert rel_err(got, want) <= TOL[dtype]
 
 
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
@@ -264,4 +366,42 @@ def test_forward_rejects_bad_calls():
     assert lib.tri_mul_forward_stage(h, 4, zp, mp, op, 1, 24, 0, wp, wsb, st) == -1
     with pytest.raises(TriMulError):
         mod.forward(z, m, direction="incoming", workspace=ws[:16])
+    # host tensors are refused by the binding before anything is launched
+    with pytest.raises(ValueError):
+        mod.forward(z, m.cpu())
+    with pytest.raises(ValueError):
+        mod.forward(z, m, out=torch.empty(z.shape, dtype=z.dtype))
+    with pytest.raises(ValueError):
+        mod.forward(z, m, workspace=torch.empty(wsb, dtype=torch.uint8))
     torch.cuda.synchronize()
+
+
+def test_temporary_workspace_is_kept_for_a_side_stream():
+    """A forward call on another stream without a workspace: the binding's temporary
+    workspace (allocated on the current stream) must not be handed out again to the
+    current stream while the side stream may still use it."""
+    d = make_random(1, 200, 64, 64, seed=12, mask="random_pairs")
+    z, m, _, _ = to_device(d, "bf16")
+    note("temporary workspace on a side stream")
+    mod = TriMul(d["weights"], 64, 64, "bf16")
+    ref = mod.forward(z, m, direction="outgoing")
+    torch.cuda.synchronize()
+    taken = []
+    plain = mod.new_workspace
+
+    def recording(*args, **kw):
+        t = plain(*args, **kw)
+        taken.append(t.data_ptr())
+        return t
+
+    mod.new_workspace = recording
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(50_000_000)  # keeps the side stream busy past the next allocation
+    out = torch.empty_like(z)
+    torch.cuda.current_stream().synchronize()
+    mod.forward(z, m, out=out, direction="outgoing", stream=side.cuda_stream)
+    again = torch.empty(mod.workspace_bytes(1, 200), dtype=torch.uint8, device="cuda")
+    assert len(taken) == 1 and again.data_ptr() != taken[0]
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)

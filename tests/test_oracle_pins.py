@@ -286,6 +286,35 @@ def test_sampled_pairs_match_full(direction):
                                ref.tri_mul_ref(z, None, w, direction)[bi, ii, jj], rtol=1e-12, atol=1e-13)
 
 
+@pytest.mark.parametrize("direction", DIRS)
+def test_lines_match_bruteforce(direction):
+    """Complete output lines against the pure-Python loops, on every line of a tiny case
+    (batch item 1 of 2, so the batch index is exercised)."""
+    z, m, w = _case(2, 4, 3, 2, seed=27, mask="random_pairs")
+    want = np.array(brute_force(z.tolist(), m.tolist(), _tolist(w), direction))
+    rows = cols = np.arange(4)
+    got_r, got_c = ref.tri_mul_ref_lines(z, m, w, direction, 1, rows, cols, operands=None)
+    np.testing.assert_allclose(got_r, want[1], rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(got_c, want[1], rtol=1e-9, atol=1e-12)
+
+
+@pytest.mark.parametrize("direction", DIRS)
+def test_lines_match_full(direction):
+    """Rows and columns at ragged positions, a chunk size that does not divide N, and shared
+    operands reused across both directions all equal the full evaluation."""
+    z, m, w = _case(2, 11, 6, 5, seed=28, mask="random_residues")
+    full = ref.tri_mul_ref(z, m, w, direction)
+    rows, cols = [0, 4, 10, 4], [10, 3]
+    ops = ref.line_operands(z, m, w, 1, chunk=3)
+    got_r, got_c = ref.tri_mul_ref_lines(z, m, w, direction, 1, rows, cols, operands=ops)
+    np.testing.assert_allclose(got_r, full[1][rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(got_c, full[1][:, cols], rtol=1e-12, atol=1e-13)
+    got_r, got_c = ref.tri_mul_ref_lines(z, None, w, direction, 0, rows, cols)
+    full = ref.tri_mul_ref(z, None, w, direction)
+    np.testing.assert_allclose(got_r, full[0][rows], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(got_c, full[0][:, cols], rtol=1e-12, atol=1e-13)
+
+
 # --- the pins are sharp: plausible mistakes planted in the oracle (on the CPU) fail them ---
 
 def _pins_pass():
