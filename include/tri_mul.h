@@ -52,6 +52,8 @@ extern "C" {
 #define TRI_MUL_MAX_WIDTH_FP32_CZ 256     /* largest c_z, fp32                            */
 #define TRI_MUL_MAX_WIDTH_FP32_C 128      /* largest c, fp32                              */
 #define TRI_MUL_LN_EPS 1e-5f              /* epsilon of both LayerNorms                   */
+/* size of the library's own workspace for tri_mul_forward_static (256 MiB per GPU) */
+#define TRI_MUL_STATIC_WORKSPACE_BYTES (256ull * 1024ull * 1024ull)
 
 typedef enum { TRI_MUL_FP32 = 0, TRI_MUL_BF16 = 1 } tri_mul_dtype;
 typedef enum { TRI_MUL_OUTGOING = 0, TRI_MUL_INCOMING = 1 } tri_mul_direction;
@@ -147,6 +149,24 @@ int tri_mul_forward(tri_mul_handle* h, const void* z, const void* pair_mask, voi
 int tri_mul_forward_residual(tri_mul_handle* h, const void* z, const void* pair_mask,
                              void* z_out, int batch, int n, int direction, void* workspace,
                              size_t workspace_bytes, void* stream);
+
+/* tri_mul_forward for callers that cannot allocate device memory or pass a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the a | b | x workspace is a file-scope device array of
+ * TRI_MUL_STATIC_WORKSPACE_BYTES inside this library, one per GPU, held until the
+ * process ends. The call allocates nothing and enqueues the same three kernels as
+ * tri_mul_forward.
+ *   - Calls whose tri_mul_workspace_bytes(h, batch, n) exceeds the array return
+ *     TRI_MUL_ERR_WORKSPACE_TOO_SMALL before any launch (bf16, c = 128: batch * n_pad^2
+ *     up to 2^19, e.g. batch 1 with n <= 512).
+ *   - Every call on one GPU shares that GPU's array, whatever the handle: calls that may
+ *     overlap on one GPU (several streams, several host threads) race on it and must be
+ *     ordered by the caller. Nothing needs the array cleared between calls.
+ *   - The array's device address is looked up once per device (at tri_mul_create on the
+ *     handle's device, else at the first call); a failed lookup returns TRI_MUL_ERR_HIP.
+ * Other arguments and errors as for tri_mul_forward. */
+int tri_mul_forward_static(tri_mul_handle* h, const void* z, const void* pair_mask, void* out,
+                           int batch, int n, int direction, void* stream);
 
 /* One kernel of the chain, same arguments as tri_mul_forward:
  *   stage 1: input LayerNorm + gated dual projection + mask -> a, b (workspace)

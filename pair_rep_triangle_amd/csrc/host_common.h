@@ -59,4 +59,8 @@ inline int check_device(int* dev_out, int* cus_out) {
   return TRI_MUL_OK;
 }
 
+// The device address of the static workspace of tri_mul_forward_static on device `dev`
+// (the current device), looked up once per device (tri_mul_static.hip).
+int static_workspace(int dev, void** ptr);
+
 }  // namespace trimul_host

@@ -200,6 +200,10 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   int dev = -1, cus = 0;
   int rc = check_device(&dev, &cus);
   if (rc != TRI_MUL_OK) return rc;
+  // set-up of the allocation-free entry point on this device: the lookup's result is kept
+  // per device and a failure is reported by tri_mul_forward_static itself
+  void* static_ws = nullptr;
+  (void)static_workspace(dev, &static_ws);
 
   const int kg = trimul::k_group(bf16);
   int kx = 0, kz = 0;

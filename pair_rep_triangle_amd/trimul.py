@@ -30,7 +30,7 @@ ERRORS = {
     -5: "ALIAS", -6: "WORKSPACE_TOO_SMALL", -7: "HIP", -8: "OUT_OF_MEMORY",
 }
 EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
-           "tri_mul_query_plan", "tri_mul_forward",
+           "tri_mul_query_plan", "tri_mul_forward_static", "tri_mul_forward",
            "tri_mul_forward_residual", "tri_mul_forward_stage",
            "tri_mul_destroy", "tri_mul_strerror", "tri_mul_last_hip_error")
 TRANSITION_EXPORTS = ("pair_transition_create", "pair_transition_forward",
@@ -89,6 +89,7 @@ def load_library(path=LIB_PATH):
     lib.tri_mul_query_plan.argtypes = [vp, i, i, ctypes.POINTER(Plan)]
     lib.tri_mul_forward.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_forward_residual.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
+    lib.tri_mul_forward_static.argtypes = [vp, vp, vp, vp, i, i, i, vp]
     lib.tri_mul_forward_stage.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_destroy.argtypes = [vp]
     lib.tri_mul_destroy.restype = None
@@ -109,7 +110,7 @@ def load_library(path=LIB_PATH):
     lib.tri_attn_destroy.restype = None
     lib.pair_transition_destroy.restype = None
     for name in ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
-                 "tri_mul_query_plan", "tri_mul_forward",
+                 "tri_mul_query_plan", "tri_mul_forward_static", "tri_mul_forward",
            "tri_mul_forward_residual", "tri_mul_forward_stage",
                  "pair_transition_create", "pair_transition_forward"):
         getattr(lib, name).restype = i
@@ -213,7 +214,7 @@ class TriMul:
         return tuple(views)
 
     # -- calls -------------------------------------------------------------------------
-    def _args(self, z, mask, out, workspace, direction, stream):
+    def _args(self, z, mask, out, workspace, direction, stream, workspace_needed=True):
         import torch
         if z.dim() != 4 or z.shape[1] != z.shape[2] or z.shape[3] != self.c_z:
             raise ValueError(f"z must be [B, N, N, {self.c_z}], got {tuple(z.shape)}")
@@ -233,12 +234,13 @@ class TriMul:
             raise ValueError("out must be a contiguous tensor shaped like z")
         if stream is None:
             stream = torch.cuda.current_stream(z.device).cuda_stream
-        if workspace is None:
+        if workspace is None and workspace_needed:
             workspace = self.new_workspace(batch, n, device=z.device)
             _keep_for_stream(workspace, stream, z)
+        ws_ptr = workspace.data_ptr() if workspace is not None else None
+        ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
         return (z.data_ptr(), None if mask is None else mask.data_ptr(), out.data_ptr(),
-                batch, n, DIRECTIONS[direction], workspace.data_ptr(),
-                workspace.numel() * workspace.element_size(), stream), out, workspace
+                batch, n, DIRECTIONS[direction], ws_ptr, ws_bytes, stream), out, workspace
 
     def forward(self, z, mask=None, out=None, direction="outgoing", workspace=None, stream=None):
         args, out, _ = self._args(z, mask, out, workspace, direction, stream)
@@ -246,6 +248,14 @@ class TriMul:
         return out
 
     __call__ = forward
+
+    def forward_static(self, z, mask=None, out=None, direction="outgoing", stream=None):
+        """forward with the library's own static workspace (tri_mul_forward_static): no
+        workspace is allocated or passed. Calls that overlap on one GPU race on it."""
+        args, out, _ = self._args(z, mask, out, None, direction, stream, workspace_needed=False)
+        _check(self.lib.tri_mul_forward_static(self._h, *args[:6], args[8]),
+               "tri_mul_forward_static")
+        return out
 
     def forward_residual(self, z, mask=None, out=None, direction="outgoing", workspace=None,
                          stream=None):
