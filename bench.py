@@ -3,11 +3,21 @@
 
 One step = the outgoing update and the incoming update (each: input gate,
 contraction, output gate) on one seeded synthetic batch resident in HBM.
+In order, the run
+  1. measures peaks on this GPU (a 1 GiB device-to-device copy, a vendor bf16 GEMM);
+  2. times every other workload once in its own launch configuration (the
+     `workloads` table: step time, p10/median/p90, TFLOP/s, fraction of the
+     3-kernel floor, per-kernel fractions of HBM and MFMA peak), which keeps the
+     GPU busy so that the headline runs at the clocks of sustained work;
+  3. times the headline workload: W untimed warm-up steps, then exactly K steps
+     between two HIP events -> ms_per_step and value;
+  4. times each kernel and each step of the headline with their own HIP events;
+  5. times the fp64 oracle on this host.
 Prints ONE JSON line:
   value         TFLOP/s over the step (matmul flops of both directions)
   roofline      the dominant kernel's algorithmic GB/s (or TFLOP/s) against the
-                MI355X peak; its duration from HIP events recorded after every
-                kernel in a second timed region of K steps
+                MI355X peak (and against the measured peak); its duration from HIP
+                events recorded after every kernel in a separate region of K steps
   cpu_baseline  the fp64 oracle timed on this host (rank 0, N=1 only)
 With --chained the step is the pair update in model order instead (outgoing with
 its residual add, then incoming on that result with its residual add); the
@@ -25,7 +35,8 @@ c_z -> 2 c_z -> c_z with ReLU, masked residual) on the same workload's z and mas
 line reports pair-updates/s with the same roofline and cpu_baseline objects.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--chained]
-                    [--launch graph|eager] [--op trimul|transition] [--no-cpu-baseline]
+                    [--launch graph|eager] [--op trimul|transition|attention]
+                    [--no-cpu-baseline] [--no-kernel-events] [--no-table]
 """
 
 import argparse
@@ -42,10 +53,6 @@ TRANSITION_METRIC = "pair-transition pair-updates/s (expansion 2, masked residua
 ATTENTION_METRIC = "triangular-attention pair-updates/s (starting+ending node, 4 heads of 32, 1 GPU)"
 KERNELS = ("k1_input_gate", "k2_contract", "k3_output_gate")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
-# A bounded spin on the GPU queued ahead of each per-kernel event region, so the host has
-# enqueued the region's launches before the GPU reaches them: the event pair around a
-# kernel then brackets the kernel, not the host's launch gap.
-HOST_AHEAD_CYCLES = 20_000_000
 
 
 def parse():
@@ -69,6 +76,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-kernel-events", action="store_true",
                    help="time whole steps only (skip the per-kernel timed region)")
+    p.add_argument("--no-table", action="store_true",
+                   help="skip the measured peaks and the other workloads' table")
     p.add_argument("--copy-calibration-mb", type=int, default=0,
                    help="also run a plain device-to-device copy of this many MiB three times "
                         "(reference kernel for scaling HBM byte counters)")
@@ -200,7 +209,6 @@ def bench_transition(args):
     if not args.no_kernel_events:
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
-        torch.cuda._sleep(HOST_AHEAD_CYCLES)
         for a, b in evs:
             a.record(stream)
             step()
@@ -225,7 +233,7 @@ def bench_transition(args):
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import pair_transition_ref
-        threads = min(16, len(os.sched_getaffinity(0)))
+        threads, affinity = cpu_threads()
         zh = torch.from_numpy(d["z"]).to(torch.bfloat16).to(torch.float64).numpy()
         reps, total = 0, 0.0
         with threadpool_limits(limits=threads):
@@ -237,8 +245,9 @@ def bench_transition(args):
         dt = total / reps
         cpu = {"value": round(pairs / dt, 1), "unit": "pair-updates/s", "cores": threads,
                "kind": "oracle", "seconds_per_pass": round(dt, 3),
+               "affinity_cores": affinity,
                "sample": f"whole workload {name}, fp64 NumPy oracle (BLAS on {threads} "
-                         f"threads), {reps} passes averaged"}
+                         f"threads: {cpu_thread_note(threads, affinity)}), {reps} passes averaged"}
 
     rec = {
         "metric": TRANSITION_METRIC, "value": round(pairs / (ms_step * 1e-3), 1),
@@ -304,7 +313,6 @@ def bench_attention(args):
     kernels, roofline = {}, None
     if not args.no_kernel_events:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-        torch.cuda._sleep(HOST_AHEAD_CYCLES)
         for k in range(args.steps):
             evs[k][0].record(stream)
             e = 1
@@ -348,7 +356,7 @@ def bench_attention(args):
     if not args.no_cpu_baseline:
         from threadpoolctl import threadpool_limits
         from oracle import tri_attention_ref
-        threads = min(16, len(os.sched_getaffinity(0)))
+        threads, affinity = cpu_threads()
         zh = torch.from_numpy(d["z"]).to(torch.bfloat16).to(torch.float64).numpy()
         with threadpool_limits(limits=threads):
             t0 = time.perf_counter()
@@ -356,8 +364,10 @@ def bench_attention(args):
             dt = time.perf_counter() - t0
         cpu = {"value": round(pairs / dt, 1), "unit": "pair-updates/s", "cores": threads,
                "kind": "oracle", "seconds_per_pass": round(dt, 2),
+               "affinity_cores": affinity,
                "sample": f"the starting node over the whole workload {name}, fp64 NumPy "
-                         f"oracle (BLAS on {threads} threads), one pass"}
+                         f"oracle (BLAS on {threads} threads: "
+                         f"{cpu_thread_note(threads, affinity)}), one pass"}
 
     flops_pair = work["ka_project"]["flops"] + work["ka_core"]["flops"]
     rec = {
@@ -378,6 +388,168 @@ def bench_attention(args):
     print(json.dumps(rec), flush=True)
 
 
+def measure_peaks(dev):
+    """Peaks measured on this GPU beside the published ones: HBM bandwidth of a plain
+    1 GiB device-to-device copy (read + write bytes over the event time, best of 5), and
+    the vendor bf16 GEMM (torch.matmul, 8192^3, best of 5) as the reachable MFMA rate."""
+    import torch
+    stream = torch.cuda.current_stream(dev)
+    src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    a = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device=dev, dtype=torch.bfloat16)
+    copy_ms, gemm_ms = [], []
+    for _ in range(5):
+        for fn, acc in ((lambda: dst.copy_(src), copy_ms), (lambda: torch.matmul(a, b), gemm_ms)):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            acc.append(e0.elapsed_time(e1))
+    del src, dst, a, b
+    return {"hbm_copy_GBps": round(2 * (1 << 30) / (min(copy_ms) * 1e-3) / 1e9, 1),
+            "bf16_gemm_TFLOPs": round(2 * 8192 ** 3 / (min(gemm_ms) * 1e-3) / 1e12, 1),
+            "how": "1 GiB device-to-device copy (read + write bytes) and torch.matmul "
+                   "8192x8192x8192 bf16, best of 5 each, HIP events"}
+
+
+class TriMulBench:
+    """One workload's modules, buffers and step for the multiplicative update."""
+
+    def __init__(self, name, seed, dev, chained=False):
+        import numpy as np
+        import torch
+        from pair_rep_triangle_amd.inputs import WORKLOADS, make_weights, make_workload
+        from pair_rep_triangle_amd.trimul import TriMul
+
+        self.name, self.spec = name, WORKLOADS[name]
+        self.d = make_workload(name, seed=seed)
+        s = self.spec
+        self.B, self.n, self.c_z, self.c, self.dtype = s["batch"], s["n"], s["c_z"], s["c"], s["dtype"]
+        self.esz = 2 if self.dtype == "bf16" else 4
+        self.w_out = self.d["weights"]
+        self.w_in = make_weights(np.random.default_rng(seed + 1), self.c_z, self.c)  # 2nd module
+        tdt = torch.bfloat16 if self.dtype == "bf16" else torch.float32
+        self.z = torch.from_numpy(self.d["z"]).to(tdt).to(dev)
+        self.mask = torch.from_numpy(self.d["mask"]).to(tdt).to(dev)
+        self.mods = [("outgoing", TriMul(self.w_out, self.c_z, self.c, self.dtype)),
+                     ("incoming", TriMul(self.w_in, self.c_z, self.c, self.dtype))]
+        self.ws = self.mods[0][1].new_workspace(self.B, self.n, device=dev)
+        self.outs = [torch.empty_like(self.z) for _ in self.mods]
+        self.stream = torch.cuda.current_stream(dev)
+        self.chained = chained
+
+    def step(self):
+        mods, outs, z, mask, ws = self.mods, self.outs, self.z, self.mask, self.ws
+        if self.chained:  # z -> outs[0] = z + upd_out(z) -> outs[1] = outs[0] + upd_in(outs[0])
+            mods[0][1].forward_residual(z, mask, out=outs[0], direction="outgoing", workspace=ws)
+            mods[1][1].forward_residual(outs[0], mask, out=outs[1], direction="incoming",
+                                        workspace=ws)
+            return
+        for (direction, mod), out in zip(mods, outs):
+            mod.forward(z, mask, out=out, direction=direction, workspace=ws)
+
+    @property
+    def pairs(self):
+        return self.B * self.n * self.n
+
+    def flops_per_step(self):
+        from pair_rep_triangle_amd.metrics import flops_per_pair
+        return 2 * flops_per_pair(self.n, self.c_z, self.c) * self.pairs
+
+    def floor_ms(self):
+        """The 3-kernel floor of one step: per kernel the larger of its algorithmic bytes
+        over the HBM peak and its flops over the MFMA peak, both directions."""
+        from pair_rep_triangle_amd.metrics import MI355X_PEAK, kernel_work
+        peak = MI355X_PEAK["bf16_TFLOPs"] if self.dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+        t = 0.0
+        for wk in kernel_work(self.n, self.c_z, self.c, self.esz).values():
+            t += max(wk["bytes"] * self.pairs / (MI355X_PEAK["hbm_GBps"] * 1e9),
+                     wk["flops"] * self.pairs / (peak * 1e12))
+        return 2 * t * 1e3
+
+    def kernel_times(self, steps):
+        """Each kernel's duration in the real K1 -> K2 -> K3 order: a HIP event after every
+        kernel on the launch stream. The host enqueues a step (six launches, seven events)
+        in a small fraction of the step's GPU time, so after the first step the queue runs
+        ahead of the GPU and no launch gap is timed. {kernel: samples in ms over both
+        directions}."""
+        import numpy as np
+        import torch
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+        for k in range(steps):
+            evs[k][0].record(self.stream)
+            e = 1
+            for (direction, mod), out in zip(self.mods, self.outs):
+                for s_idx in (1, 2, 3):
+                    mod.stage(s_idx, self.z, self.mask, out=out, direction=direction,
+                              workspace=self.ws)
+                    evs[k][e].record(self.stream)
+                    e += 1
+        torch.cuda.synchronize()
+        per = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(6)]
+                        for k in range(steps)])
+        return {kname: np.concatenate([per[:, i], per[:, i + 3]]) for i, kname in enumerate(KERNELS)}
+
+    def step_times(self, steps):
+        """Each whole step between its own pair of HIP events."""
+        import numpy as np
+        import torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for a, b in evs:
+            a.record(self.stream)
+            self.step()
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in evs])
+
+    def kernel_report(self, samples):
+        from pair_rep_triangle_amd.metrics import MI355X_PEAK, kernel_work
+        import numpy as np
+        work = kernel_work(self.n, self.c_z, self.c, self.esz)
+        peak_fl = MI355X_PEAK["bf16_TFLOPs"] if self.dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+        ridge = peak_fl * 1e12 / (MI355X_PEAK["hbm_GBps"] * 1e9)
+        kernels = {}
+        for kname, smp in samples.items():
+            avg_ms, med_ms = float(smp.mean()), float(np.median(smp))
+            wk = work[kname]
+            gbps = wk["bytes"] * self.pairs / (avg_ms * 1e-3) / 1e9
+            tfl = wk["flops"] * self.pairs / (avg_ms * 1e-3) / 1e12
+            kernels[kname] = {
+                "avg_us": round(avg_ms * 1e3, 3), "median_us": round(med_ms * 1e3, 3),
+                "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1),
+                "hbm_frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4),
+                "mfma_frac": round(tfl / peak_fl, 4),
+                "bound": "hbm" if wk["flops"] / wk["bytes"] < ridge else "mfma",
+                "bytes_per_launch": wk["bytes"] * self.pairs,
+                "flops_per_launch": wk["flops"] * self.pairs,
+            }
+        return kernels
+
+    def summary(self, ms_step, step_samples, kernels):
+        import numpy as np
+        fl = self.flops_per_step()
+        rec = {"ms_per_step": round(ms_step, 4),
+               "TFLOPs": round(fl / (ms_step * 1e-3) / 1e12, 2),
+               "pair_updates_per_s": round(2 * self.pairs / (ms_step * 1e-3), 1),
+               "floor_ms": round(self.floor_ms(), 4),
+               "floor_frac": round(self.floor_ms() / ms_step, 4)}
+        if step_samples is not None:
+            rec["step_ms_p10_median_p90"] = [round(float(np.percentile(step_samples, q)), 4)
+                                             for q in (10, 50, 90)]
+        if kernels:
+            rec["kernels"] = {k: {f: v[f] for f in ("avg_us", "hbm_frac", "mfma_frac", "bound")}
+                              for k, v in kernels.items()}
+        return rec
+
+    def close(self):
+        for _, mod in self.mods:
+            mod.close()
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -391,97 +563,56 @@ def main():
         bench_attention(args)
         return
 
-    import numpy as np
     import torch
-    from pair_rep_triangle_amd.inputs import HEADLINE, WORKLOADS, make_weights, make_workload
-    from pair_rep_triangle_amd.metrics import MI355X_PEAK, flops_per_pair, kernel_work
-    from pair_rep_triangle_amd.trimul import TriMul
+    from pair_rep_triangle_amd.inputs import HEADLINE, WORKLOADS
+    from pair_rep_triangle_amd.metrics import MI355X_PEAK
 
     name = args.workload or HEADLINE
-    spec = WORKLOADS[name]
-    d = make_workload(name, seed=args.seed)
-    B, n, c_z, c, dtype = spec["batch"], spec["n"], spec["c_z"], spec["c"], spec["dtype"]
-    w_out = d["weights"]
-    w_in = make_weights(np.random.default_rng(args.seed + 1), c_z, c)  # second module
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
-    esz = 2 if dtype == "bf16" else 4
-
     dev = torch.device("cuda:0")
-    z = torch.from_numpy(d["z"]).to(tdt).to(dev)
-    mask = torch.from_numpy(d["mask"]).to(tdt).to(dev)
-    mods = [("outgoing", TriMul(w_out, c_z, c, dtype)), ("incoming", TriMul(w_in, c_z, c, dtype))]
-    ws = mods[0][1].new_workspace(B, n, device=dev)
-    outs = [torch.empty_like(z) for _ in mods]
-    stream = torch.cuda.current_stream(dev)
+    # the headline's inputs go to the GPU first: building them on the host takes a while,
+    # and the GPU's clocks drop while it idles, so its timed steps must follow GPU work
+    hb = TriMulBench(name, args.seed, dev, chained=args.chained)
 
-    def step():
-        if args.chained:  # z -> outs[0] = z + upd_out(z) -> outs[1] = outs[0] + upd_in(outs[0])
-            mods[0][1].forward_residual(z, mask, out=outs[0], direction="outgoing", workspace=ws)
-            mods[1][1].forward_residual(outs[0], mask, out=outs[1], direction="incoming",
-                                        workspace=ws)
-            return
-        for (direction, mod), out in zip(mods, outs):
-            mod.forward(z, mask, out=out, direction=direction, workspace=ws)
+    # 1. peaks measured on this GPU
+    peaks = measure_peaks(dev) if not args.no_table else None
 
+    # 2. every other workload once, each in the launch configuration of its own bench line
+    #    (K steps after max(W, 3) warm-up steps, then per-kernel and per-step events). The
+    #    GPU is busy throughout, so the headline below runs at the clocks of sustained work.
+    table = {}
+    if not args.no_table:
+        for other in WORKLOADS:
+            if other == name:
+                continue
+            wb = TriMulBench(other, args.seed, dev)
+            for _ in range(max(args.warmup, 3)):
+                wb.step()
+            ms, _ = timed_steps(wb.step, args.steps, wb.stream)
+            table[other] = wb.summary(ms, wb.step_times(args.steps),
+                                      wb.kernel_report(wb.kernel_times(args.steps)))
+            wb.close()
+            del wb
+            torch.cuda.synchronize()
+            torch.cuda.empty_cache()
+
+    # 3. the headline: W untimed warm-up steps, then exactly K timed steps
     for _ in range(args.warmup):
-        step()
+        hb.step()
     torch.cuda.synchronize()
-
     copy_calibration(args.copy_calibration_mb, dev)
-
-    # timed region 1: K whole steps (outgoing + incoming), HIP events on the launch stream;
-    # eager launches, then (--launch graph) the same step captured once and replayed K times
-    ms_eager, wall = timed_steps(step, args.steps, stream)
+    ms_eager, wall = timed_steps(hb.step, args.steps, hb.stream)
     ms_step, launch = ms_eager, "eager"
     if args.launch == "graph":
-        graph = graph_of(step, dev)
-        ms_step, wall = timed_steps(graph.replay, args.steps, stream)
+        graph = graph_of(hb.step, dev)
+        ms_step, wall = timed_steps(graph.replay, args.steps, hb.stream)
         launch = "hipgraph"
 
-    # timed region 2: the same K steps again with a HIP event after every kernel (on the
-    # launch stream), for each kernel's duration inside the real K1 -> K2 -> K3 order.
-    # Kept apart from region 1 because every event adds a marker packet to the stream.
-    # The host queues it while the GPU runs a short spin, so no launch gap is timed.
-    per_kernel_ms = {}
+    # 4. per-kernel and per-step event regions of the same workload (kept apart from the
+    #    timed region: every event adds a marker packet to the stream)
+    kernels, step_samples = {}, None
     if not args.no_kernel_events:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-        torch.cuda._sleep(HOST_AHEAD_CYCLES)
-        for k in range(args.steps):
-            evs[k][0].record(stream)
-            e = 1
-            for (direction, mod), out in zip(mods, outs):
-                for s_idx in (1, 2, 3):
-                    mod.stage(s_idx, z, mask, out=out, direction=direction, workspace=ws)
-                    evs[k][e].record(stream)
-                    e += 1
-        torch.cuda.synchronize()
-        per = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(6)]
-                        for k in range(args.steps)])
-        for idx, kname in enumerate(KERNELS):
-            samples = np.concatenate([per[:, idx], per[:, idx + 3]])  # both directions
-            per_kernel_ms[kname] = (float(samples.mean()), float(np.median(samples)))
-
-    pairs = B * n * n
-    fl_dir = flops_per_pair(n, c_z, c) * pairs
-    tflops = 2 * fl_dir / (ms_step * 1e-3) / 1e12
-    pair_updates = 2 * pairs / (ms_step * 1e-3)
-
-    work = kernel_work(n, c_z, c, esz)
-    kernels = {}
-    for kname, (avg_ms, med_ms) in per_kernel_ms.items():
-        wk = work[kname]
-        gbps = wk["bytes"] * pairs / (avg_ms * 1e-3) / 1e9
-        tfl = wk["flops"] * pairs / (avg_ms * 1e-3) / 1e12
-        ai = wk["flops"] / wk["bytes"]
-        peak_fl = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
-        ridge = peak_fl * 1e12 / (MI355X_PEAK["hbm_GBps"] * 1e9)
-        bound = "hbm" if ai < ridge else "mfma"
-        kernels[kname] = {
-            "avg_us": round(avg_ms * 1e3, 3), "median_us": round(med_ms * 1e3, 3), "GBps": round(gbps, 1), "TFLOPs": round(tfl, 1),
-            "hbm_frac": round(gbps / MI355X_PEAK["hbm_GBps"], 4),
-            "mfma_frac": round(tfl / peak_fl, 4), "bound": bound,
-            "bytes_per_launch": wk["bytes"] * pairs, "flops_per_launch": wk["flops"] * pairs,
-        }
+        kernels = hb.kernel_report(hb.kernel_times(args.steps))
+        step_samples = hb.step_times(args.steps)
 
     roofline = None
     if kernels:
@@ -493,38 +624,66 @@ def main():
                         "peak": MI355X_PEAK["hbm_GBps"], "unit": "GB/s",
                         "frac": round(kd["GBps"] / MI355X_PEAK["hbm_GBps"], 4), "traffic": traffic}
         else:
-            pk = MI355X_PEAK["bf16_TFLOPs"] if dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
+            pk = MI355X_PEAK["bf16_TFLOPs"] if hb.dtype == "bf16" else MI355X_PEAK["fp32_mfma_TFLOPs"]
             roofline = {"kernel": dom, "bound": "mfma", "achieved": kd["TFLOPs"], "peak": pk,
                         "unit": "TFLOP/s", "frac": round(kd["TFLOPs"] / pk, 4), "traffic": traffic}
+        if peaks:
+            roofline["frac_of_measured_peak"] = round(
+                kd["GBps"] / peaks["hbm_copy_GBps"] if kd["bound"] == "hbm"
+                else kd["TFLOPs"] / peaks["bf16_gemm_TFLOPs"], 4)
 
+    # 5. the oracle on the host
     cpu = None
     if not args.no_cpu_baseline:
-        threads = min(16, len(os.sched_getaffinity(0)))
-        dt, reps = cpu_baseline(d, [("outgoing", w_out), ("incoming", w_in)], threads)
-        cpu = {"value": round(2 * fl_dir / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+        threads, affinity = cpu_threads()
+        dt, reps = cpu_baseline(hb.d, [("outgoing", hb.w_out), ("incoming", hb.w_in)], threads)
+        fl = hb.flops_per_step()
+        cpu = {"value": round(fl / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
                "kind": "oracle", "seconds_per_pass": round(dt, 2),
-               "pair_updates_per_s": round(2 * pairs / dt, 1),
+               "pair_updates_per_s": round(2 * hb.pairs / dt, 1), "affinity_cores": affinity,
                "sample": f"whole workload {name}, outgoing + incoming, fp64 NumPy oracle "
-                         f"(BLAS on {threads} threads), {reps} passes averaged"}
+                         f"(BLAS on {threads} threads: {cpu_thread_note(threads, affinity)}), "
+                         f"{reps} passes averaged"}
 
+    head = hb.summary(ms_step, step_samples, kernels)
+    table[name] = dict(head, headline=True)
     rec = {
-        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "metric": METRIC, "value": head["TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),
         "ms_per_step_eager": round(ms_eager, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": dtype,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": hb.dtype,
         "data": "synthetic",
-        "config": {"workload": name, "batch": B, "n": n, "c_z": c_z, "c": c,
-                   "valid_length": d["meta"].get("valid_length", n),
+        "config": {"workload": name, "batch": hb.B, "n": hb.n, "c_z": hb.c_z, "c": hb.c,
+                   "valid_length": hb.d["meta"].get("valid_length", hb.n),
                    "directions": ("outgoing->incoming, chained with residual adds"
                                   if args.chained else "outgoing+incoming"),
-                   "mask": spec["mask"], "launch": launch},
-        "pair_updates_per_s": round(pair_updates, 1),
+                   "mask": hb.spec["mask"], "launch": launch},
+        "pair_updates_per_s": head["pair_updates_per_s"],
+        "floor_frac": head["floor_frac"],
+        "step_ms_p10_median_p90": head.get("step_ms_p10_median_p90"),
         "wall_s": round(wall, 3),
         "roofline": roofline,
         "kernels": kernels,
+        "measured_peaks": peaks,
+        "workloads": table,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
+
+
+def cpu_threads():
+    """Threads for the oracle: every core in the process's affinity, capped by the host's
+    CPU share when the environment sets one (OMP_NUM_THREADS). Returns (threads, affinity)."""
+    affinity = len(os.sched_getaffinity(0))
+    share = os.environ.get("OMP_NUM_THREADS")
+    threads = min(affinity, int(share)) if share and share.isdigit() and int(share) > 0 else affinity
+    return threads, affinity
+
+
+def cpu_thread_note(threads, affinity):
+    if threads == affinity:
+        return "every core in the affinity mask"
+    return f"the host's CPU share OMP_NUM_THREADS={threads} of {affinity} cores in the affinity mask"
 
 
 def measured_traffic(workload, kernel):

@@ -11,8 +11,13 @@ namespace trimul {
 
 // Workgroup tile 256 (i) x 128 (j), 4 waves as 2 x 2, each 128 x 64 (4 x 2 MFMA 32x32
 // tiles, 128 fp32 accumulators per lane). k advances 64 bytes per row and stage; stages
-// move from global memory straight into LDS (global_load_lds, no registers on the way)
-// through a ring of three LDS buffers, so two stages are in flight while one is used.
+// move from global memory straight into LDS (buffer loads with the LDS bit, no registers
+// on the way) through a ring of three LDS buffers, so two stages are in flight while one
+// is used. A lane's byte offset inside the tile's rows is the same for every stage (the
+// stage is the scalar offset), so no address register is rewritten while a load that
+// reads it may still be waiting to issue. The six loads that fetch stage s + 2 are spread
+// between the sixteen MFMAs of stage s: a load waits for the CU's memory path to accept
+// it, and the MFMAs already issued keep the matrix unit busy meanwhile.
 // Inside a buffer a row is four 16-byte chunks; chunk c of row r sits at position
 // c ^ ((r ^ (r >> 2)) & 3), which keeps the MFMA operand reads free of bank conflicts
 // (checked for both 32- and 64-bank LDS). The output tile is staged in LDS and leaves as
@@ -27,9 +32,30 @@ constexpr int K2_KC = 4;                                   // 16-byte chunks per
 constexpr int K2_A_BYTES = K2_BM * K2_KC * 16;             // 16 KB
 constexpr int K2_B_BYTES = K2_BN * K2_KC * 16;             // 8 KB
 constexpr int K2_STAGE_BYTES = K2_A_BYTES + K2_B_BYTES;    // 24 KB
+constexpr int K2_LOADS_A = K2_BM / 16 / 4;                 // per thread and stage: 4
+constexpr int K2_LOADS = K2_LOADS_A + K2_BN / 16 / 4;      // 6
 static_assert(N_PAD % K2_BM == 0 && N_PAD % K2_BN == 0, "padded side covers whole tiles");
 
 __device__ __forceinline__ int k2_swizzle(int r) { return (r ^ (r >> 2)) & 3; }
+
+// 16 bytes per lane through a buffer resource straight into LDS: lane i writes
+// lds_base + 16 i (lds_base wave-uniform); completion is counted by vmcnt.
+__device__ __forceinline__ void lds_dma16_buf(__amdgpu_buffer_rsrc_t r, unsigned int voff,
+                                              int soff, void* lds_base) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base,
+                                           16, (int)voff, soff, 0, 0);
+}
+
+// Scheduling groups for the instructions of one basic block: NL times (the next share of
+// MF MFMAs, then one memory load), spreading NL loads evenly over MF MFMAs.
+template <int MF, int NL, int Q = 0>
+__device__ __forceinline__ void mfma_load_groups() {
+  if constexpr (Q < NL) {
+    __builtin_amdgcn_sched_group_barrier(0x008, (MF * (Q + 1)) / NL - (MF * Q) / NL, 0);
+    __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+    mfma_load_groups<MF, NL, Q + 1>();
+  }
+}
 
 template <class T>
 __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict__ A,
@@ -37,6 +63,8 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
                                                              T* __restrict__ X, int np) {
   constexpr int E = Traits<T>::E;
   constexpr int KT = K2_KC * E;  // k per stage
+  // MFMA instructions per wave and stage (the fp32 form takes four per 16-byte chunk)
+  constexpr int MFMAS = 16 * (sizeof(T) == 4 ? 4 : 1);
   __shared__ __attribute__((aligned(16))) unsigned char lds[K2_STAGES * K2_STAGE_BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -54,27 +82,33 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
   const size_t mat = (size_t)np * np;
   const T* Ab = A + bc * mat + (size_t)ti * K2_BM * np;
   const T* Bb = B + bc * mat + (size_t)tj * K2_BN * np;
+  // the tile's rows of A and B (at most 256 rows of 32768 elements: within 32 bits)
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc_u32(Ab, (unsigned int)(K2_BM * np * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc_u32(Bb, (unsigned int)(K2_BN * np * sizeof(T)));
 
   // this lane's slot in a 1 KB direct-load block: row lane/4 of the block's 16, position
-  // lane%4, which holds chunk (position ^ swizzle(row)) of the row
+  // lane%4, which holds chunk (position ^ swizzle(row)) of the row. Block q of this wave
+  // is block wave + 4q of the stage (A: 16 blocks, B: 8).
   const int brow = lane >> 2;
-  auto issue = [&](int s) {
+  unsigned int voff[K2_LOADS];
+#pragma unroll
+  for (int q = 0; q < K2_LOADS; ++q) {
+    const int blk = wave + 4 * (q < K2_LOADS_A ? q : q - K2_LOADS_A), row = blk * 16 + brow;
+    const int c = (lane & 3) ^ k2_swizzle(row);
+    voff[q] = (unsigned int)(((size_t)row * np + c * E) * sizeof(T));
+  }
+  auto issue_one = [&](int s, int q) {
     unsigned char* base = lds + (s % K2_STAGES) * K2_STAGE_BYTES;
-    const int k0 = s * KT;
-#pragma unroll
-    for (int q = 0; q < K2_BM / 16 / 4; ++q) {  // A: 16 blocks of 16 rows, 4 per wave
-      const int blk = wave + 4 * q, row = blk * 16 + brow;
-      const int c = (lane & 3) ^ k2_swizzle(row);
-      lds_dma16(Ab + (size_t)row * np + k0 + c * E, base + blk * 1024);
-    }
-#pragma unroll
-    for (int q = 0; q < K2_BN / 16 / 4; ++q) {  // B: 8 blocks, 2 per wave
-      const int blk = wave + 4 * q, row = blk * 16 + brow;
-      const int c = (lane & 3) ^ k2_swizzle(row);
-      lds_dma16(Bb + (size_t)row * np + k0 + c * E, base + K2_A_BYTES + blk * 1024);
-    }
+    const int soff = s * KT * (int)sizeof(T);
+    if (q < K2_LOADS_A)
+      lds_dma16_buf(ra, voff[q], soff, base + (wave + 4 * q) * 1024);
+    else
+      lds_dma16_buf(rb, voff[q], soff, base + K2_A_BYTES + (wave + 4 * (q - K2_LOADS_A)) * 1024);
   };
-  constexpr int LOADS_PER_STAGE = K2_BM / 16 / 4 + K2_BN / 16 / 4;  // per thread
+  auto issue = [&](int s) {
+#pragma unroll
+    for (int q = 0; q < K2_LOADS; ++q) issue_one(s, q);
+  };
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -87,47 +121,66 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
   // operand rows of this lane: i rows wm*128 + mt*32 + lane%32, j rows wn*64 + nt*32 +
   // lane%32; all have the same swizzle (the row bases are multiples of 32)
   const int sw = k2_swizzle(lane & 31);
-  auto compute = [&](int s) {
+  // One stage: all operand reads first, then the MFMAs; with `next` >= 0 the loads of
+  // stage `next` are placed between the MFMAs (sched_group_barrier: 2 or 3 MFMAs, one
+  // load, six times).
+  auto compute = [&](int s, int next) {
     const unsigned char* cur = lds + (s % K2_STAGES) * K2_STAGE_BYTES;
+    chunk_t fa[2][4], fb[2][2];
 #pragma unroll
     for (int step = 0; step < K2_KC / 2; ++step) {
       const int pos = ((2 * step + (lane >> 5)) ^ sw) * 16;
-      chunk_t fa[4], fb[2];
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
-        fa[mt] = ld16(cur + (wm * 128 + mt * 32 + (lane & 31)) * 64 + pos);
+        fa[step][mt] = ld16(cur + (wm * 128 + mt * 32 + (lane & 31)) * 64 + pos);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
-        fb[nt] = ld16(cur + K2_A_BYTES + (wn * 64 + nt * 32 + (lane & 31)) * 64 + pos);
-      // operands swapped: the MFMA produces D[j][i] = x[i][j], so each lane ends up
-      // with runs of 4 consecutive j of one row i.
+        fb[step][nt] = ld16(cur + K2_A_BYTES + (wn * 64 + nt * 32 + (lane & 31)) * 64 + pos);
+    }
+#pragma unroll
+    for (int step = 0; step < K2_KC / 2; ++step)
+      // operands swapped: the MFMA produces D[j][i] = x[i][j], so each lane ends up with
+      // runs of 4 consecutive j of one row i.
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mma32(acc[mt][nt], fb[nt], fa[mt], T());
+        for (int nt = 0; nt < 2; ++nt)
+          acc[mt][nt] = mma32(acc[mt][nt], fb[step][nt], fa[step][mt], T());
+    if (next >= 0) {
+      issue(next);
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // the operand reads
+      mfma_load_groups<MFMAS, K2_LOADS>();
     }
   };
-
-  const int nst = np / KT;  // at least 2: np is a multiple of 256
-  issue(0);
-  issue(1);
-  for (int s = 0; s < nst; ++s) {
-    // this thread's loads of stage s are done once at most the next stage's remain
-    if (s + 1 < nst)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | LOADS_PER_STAGE);  // vmcnt(LOADS_PER_STAGE)
+  // stage s's loads are done once at most the next stage's remain; every wave's part of
+  // stage s is then in LDS after the barrier, and every wave is done with stage s-1, whose
+  // buffer the loads of stage s+2 overwrite. A bare s_barrier: __syncthreads() would also
+  // wait for the stage s+1 loads still in flight. The empty asm statements keep the
+  // compiler from moving LDS accesses across it.
+  // The wait also covers this wave's LDS reads (lgkmcnt(0)), so none of stage s-1 is still
+  // pending when another wave's loads start to overwrite its buffer.
+  auto arrive = [&](bool last) {
+    if (!last)
+      __builtin_amdgcn_s_waitcnt(0x0070 | K2_LOADS);  // vmcnt(K2_LOADS) lgkmcnt(0)
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
-    // every wave's part of stage s is in LDS, and every wave is done with stage s-1,
-    // whose buffer the loads of stage s+2 overwrite (its LDS reads all fed MFMAs, so
-    // they have completed). A bare s_barrier: __syncthreads() would also wait for the
-    // stage s+1 loads still in flight. The empty asm statements keep the compiler from
-    // moving LDS accesses across it.
+      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
-    if (s + 2 < nst) issue(s + 2);
-    compute(s);
+  };
+
+  const int nst = np / KT;  // at least 8: np is a multiple of 256
+  issue(0);
+  issue(1);
+#pragma unroll 1
+  for (int s = 0; s + 2 < nst; ++s) {
+    arrive(false);
+    compute(s, s + 2);
   }
+  arrive(false);
+  compute(nst - 2, -1);
+  arrive(true);
+  compute(nst - 1, -1);
   __syncthreads();  // all waves are done reading the ring before it holds the output
 
   T* Xb = X + bc * mat + (size_t)ti * K2_BM * np + tj * K2_BN;

@@ -20,7 +20,8 @@ ATTENTION_FIELDS = ("ln_gamma", "ln_beta", "w_q", "w_k", "w_v", "w_b", "w_g", "b
 NODES = {"starting": 0, "ending": 1}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtrimul.so")
+# the in-tree build; PAIR_REP_TRIANGLE_LIB names another build of the same library
+LIB_PATH = os.environ.get("PAIR_REP_TRIANGLE_LIB") or os.path.join(_HERE, "libtrimul.so")
 
 TRI_MUL_FP32, TRI_MUL_BF16 = 0, 1
 DIRECTIONS = {"outgoing": 0, "incoming": 1}
