@@ -418,7 +418,7 @@ def measure_peaks(dev):
 class TriMulBench:
     """One workload's modules, buffers and step for the multiplicative update."""
 
-    def __init__(self, name, seed, dev, chained=False):
+    def __init__(self, name, seed, dev, chained=False, skip=False):
         import numpy as np
         import torch
         from pair_rep_triangle_amd.inputs import WORKLOADS, make_weights, make_workload
@@ -440,16 +440,36 @@ class TriMulBench:
         self.outs = [torch.empty_like(self.z) for _ in self.mods]
         self.stream = torch.cuda.current_stream(dev)
         self.chained = chained
+        # with skip, a step first computes the mask extents (once, for both updates) and
+        # both updates skip the contraction past each item's extent
+        self.skip = skip
+        self.extents = torch.empty((self.B, 64), dtype=torch.int32, device=dev)
 
     def step(self):
+        from pair_rep_triangle_amd.trimul import mask_extents
         mods, outs, z, mask, ws = self.mods, self.outs, self.z, self.mask, self.ws
+        ext = mask_extents(mask, out=self.extents) if self.skip else None
         if self.chained:  # z -> outs[0] = z + upd_out(z) -> outs[1] = outs[0] + upd_in(outs[0])
-            mods[0][1].forward_residual(z, mask, out=outs[0], direction="outgoing", workspace=ws)
+            mods[0][1].forward_residual(z, mask, out=outs[0], direction="outgoing", workspace=ws,
+                                        extents=ext)
             mods[1][1].forward_residual(outs[0], mask, out=outs[1], direction="incoming",
-                                        workspace=ws)
+                                        workspace=ws, extents=ext)
             return
         for (direction, mod), out in zip(mods, outs):
-            mod.forward(z, mask, out=out, direction=direction, workspace=ws)
+            mod.forward(z, mask, out=out, direction=direction, workspace=ws, extents=ext)
+
+    def valid_lengths(self):
+        meta = self.d["meta"]
+        if "valid_lengths" in meta:
+            return list(meta["valid_lengths"])
+        return [meta.get("valid_length", self.n)] * self.B
+
+    def useful_flops_per_step(self):
+        """Matmul flops of both directions counted over each item's valid L x L pairs
+        with the contraction over its L residues (the work that remains when padding is
+        skipped)."""
+        from pair_rep_triangle_amd.metrics import flops_per_pair
+        return 2 * sum(L * L * flops_per_pair(L, self.c_z, self.c) for L in self.valid_lengths())
 
     @property
     def pairs(self):
@@ -531,6 +551,7 @@ class TriMulBench:
 
     def summary(self, ms_step, step_samples, kernels):
         import numpy as np
+        self.last_ms = ms_step
         fl = self.flops_per_step()
         rec = {"ms_per_step": round(ms_step, 4),
                "TFLOPs": round(fl / (ms_step * 1e-3) / 1e12, 2),
@@ -548,6 +569,21 @@ class TriMulBench:
     def close(self):
         for _, mod in self.mods:
             mod.close()
+
+
+def skip_summary(wb, args):
+    """The same workload's step with mask-extent skipping: the extents computed once per
+    step, both updates skipping past each item's extent."""
+    wb.skip = True
+    for _ in range(max(args.warmup, 3)):
+        wb.step()
+    ms, _ = timed_steps(wb.step, args.steps, wb.stream)
+    wb.skip = False
+    useful = wb.useful_flops_per_step()
+    return {"skip": {"ms_per_step": round(ms, 4),
+                     "speedup": round(wb.last_ms / ms, 3) if getattr(wb, "last_ms", None) else None,
+                     "useful_TFLOPs": round(useful / (ms * 1e-3) / 1e12, 2),
+                     "valid_lengths": wb.valid_lengths()}}
 
 
 def main():
@@ -590,6 +626,8 @@ def main():
             ms, _ = timed_steps(wb.step, args.steps, wb.stream)
             table[other] = wb.summary(ms, wb.step_times(args.steps),
                                       wb.kernel_report(wb.kernel_times(args.steps)))
+            if wb.spec["mask"] in ("block", "lengths"):
+                table[other].update(skip_summary(wb, args))
             wb.close()
             del wb
             torch.cuda.synchronize()
@@ -647,6 +685,8 @@ def main():
 
     head = hb.summary(ms_step, step_samples, kernels)
     table[name] = dict(head, headline=True)
+    if not args.no_table and hb.spec["mask"] in ("block", "lengths") and not args.chained:
+        table[name].update(skip_summary(hb, args))
     rec = {
         "metric": METRIC, "value": head["TFLOPs"], "unit": "TFLOP/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 4),

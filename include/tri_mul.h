@@ -75,7 +75,7 @@ typedef struct tri_mul_handle tri_mul_handle;
 
 /* Where the intermediates live inside a workspace (byte offsets from its
  * start). a, b and x are each [batch][c][n_pad][n_pad] in the handle's dtype,
- * n_pad = n rounded up to a multiple of 256, entries outside n x n are zero
+ * n_pad = n rounded up to a multiple of 64, entries outside n x n are zero
  * for a and b. For outgoing, a[b][ch][i][k] = a_bik; for incoming the input
  * kernel stores the operands transposed, a[b][ch][i][k] = a_bki (same for b),
  * so the contraction is x[b][ch][i][j] = sum_k a[..][i][k] * b[..][j][k] in
@@ -158,7 +158,7 @@ int tri_mul_forward_residual(tri_mul_handle* h, const void* z, const void* pair_
  * tri_mul_forward.
  *   - Calls whose tri_mul_workspace_bytes(h, batch, n) exceeds the array return
  *     TRI_MUL_ERR_WORKSPACE_TOO_SMALL before any launch (bf16, c = 128: batch * n_pad^2
- *     up to 2^19, e.g. batch 1 with n <= 512).
+ *     up to 349525, e.g. batch 1 with n <= 576).
  *   - Every call on one GPU shares that GPU's array, whatever the handle: calls that may
  *     overlap on one GPU (several streams, several host threads) race on it and must be
  *     ordered by the caller. Nothing needs the array cleared between calls.
@@ -167,6 +167,40 @@ int tri_mul_forward_residual(tri_mul_handle* h, const void* z, const void* pair_
  * Other arguments and errors as for tri_mul_forward. */
 int tri_mul_forward_static(tri_mul_handle* h, const void* z, const void* pair_mask, void* out,
                            int batch, int n, int direction, void* stream);
+
+/* Mask extents, computed once per model forward and reused by every update that shares the
+ * mask (the RFProteína architecture page, "Dual-GEMM gates": the input gate takes the
+ * left-aligned pair mask as per-row valid counts computed once per forward and reused by
+ * all pair updates). For batch item b the extent is
+ *   L_b = 1 + max{ max(i, j) : pair_mask[b][i][j] != 0 },   0 if the item has no nonzero,
+ * the side of the smallest leading square holding every nonzero pair; for the outer
+ * product of a left-aligned residue mask it is the item's valid length.
+ *   pair_mask  [batch][n][n], dtype TRI_MUL_BF16 or TRI_MUL_FP32 (element-aligned)
+ *   extents    [batch][TRI_MUL_EXTENT_PARTS] int32 device memory, 4-byte aligned, must not
+ *              overlap the mask; receives partial maxima (L_b is the largest of its item's
+ *              entries). Fully written by the call: no clearing needed, reusable as is.
+ * Enqueues one small kernel on `stream`. Errors: INVALID_ARG (NULL, sizes), UNSUPPORTED
+ * (dtype), ALIGNMENT, ALIAS, UNSUPPORTED_DEVICE, HIP. */
+#define TRI_MUL_EXTENT_PARTS 64
+int tri_mul_mask_extents(int dtype, const void* pair_mask, int batch, int n, int* extents,
+                         void* stream);
+
+/* tri_mul_forward (residual = 0) or tri_mul_forward_residual (residual = 1) with work
+ * skipping: the contraction of item b runs over k < L_b only (rounded up to its 32-element
+ * stage), and output tiles wholly past L_b run no contraction (their x is zero). The
+ * results equal the plain call's exactly when `extents` are tri_mul_mask_extents of this
+ * pair_mask: outside the leading L_b x L_b square both operands are zero. The input and
+ * output kernels skip the tiles outside that square without reading them, and (as in the
+ * plain call) run no MFMA for tiles whose mask is all zero.
+ *   extents  as written by tri_mul_mask_extents for (pair_mask, batch, n); read only, may
+ *            not overlap out or the workspace (ALIAS); 4-byte aligned.
+ * Other arguments, in-place rules and errors as for tri_mul_forward / _residual, except
+ * that pair_mask is required; INVALID_ARG also for a NULL pair_mask or extents and for
+ * residual outside {0, 1}. With extents, the workspace's a and b are not written outside
+ * each item's leading L_b x L_b square. */
+int tri_mul_forward_extents(tri_mul_handle* h, const void* z, const void* pair_mask,
+                            const int* extents, void* out, int batch, int n, int direction,
+                            int residual, void* workspace, size_t workspace_bytes, void* stream);
 
 /* One kernel of the chain, same arguments as tri_mul_forward:
  *   stage 1: input LayerNorm + gated dual projection + mask -> a, b (workspace)

@@ -215,6 +215,88 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// Maximum over the 64 lanes of a wave (every lane receives it).
+__device__ __forceinline__ int wave_max(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = max(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+// The mask extent of batch item bb (the maximum of its TRI_MUL_EXTENT_PARTS = 64 partial
+// extents, one per lane), clamped to [0, limit]; `limit` when there are no extents.
+// Wave-uniform.
+__device__ __forceinline__ int mask_extent(const int* extents, int bb, int limit) {
+  if (!extents) return limit;
+  int v = wave_max(extents[bb * 64 + (int)(threadIdx.x & 63)]);
+  v = __builtin_amdgcn_readfirstlane(v);
+  return v < 0 ? 0 : (v > limit ? limit : v);
+}
+
+// The bound of batch item bb for a persistent wave that visits items in order: the item's
+// mask extent (re-read only when the item changes), or n without extents. Wave-uniform.
+struct ExtentCache {
+  int bb = -1, ext = 0;
+};
+__device__ __forceinline__ int item_bound(const int* extents, int bb, int n, ExtentCache& c) {
+  if (!extents) return n;
+  if (bb != c.bb) {
+    c.ext = mask_extent(extents, bb, n);
+    c.bb = bb;
+  }
+  return c.ext;
+}
+
+// The tiles inside each item's leading L_b x L_b square (L_b its mask extent), numbered
+// item by item, row by row, `tw`-pair column tiles within a row: the work list of a
+// persistent wave when padding is skipped, so that every wave gets an equal share of the
+// tiles that are left. A wave visits its tiles in increasing order; the cursor keeps the
+// item the last lookup landed in. Wave-uniform.
+struct ActiveTiles {
+  const int* extents;
+  int n, batch, tw;
+  int cb, cbase, ccount, cntw;  // cursor: item cb's tiles start at index cbase
+  __device__ __forceinline__ void load(int b) {
+    const int L = mask_extent(extents, b, n);
+    cntw = (L + tw - 1) / tw;
+    ccount = L * cntw;
+  }
+  __device__ __forceinline__ void init(const int* e, int n_, int batch_, int tw_) {
+    extents = e;
+    n = n_;
+    batch = batch_;
+    tw = tw_;
+    cb = 0;
+    cbase = 0;
+    load(0);
+  }
+  // the number of tiles over all items
+  __device__ __forceinline__ int total() {
+    int sum = 0;
+    for (int b = 0; b < batch; ++b) {
+      const int L = mask_extent(extents, b, n);
+      sum += L * ((L + tw - 1) / tw);
+    }
+    return sum;
+  }
+  // tile t -> item bb, row r, first column s0 (t below total())
+  __device__ __forceinline__ void at(int t, int& bb, int& r, int& s0) {
+    if (t < cbase) {
+      cb = 0;
+      cbase = 0;
+      load(0);
+    }
+    while (t >= cbase + ccount && cb + 1 < batch) {
+      cbase += ccount;
+      ++cb;
+      load(cb);
+    }
+    const int l = t - cbase;
+    r = cntw > 0 ? l / cntw : 0;
+    s0 = (l - r * cntw) * tw;
+    bb = cb;
+  }
+};
+
 // Orders this wave's earlier LDS writes before its later LDS reads of other lanes' data
 // (LDS operations of one wave are executed in issue order; the fences stop the compiler
 // from moving accesses across this point and wait for the writes to complete).

@@ -296,7 +296,8 @@ template <class T>
 __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     const T* __restrict__ z, const T* __restrict__ mask, T* __restrict__ a_out,
     T* __restrict__ b_out, const chunk_t* __restrict__ image, int n, int np, int cz, int c,
-    int incoming, int mask_all, int ug, int total_tiles) {
+    int incoming, int mask_all, int ug, int total_tiles, const int* __restrict__ extents,
+    int compact) {
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int KZ = 4;               // chunk groups along c_z
@@ -321,8 +322,20 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   const int arow = 16 * (p >> 2) + (p & 3);  // tile pair of A row p in subtile 0 (+4 per st)
 
   // tile t -> (bb, r, sx): storage row r, columns sx*64 .. +63; the z pairs are (r, s)
-  // outgoing and (s, r) incoming
+  // outgoing and (s, r) incoming. With `compact` (mask extents, few items) the tiles are
+  // those inside each item's extent only, so every wave gets an equal share of the work
+  // that is left.
+  ActiveTiles sched;
+  if (compact) {
+    sched.init(extents, n, total_tiles / (np * ntx), K1W_TP);
+    total_tiles = sched.total();
+    if (total_tiles == 0) return;  // workgroup-uniform: no item has a valid pair
+  }
   auto coords = [&](int t, int& bb, int& r, int& s0) {
+    if (compact) {
+      sched.at(t, bb, r, s0);
+      return;
+    }
     bb = t / (np * ntx);
     const int rem = t - bb * np * ntx;
     r = rem / ntx;
@@ -346,13 +359,18 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   // byte sizes below 2^31: this form runs only where one batch item of z is under 2 GiB
   const unsigned int zstep = (unsigned int)(4 * pstride * cz * sizeof(T));
   const unsigned int mstep = (unsigned int)(4 * pstride * sizeof(T));
+  // With mask extents, a tile outside its item's leading L x L square is inactive: its
+  // loads read nothing (zero extents), it writes nothing (the contraction reads no operand
+  // row or column past L), and the pairs of an active tile past L count as masked.
+  ExtentCache ecache;
   auto fetch = [&](int t, Pre& f) {
     int bb, r, s0;
     coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);  // waves past the end refetch
-    const bool row_ok = r < n && s0 < n;
+    const int lim = item_bound(extents, bb, n, ecache);
+    const bool row_ok = r < lim && s0 < lim;
     const size_t p0 = row_ok ? (incoming ? ((size_t)bb * n + s0) * n + r : ((size_t)bb * n + r) * n + s0) : 0;
     // pairs of the storage row from the tile's first one to the last real one
-    const unsigned int span = row_ok ? (unsigned int)(n - s0 - 1) * (unsigned int)pstride + 1 : 0u;
+    const unsigned int span = row_ok ? (unsigned int)(lim - s0 - 1) * (unsigned int)pstride + 1 : 0u;
     const unsigned int zext = span * (unsigned int)(cz * sizeof(T));
     const unsigned int mext = span * (unsigned int)sizeof(T);
 #pragma unroll
@@ -395,16 +413,18 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   // so its waits count only those.
   chunk_t za[ST][KZ];
   f32x4 m4[ST];
-  bool ones = false;  // every mask value of the tile is 1 (wave-uniform)
+  bool ones = false;   // every mask value of the tile is 1 (wave-uniform)
+  bool zeros = false;  // every mask value of the tile is 0: its outputs are zero
   auto prepare = [&](int t) {
     int bb, r, s0;
     coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);
+    const int lim = item_bound(extents, bb, n, ecache);
     int opaque;  // keeps the loop-invariant masks inside the loop
     asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
     float mv[ST];
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
-      const unsigned int okm = 0u - (unsigned int)(r < n && s0 + arow + 4 * st < n);
+      const unsigned int okm = 0u - (unsigned int)(r < lim && s0 + arow + 4 * st < lim);
       mv[st] = __uint_as_float(__float_as_uint(to_f32(f.m[st])) & okm);
 #pragma unroll
       for (int ks = 0; ks < KZ; ++ks) {
@@ -417,6 +437,7 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
 #pragma unroll
     for (int st = 0; st < ST; ++st) mb[st * 16 + p] = mv[st];
     ones = __all(mv[0] == 1.f && mv[1] == 1.f && mv[2] == 1.f && mv[3] == 1.f);
+    zeros = __all(mv[0] == 0.f && mv[1] == 0.f && mv[2] == 0.f && mv[3] == 0.f);
     wave_lds_sync();
 #pragma unroll
     for (int st = 0; st < ST; ++st) m4[st] = ld16f(mb + st * 16 + 4 * q);
@@ -560,10 +581,20 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
       fetch(t + nw, f);  // za is dead: the next tile's z loads go out now
       emit(unit_dst(ug - 1), accb, masked);
     };
-    if (ones)
+    const int lim = item_bound(extents, bb, n, ecache);
+    if (extents && !(r < lim && s0 < lim)) {
+      fetch(t + nw, f);  // inactive (outside the item's extent): nothing to compute or write
+    } else if (zeros) {
+      // a tile wholly outside the mask: no MFMA and no epilogue, its unit rows are zeros
+      fetch(t + nw, f);
+      const float zo[16] = {};
+#pragma unroll 1
+      for (int uu = 0; uu < ug; ++uu) store16(unit_dst(uu), zo);
+    } else if (ones) {
       run_units(std::false_type{});
-    else
+    } else {
       run_units(std::true_type{});
+    }
     prepare(t + nw);
     ++done;
   }
@@ -605,7 +636,7 @@ static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
   hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K1W_THREADS), lds, st, (const T*)a.z,
                      (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b,
                      (const chunk_t*)a.k1w_image, a.n, a.np, a.cz, a.c, a.incoming, mask_all, ug,
-                     total);
+                     total, a.extents, a.extents && a.batch <= COMPACT_MAX_ITEMS ? 1 : 0);
   *done = true;
   return hipGetLastError();
 }

@@ -22,9 +22,8 @@ namespace trimul {
 // c ^ ((r ^ (r >> 2)) & 3), which keeps the MFMA operand reads free of bank conflicts
 // (checked for both 32- and 64-bank LDS). The output tile is staged in LDS and leaves as
 // 16-byte row-contiguous stores.
-// Flat grid of (np/256) * (np/128) * batch*c workgroups, remapped so that consecutive
-// tiles of one channel land on the same XCD (workgroup ids are dealt round-robin over the
-// 8 XCDs) and share its L2.
+// Flat grid of ceil(np/256) * ceil(np/128) * batch*c workgroups, remapped so that the
+// tiles of one channel land on the same XCD and share its L2.
 constexpr int K2_BM = 256, K2_BN = 128;
 constexpr int K2_THREADS = 256;
 constexpr int K2_STAGES = 3;
@@ -34,7 +33,7 @@ constexpr int K2_B_BYTES = K2_BN * K2_KC * 16;             // 8 KB
 constexpr int K2_STAGE_BYTES = K2_A_BYTES + K2_B_BYTES;    // 24 KB
 constexpr int K2_LOADS_A = K2_BM / 16 / 4;                 // per thread and stage: 4
 constexpr int K2_LOADS = K2_LOADS_A + K2_BN / 16 / 4;      // 6
-static_assert(N_PAD % K2_BM == 0 && N_PAD % K2_BN == 0, "padded side covers whole tiles");
+static_assert(N_PAD % 64 == 0, "operand rows of whole 128-byte lines; 64-pair input tiles");
 
 __device__ __forceinline__ int k2_swizzle(int r) { return (r ^ (r >> 2)) & 3; }
 
@@ -57,10 +56,18 @@ __device__ __forceinline__ void mfma_load_groups() {
   }
 }
 
+// The operands are zero past row and column n (and, with mask extents from k0, past each
+// item's extent L_b, inside which every nonzero pair lies): the k loop stops at that bound
+// rounded up to a stage, the operand rows past it are not read (the buffer resources end
+// there, so their loads return zeros), and a tile that lies wholly past it runs no stage
+// and stores zeros. The padded side np is a multiple of 64, not of the tile: the last tile
+// row and column may be partial, and their stores past np are dropped.
 template <class T>
 __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict__ A,
                                                              const T* __restrict__ B,
-                                                             T* __restrict__ X, int np) {
+                                                             T* __restrict__ X, int n, int np,
+                                                             const int* __restrict__ extents,
+                                                             int c) {
   constexpr int E = Traits<T>::E;
   constexpr int KT = K2_KC * E;  // k per stage
   // MFMA instructions per wave and stage (the fp32 form takes four per 16-byte chunk)
@@ -71,20 +78,29 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
 
-  const int bid = blockIdx.x, total = gridDim.x;
-  const int per = total >> 3;
-  const int logical = bid < (per << 3) ? (bid & 7) * per + (bid >> 3) : bid;
-  const int tn = np / K2_BN;
-  const int tiles = (np / K2_BM) * tn;
-  const int bc = logical / tiles, tile = logical - bc * tiles;
+  // Workgroup ids are dealt round-robin over the 8 XCDs: XCD x runs ids x, x + 8, ...
+  // Its k-th workgroup takes tile k % tiles of channel plane 8 (k / tiles) + x, so the tiles
+  // of one plane stay on one XCD (sharing its L2) and every XCD holds planes of every batch
+  // item (B * c is a multiple of 16), which keeps the XCDs evenly loaded when items differ
+  // in extent.
+  const int bid = blockIdx.x;
+  const int tn = (np + K2_BN - 1) / K2_BN;
+  const int tiles = ((np + K2_BM - 1) / K2_BM) * tn;
+  const int xcd = bid & 7, k = bid >> 3;
+  const int bc = (k / tiles) * 8 + xcd, tile = k - (k / tiles) * tiles;
   const int ti = tile / tn, tj = tile - ti * tn;
 
+  // the bound past which both operands are zero: the item's extent, else n
+  const int ext = extents ? mask_extent(extents, bc / c, n) : n;
   const size_t mat = (size_t)np * np;
   const T* Ab = A + bc * mat + (size_t)ti * K2_BM * np;
   const T* Bb = B + bc * mat + (size_t)tj * K2_BN * np;
-  // the tile's rows of A and B (at most 256 rows of 32768 elements: within 32 bits)
-  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc_u32(Ab, (unsigned int)(K2_BM * np * sizeof(T)));
-  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc_u32(Bb, (unsigned int)(K2_BN * np * sizeof(T)));
+  // the tile's rows of A and B that lie inside the bound (at most 256 rows of 32768
+  // elements: within 32 bits); loads of the rows past them return zeros
+  const int rows_a = min(max(ext - ti * K2_BM, 0), K2_BM);
+  const int rows_b = min(max(ext - tj * K2_BN, 0), K2_BN);
+  const __amdgpu_buffer_rsrc_t ra = buffer_rsrc_u32(Ab, (unsigned int)(rows_a * np * sizeof(T)));
+  const __amdgpu_buffer_rsrc_t rb = buffer_rsrc_u32(Bb, (unsigned int)(rows_b * np * sizeof(T)));
 
   // this lane's slot in a 1 KB direct-load block: row lane/4 of the block's 16, position
   // lane%4, which holds chunk (position ^ swizzle(row)) of the row. Block q of this wave
@@ -169,18 +185,26 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
     asm volatile("" ::: "memory");
   };
 
-  const int nst = np / KT;  // at least 8: np is a multiple of 256
-  issue(0);
-  issue(1);
+  // stages of the k loop: up to the bound rounded up to a stage (np is a multiple of the
+  // stage), none when the tile lies past the bound
+  const int nst = (rows_a == 0 || rows_b == 0) ? 0 : (ext + KT - 1) / KT;
+  if (nst >= 2) {
+    issue(0);
+    issue(1);
 #pragma unroll 1
-  for (int s = 0; s + 2 < nst; ++s) {
+    for (int s = 0; s + 2 < nst; ++s) {
+      arrive(false);
+      compute(s, s + 2);
+    }
     arrive(false);
-    compute(s, s + 2);
+    compute(nst - 2, -1);
+    arrive(true);
+    compute(nst - 1, -1);
+  } else if (nst == 1) {
+    issue(0);
+    arrive(true);
+    compute(0, -1);
   }
-  arrive(false);
-  compute(nst - 2, -1);
-  arrive(true);
-  compute(nst - 1, -1);
   __syncthreads();  // all waves are done reading the ring before it holds the output
 
   T* Xb = X + bc * mat + (size_t)ti * K2_BM * np + tj * K2_BN;
@@ -202,13 +226,17 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
         }
     __syncthreads();
     constexpr int CPR = K2_BN / E;
+    // the tile's part inside the padded plane (a partial last tile row or column)
+    const int vrows = min(np - ti * K2_BM, K2_BM), vchunks = min(np - tj * K2_BN, K2_BN) / E;
 #pragma unroll 4
     for (int idx = tid; idx < K2_BM * CPR; idx += K2_THREADS) {
       const int row = idx / CPR, cc = idx - row * CPR;
-      st16(Xb + (size_t)row * np + cc * E, ld16(xs + row * XROW + cc * E));
+      if (row < vrows && cc < vchunks)
+        st16(Xb + (size_t)row * np + cc * E, ld16(xs + row * XROW + cc * E));
     }
   } else {
-    // fp32: four consecutive j per lane are one 16-byte store
+    // fp32: four consecutive j per lane are one 16-byte store (inside the padded plane)
+    const int vrows = min(np - ti * K2_BM, K2_BM), vcols = min(np - tj * K2_BN, K2_BN);
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -217,24 +245,25 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
         for (int q = 0; q < 4; ++q) {
           const int i = wm * 128 + mt * 32 + (lane & 31);
           const int j = wn * 64 + nt * 32 + 8 * q + 4 * (lane >> 5);
-          store4(Xb + (size_t)i * np + j, acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1],
-                 acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
+          if (i < vrows && j < vcols)
+            store4(Xb + (size_t)i * np + j, acc[mt][nt][4 * q], acc[mt][nt][4 * q + 1],
+                   acc[mt][nt][4 * q + 2], acc[mt][nt][4 * q + 3]);
         }
   }
 }
 
 size_t k2_grid(int np, int batch, int c) {
-  return (size_t)(np / K2_BM) * (np / K2_BN) * batch * c;
+  return (size_t)((np + K2_BM - 1) / K2_BM) * ((np + K2_BN - 1) / K2_BN) * batch * c;
 }
 
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st) {
   dim3 grid((unsigned)k2_grid(a.np, a.batch, a.c));
   if (bf16_storage)
     hipLaunchKernelGGL(k2_contract<bf16>, grid, dim3(K2_THREADS), 0, st, (const bf16*)a.a,
-                       (const bf16*)a.b, (bf16*)a.x, a.np);
+                       (const bf16*)a.b, (bf16*)a.x, a.n, a.np, a.extents, a.c);
   else
     hipLaunchKernelGGL(k2_contract<float>, grid, dim3(K2_THREADS), 0, st, (const float*)a.a,
-                       (const float*)a.b, (float*)a.x, a.np);
+                       (const float*)a.b, (float*)a.x, a.n, a.np, a.extents, a.c);
   return hipGetLastError();
 }
 

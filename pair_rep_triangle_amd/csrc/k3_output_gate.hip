@@ -209,6 +209,10 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
     const T* xs = xbuf(cur);
     const T* zs = zbuf(cur);
     const float* mv = mvbuf + cur * TP;
+    // a tile wholly outside the mask runs no MFMA: with m = 0 the finite start values give
+    // a zero update (its x is never read)
+    static_assert(TP == 64, "one mask value per lane");
+    const bool skip = __all(mv[lane] == 0.f);
 #pragma unroll
     for (int pt = 0; pt < TP / 16; ++pt) {
       f32x4 ap[UPW], ag[UPW];
@@ -220,17 +224,19 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
       const int pr = pt * 16 + (lane & 15);  // B-operand column = pair
       const T* xr = xs + pr * xstride + (lane >> 4) * E;
       const T* zr = zs + pr * zstride + (lane >> 4) * E;
+      if (!skip) {
 #pragma unroll
-      for (int ks = 0; ks < KXM; ++ks) {
-        const chunk_t xf = ld16(xr + ks * KG);
+        for (int ks = 0; ks < KXM; ++ks) {
+          const chunk_t xf = ld16(xr + ks * KG);
 #pragma unroll
-        for (int jj = 0; jj < UPW; ++jj) ap[jj] = mma16(ap[jj], wor[jj][ks], xf, T());
-      }
+          for (int jj = 0; jj < UPW; ++jj) ap[jj] = mma16(ap[jj], wor[jj][ks], xf, T());
+        }
 #pragma unroll
-      for (int ks = 0; ks < KZM; ++ks) {
-        const chunk_t zf = ld16(zr + ks * KG);
+        for (int ks = 0; ks < KZM; ++ks) {
+          const chunk_t zf = ld16(zr + ks * KG);
 #pragma unroll
-        for (int jj = 0; jj < UPW; ++jj) ag[jj] = mma16(ag[jj], wgr[jj][ks], zf, T());
+          for (int jj = 0; jj < UPW; ++jj) ag[jj] = mma16(ag[jj], wgr[jj][ks], zf, T());
+        }
       }
       const int j = j0 + pr;
       const float m = mv[pr];
@@ -279,7 +285,8 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     const T* __restrict__ x, ZIn<T, RESID> z, const T* __restrict__ mask, ZOut<T, RESID> out,
     const T* __restrict__ wo, const float* __restrict__ to,
     const T* __restrict__ wg, const float* __restrict__ tg, int n, int np, int cz, int czp, int c,
-    int cp, int mask_all, int ug, int total_tiles) {
+    int cp, int mask_all, int ug, int total_tiles, const int* __restrict__ extents,
+    int compact) {
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int THREADS = 64 * W;
@@ -375,17 +382,42 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     }
     moff[st] = mask_all ? 0u : (unsigned int)((st * 16 + p) * sizeof(T));
   }
+  // With mask extents, the pairs past the item's extent L read as zero (mask 0) and a
+  // tile outside the leading L x L square reads nothing: it is a zero update (skipped).
+  // With `compact` (few items) the tile list holds only the tiles inside the extents, so
+  // the remaining work is shared evenly; the outputs of the pairs outside are written by
+  // k3_fill_outside.
+  ExtentCache ecache;
+  ActiveTiles sched;
+  if (compact) {
+    sched.init(extents, n, total_tiles / (n * ntw), TW);
+    total_tiles = sched.total();
+    if (total_tiles == 0) return;  // no item has a valid pair (no barrier follows)
+  }
+  auto coords = [&](int t, int& bb, int& i, int& j0) {
+    if (compact) {
+      sched.at(t, bb, i, j0);
+      return;
+    }
+    bb = t / (n * ntw);
+    const int rem = t - bb * n * ntw;
+    i = rem / ntw;
+    j0 = (rem - i * ntw) * TW;
+  };
   auto fetch = [&](int t, Pre& f) {
     t = t < total_tiles ? t : total_tiles - 1;  // waves without a tile fetch the last one
-    const int bb = t / (n * ntw);
-    const int rem = t - bb * n * ntw;
-    const int i = rem / ntw, j0 = (rem - i * ntw) * TW;
-    const size_t xext = (size_t)c * plane * sizeof(T);  // below 2^31 (checked at launch)
+    int bb, i, j0;
+    coords(t, bb, i, j0);
+    const int lim = item_bound(extents, bb, n, ecache);
+    const bool act = i < lim && j0 < lim;
+    const size_t xext = act ? (size_t)c * plane * sizeof(T) : 0;  // below 2^31 (launch check)
     const __amdgpu_buffer_rsrc_t rx = buffer_rsrc(x + (size_t)bb * c * plane, xext);
     const size_t row0 = ((size_t)bb * n + i) * n + j0;  // first pair of the tile
-    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(z + row0 * cz, (size_t)(n - j0) * cz * sizeof(T));
+    const size_t live = act ? (size_t)(lim - j0) : 0;    // pairs of the tile that are read
+    const __amdgpu_buffer_rsrc_t rz = buffer_rsrc(z + row0 * cz, live * cz * sizeof(T));
     const __amdgpu_buffer_rsrc_t rm =
-        buffer_rsrc(mask_all ? mask : mask + row0, mask_all ? sizeof(T) : (size_t)(n - j0) * sizeof(T));
+        buffer_rsrc(mask_all ? mask : mask + row0,
+                    mask_all ? (act ? sizeof(T) : 0) : live * sizeof(T));
     const int xs = (int)(((size_t)i * np + j0) * sizeof(T));
 #pragma unroll
     for (int k = 0; k < XBM; ++k)
@@ -405,144 +437,152 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
   Pre f;
   fetch(t, f);
   for (; t < total_tiles; t += nw) {
-    const int bb = t / (n * ntw);
-    const int rem = t - bb * n * ntw;
-    const int i = rem / ntw, j0 = (rem - i * ntw) * TW;
-
-    // x: transpose the XBC x E blocks into pair-major staging rows. Every lane stores (no
-    // predicated-off memory operations in the loop): a lane without a block writes its
-    // junk into the last E columns of the rows, which nothing reads.
-#pragma unroll
-    for (int k = 0; k < XBM; ++k) {
-      const int blk = lane + 64 * k;
-      const bool real = blk < xblocks;
-      const int bl = real ? blk : 0;
-      const int o = bl / cbn, cb = bl - o * cbn;
-      const int col0 = real ? cb * XBC : sst - E;
-      T tb[XBC][E];
-#pragma unroll
-      for (int e = 0; e < XBC; ++e) {
-        const T* pv = (const T*)&f.xv[k][e];
-#pragma unroll
-        for (int ff = 0; ff < E; ++ff) tb[e][ff] = pv[ff];
-      }
-#pragma unroll
-      for (int ff = 0; ff < E; ++ff) {
-        if constexpr (XBC == E) {
-          T col[E];
-#pragma unroll
-          for (int e = 0; e < E; ++e) col[e] = tb[e][ff];
-          st16(stg + (o * E + ff) * sst + col0, __builtin_bit_cast(chunk_t, col));
-        } else {
-          static_assert(XBC * 2 == E, "half-width x blocks");
-          T col[XBC];
-#pragma unroll
-          for (int e = 0; e < XBC; ++e) col[e] = tb[e][ff];
-          *(half_t*)(stg + (o * E + ff) * sst + col0) = __builtin_bit_cast(half_t, col);
-        }
-      }
-    }
-    // The weight and start-vector addresses and the padding masks are the same in every
-    // tile; an opaque zero, produced anew each tile, keeps the compiler from hoisting them
-    // out of the tile loop (which would pin all of them in registers for the whole launch).
-    int opaque;
-    asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
-    chunk_t bx[ST][KXM], bz[ST][KZM];
+    int bb, i, j0;
+    coords(t, bb, i, j0);
     float mrow[ST];
+    bool ones = true, none = true;
 #pragma unroll
     for (int st = 0; st < ST; ++st) {
-#pragma unroll
-      for (int ks = 0; ks < KZM; ++ks) bz[st][ks] = f.zv[st][ks];
       mrow[st] = j0 + st * 16 + p < n ? to_f32(f.m[st]) : 0.f;
+      ones = ones && mrow[st] == 1.f;
+      none = none && mrow[st] == 0.f;
     }
-    wave_lds_sync();
+    // a tile wholly outside the mask: zero update, no x transpose, LayerNorm or MFMA (its
+    // x is never read)
+    const bool skip = __all(none);
+    if (skip) {
+      fetch(t + nw < total_tiles ? t + nw : t, f);
+    } else {
+      // x: transpose the XBC x E blocks into pair-major staging rows. Every lane stores (no
+      // predicated-off memory operations in the loop): a lane without a block writes its
+      // junk into the last E columns of the rows, which nothing reads.
 #pragma unroll
-    for (int st = 0; st < ST; ++st)
+      for (int k = 0; k < XBM; ++k) {
+        const int blk = lane + 64 * k;
+        const bool real = blk < xblocks;
+        const int bl = real ? blk : 0;
+        const int o = bl / cbn, cb = bl - o * cbn;
+        const int col0 = real ? cb * XBC : sst - E;
+        T tb[XBC][E];
 #pragma unroll
-      for (int ks = 0; ks < KXM; ++ks) bx[st][ks] = ld16(stg + (st * 16 + p) * sst + ks * KG + q * E);
-    // widths that do not fill the compiled chunk count: zero the chunks past the real
-    // channels (a wave-uniform branch, not taken at full width)
-    if (c < cp || cz < czp) {
-      const int ch0q = q * E + opaque;
+        for (int e = 0; e < XBC; ++e) {
+          const T* pv = (const T*)&f.xv[k][e];
 #pragma unroll
-      for (int ks = 0; ks < KXM; ++ks) {
-        const unsigned int kx = ks * KG + ch0q < c ? ~0u : 0u;
+          for (int ff = 0; ff < E; ++ff) tb[e][ff] = pv[ff];
+        }
 #pragma unroll
-        for (int st = 0; st < ST; ++st) bx[st][ks] &= kx;
-      }
+        for (int ff = 0; ff < E; ++ff) {
+          if constexpr (XBC == E) {
+            T col[E];
 #pragma unroll
-      for (int ks = 0; ks < KZM; ++ks) {
-        const unsigned int kz = ks * KG + ch0q < cz ? ~0u : 0u;
+            for (int e = 0; e < E; ++e) col[e] = tb[e][ff];
+            st16(stg + (o * E + ff) * sst + col0, __builtin_bit_cast(chunk_t, col));
+          } else {
+            static_assert(XBC * 2 == E, "half-width x blocks");
+            T col[XBC];
 #pragma unroll
-        for (int st = 0; st < ST; ++st) bz[st][ks] &= kz;
-      }
-    }
-
-    // the next tile's loads are in flight from here on (the last tile refetches itself)
-    fetch(t + nw < total_tiles ? t + nw : t, f);
-
-#pragma unroll
-    for (int st = 0; st < ST; ++st) {
-      normalize_operand_row<KXM>(bx[st], c, lane, T());
-      normalize_operand_row<KZM>(bz[st], cz, lane, T());
-    }
-
-    // units of this group (a rolled loop: unrolled, the scheduler overlaps the units' LDS
-    // reads beyond the register budget). Tiles whose pairs all have mask 1 skip the
-    // multiply by m (a wave-uniform branch).
-    const T* const wo_t = wo_s + opaque;
-    const T* const wg_t = wg_s + opaque;
-    const float* const to_t = to_s + opaque;
-    const float* const tg_t = tg_s + opaque;
-    auto units = [&](auto masked) {
-      constexpr bool MASKED = decltype(masked)::value;
-#pragma unroll 1
-      for (int u = 0; u < ug; ++u) {
-        {
-          const int r0 = u * 16;
-          const f32x4 bo4 = ld16f(to_t + r0 + 4 * q), bg4 = ld16f(tg_t + r0 + 4 * q);
-          f32x4 ap[ST], ag[ST];
-#pragma unroll
-          for (int st = 0; st < ST; ++st) {
-            ap[st] = bo4;
-            ag[st] = bg4;
-          }
-          // all of the unit's weight chunks are requested before the first MFMA, so the
-          // LDS latency is paid once per unit rather than once per chunk
-          const T* wor = wo_t + (r0 + p) * wos + q * E;
-          const T* wgr = wg_t + (r0 + p) * wgs + q * E;
-          chunk_t wa[KXM], wb[KZM];
-#pragma unroll
-          for (int ks = 0; ks < KXM; ++ks) wa[ks] = ld16(wor + ks * KG);
-#pragma unroll
-          for (int ks = 0; ks < KZM; ++ks) wb[ks] = ld16(wgr + ks * KG);
-#pragma unroll
-          for (int ks = 0; ks < KXM; ++ks)
-#pragma unroll
-            for (int st = 0; st < ST; ++st) ap[st] = mma16(ap[st], wa[ks], bx[st][ks], T());
-#pragma unroll
-          for (int ks = 0; ks < KZM; ++ks)
-#pragma unroll
-            for (int st = 0; st < ST; ++st) ag[st] = mma16(ag[st], wb[ks], bz[st][ks], T());
-          // accumulator register r <-> output channel ch0 + r0 + 4q + r of pair st*16 + p
-#pragma unroll
-          for (int st = 0; st < ST; ++st) {
-            float o4[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-              o4[r] = gate_mul(MASKED ? ap[st][r] * mrow[st] : ap[st][r], ag[st][r]);
-            store4(stg + (st * 16 + p) * sst + r0 + 4 * q, o4[0], o4[1], o4[2], o4[3]);
+            for (int e = 0; e < XBC; ++e) col[e] = tb[e][ff];
+            *(half_t*)(stg + (o * E + ff) * sst + col0) = __builtin_bit_cast(half_t, col);
           }
         }
       }
-    };
-    bool ones = true;
+      // The weight and start-vector addresses and the padding masks are the same in every
+      // tile; an opaque zero, produced anew each tile, keeps the compiler from hoisting them
+      // out of the tile loop (which would pin all of them in registers for the whole launch).
+      int opaque;
+      asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
+      chunk_t bx[ST][KXM], bz[ST][KZM];
 #pragma unroll
-    for (int st = 0; st < ST; ++st) ones = ones && mrow[st] == 1.f;
-    if (__all(ones))
-      units(std::false_type());
-    else
-      units(std::true_type());
+      for (int st = 0; st < ST; ++st)
+#pragma unroll
+        for (int ks = 0; ks < KZM; ++ks) bz[st][ks] = f.zv[st][ks];
+      wave_lds_sync();
+#pragma unroll
+      for (int st = 0; st < ST; ++st)
+#pragma unroll
+        for (int ks = 0; ks < KXM; ++ks)
+          bx[st][ks] = ld16(stg + (st * 16 + p) * sst + ks * KG + q * E);
+      // widths that do not fill the compiled chunk count: zero the chunks past the real
+      // channels (a wave-uniform branch, not taken at full width)
+      if (c < cp || cz < czp) {
+        const int ch0q = q * E + opaque;
+#pragma unroll
+        for (int ks = 0; ks < KXM; ++ks) {
+          const unsigned int kx = ks * KG + ch0q < c ? ~0u : 0u;
+#pragma unroll
+          for (int st = 0; st < ST; ++st) bx[st][ks] &= kx;
+        }
+#pragma unroll
+        for (int ks = 0; ks < KZM; ++ks) {
+          const unsigned int kz = ks * KG + ch0q < cz ? ~0u : 0u;
+#pragma unroll
+          for (int st = 0; st < ST; ++st) bz[st][ks] &= kz;
+        }
+      }
+
+      // the next tile's loads are in flight from here on (the last tile refetches itself)
+      fetch(t + nw < total_tiles ? t + nw : t, f);
+
+#pragma unroll
+      for (int st = 0; st < ST; ++st) {
+        normalize_operand_row<KXM>(bx[st], c, lane, T());
+        normalize_operand_row<KZM>(bz[st], cz, lane, T());
+      }
+
+      // units of this group (a rolled loop: unrolled, the scheduler overlaps the units' LDS
+      // reads beyond the register budget). Tiles whose pairs all have mask 1 skip the
+      // multiply by m (a wave-uniform branch).
+      const T* const wo_t = wo_s + opaque;
+      const T* const wg_t = wg_s + opaque;
+      const float* const to_t = to_s + opaque;
+      const float* const tg_t = tg_s + opaque;
+      auto units = [&](auto masked) {
+        constexpr bool MASKED = decltype(masked)::value;
+#pragma unroll 1
+        for (int u = 0; u < ug; ++u) {
+          {
+            const int r0 = u * 16;
+            const f32x4 bo4 = ld16f(to_t + r0 + 4 * q), bg4 = ld16f(tg_t + r0 + 4 * q);
+            f32x4 ap[ST], ag[ST];
+#pragma unroll
+            for (int st = 0; st < ST; ++st) {
+              ap[st] = bo4;
+              ag[st] = bg4;
+            }
+            // all of the unit's weight chunks are requested before the first MFMA, so the
+            // LDS latency is paid once per unit rather than once per chunk
+            const T* wor = wo_t + (r0 + p) * wos + q * E;
+            const T* wgr = wg_t + (r0 + p) * wgs + q * E;
+            chunk_t wa[KXM], wb[KZM];
+#pragma unroll
+            for (int ks = 0; ks < KXM; ++ks) wa[ks] = ld16(wor + ks * KG);
+#pragma unroll
+            for (int ks = 0; ks < KZM; ++ks) wb[ks] = ld16(wgr + ks * KG);
+#pragma unroll
+            for (int ks = 0; ks < KXM; ++ks)
+#pragma unroll
+              for (int st = 0; st < ST; ++st) ap[st] = mma16(ap[st], wa[ks], bx[st][ks], T());
+#pragma unroll
+            for (int ks = 0; ks < KZM; ++ks)
+#pragma unroll
+              for (int st = 0; st < ST; ++st) ag[st] = mma16(ag[st], wb[ks], bz[st][ks], T());
+            // accumulator register r <-> output channel ch0 + r0 + 4q + r of pair st*16 + p
+#pragma unroll
+            for (int st = 0; st < ST; ++st) {
+              float o4[4];
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                o4[r] = gate_mul(MASKED ? ap[st][r] * mrow[st] : ap[st][r], ag[st][r]);
+              store4(stg + (st * 16 + p) * sst + r0 + 4 * q, o4[0], o4[1], o4[2], o4[3]);
+            }
+          }
+        }
+      };
+      if (__all(ones))
+        units(std::false_type());
+      else
+        units(std::true_type());
+    }  // not skipped
 
     // staging -> out: the group's channel range of TW consecutive pairs. The number of
     // stores is fixed and none is predicated off: a lane whose chunk lies past the row end
@@ -570,6 +610,8 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     // The output is the last thing the update writes and nothing in the update reads it
     // again: non-temporal stores keep it from displacing x and z in the caches (K3 took
     // 52.7 instead of 55.2 us at N = 512, c_z = c = 128).
+    // a skipped tile's update is zero: its staging rows are not read
+    const chunk_t zero = {0u, 0u, 0u, 0u};
     if constexpr (RESID) {
       // out = z + update. Every z chunk is read before any chunk is written, so the
       // duplicate stores past the row end also add the update to the original z (out may
@@ -579,14 +621,45 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
       for (int k = 0; k < NOUT; ++k) zr[k] = ld16(z + goff[k]);
 #pragma unroll
       for (int k = 0; k < NOUT; ++k)
-        __builtin_nontemporal_store(add_chunks(ld16(stg + soff[k]), zr[k], T()),
+        __builtin_nontemporal_store(add_chunks(skip ? zero : ld16(stg + soff[k]), zr[k], T()),
                                     (chunk_t*)(out + goff[k]));
     } else {
 #pragma unroll
       for (int k = 0; k < NOUT; ++k)
-        __builtin_nontemporal_store(ld16(stg + soff[k]), (chunk_t*)(out + goff[k]));
+        __builtin_nontemporal_store(skip ? zero : ld16(stg + soff[k]), (chunk_t*)(out + goff[k]));
     }
   }
+}
+
+// The outputs of the pairs outside each item's extent (its leading L x L square), where
+// the update is zero: out = 0, or out = z with the residual add. Workgroup (i, b) writes
+// row i of item b from column L on (the whole row when i >= L); the row's pairs are one
+// contiguous run of 16-byte chunks.
+template <class T, bool RESID>
+__global__ __launch_bounds__(256) void k3_fill_outside(const T* __restrict__ z,
+                                                       T* __restrict__ out,
+                                                       const int* __restrict__ extents, int n,
+                                                       int cz) {
+  constexpr int E = Traits<T>::E;
+  const int i = blockIdx.x, bb = blockIdx.y;
+  const int L = mask_extent(extents, bb, n);
+  const int j0 = i < L ? L : 0;
+  const size_t row = ((size_t)bb * n + i) * n;
+  const size_t c0 = (row + j0) * cz / E, c1 = (row + n) * cz / E;  // chunk range
+  const chunk_t zero = {0u, 0u, 0u, 0u};
+  for (size_t k = c0 + threadIdx.x; k < c1; k += 256) {
+    if constexpr (RESID)
+      __builtin_nontemporal_store(ld16(z + k * E), (chunk_t*)(out + k * E));
+    else
+      __builtin_nontemporal_store(zero, (chunk_t*)(out + k * E));
+  }
+}
+
+template <class T, bool RESID>
+static hipError_t launch_fill_outside(const StageArgs& a, hipStream_t st) {
+  hipLaunchKernelGGL((k3_fill_outside<T, RESID>), dim3(a.n, a.batch), dim3(256), 0, st,
+                     (const T*)a.z, (T*)a.out, a.extents, a.n, a.cz);
+  return hipGetLastError();
 }
 
 // Shapes of the wave-independent form: 8 waves per workgroup; narrow rows (KXM + KZM <= 8
@@ -657,10 +730,17 @@ static hipError_t launch_k3w_t(const StageArgs& a, hipStream_t st, bool* done) {
     const int need = (total + W - 1) / W;
     const int blocks = need < cap ? need : cap;
     const int mask_all = a.mask == nullptr;
+    // with extents and few items, the kernel runs only the tiles inside the extents and the
+    // outputs outside are written first (in place they already hold z + 0)
+    const bool compact = a.extents && a.batch <= COMPACT_MAX_ITEMS;
+    if (compact && !(RESID && a.out == a.z)) {
+      hipError_t e2 = launch_fill_outside<T, RESID>(a, st);
+      if (e2 != hipSuccess) return e2;
+    }
     hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(64 * W), lds, st, (const T*)a.x,
                        (const T*)a.z, (const T*)(mask_all ? a.one : a.mask), (T*)a.out,
                        (const T*)a.wo, a.to, (const T*)a.wg, a.tg, a.n, a.np, a.cz, a.czp, a.c,
-                       a.cp, mask_all, ug, total);
+                       a.cp, mask_all, ug, total, a.extents, compact ? 1 : 0);
     *done = true;
     return hipGetLastError();
   }

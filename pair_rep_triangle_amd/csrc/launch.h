@@ -39,12 +39,18 @@ struct StageArgs {
   int batch, n, np, cz, czp, c, cp, incoming, num_cus;
   int residual;      // stage 3 writes z + update instead of the update (out may be z)
   KernelPlan* plan;  // when set, the k1 / k3 launchers record their choice and launch nothing
+  const int* extents;  // [batch][64] partial mask extents (k0) or nullptr: the contraction
+                       // then covers the whole padded side
 };
 
 // k extent of one 16x16 MFMA chunk group: 32 (bf16) or 16 (fp32).
 inline int k_group(bool bf16_storage) { return bf16_storage ? 32 : 16; }
 inline int round_up(int v, int m) { return (v + m - 1) / m * m; }
-constexpr int N_PAD = 256;  // side padding of a, b, x (covers whole contraction tiles)
+// With mask extents and at most this many batch items, the persistent projection kernels
+// hand out only the tiles inside each item's extent (every wave reads all items' extents);
+// with more items they keep the full tile list and skip the tiles outside.
+constexpr int COMPACT_MAX_ITEMS = 32;
+constexpr int N_PAD = 64;  // side padding of a, b, x (whole 64-pair input tiles)
 constexpr size_t LDS_PER_CU = 160 * 1024;  // gfx950 LDS per CU (the most one workgroup may use)
 
 // The projection kernels keep their weights in registers, sized at compile time by the
@@ -91,6 +97,8 @@ inline int resident_blocks(const void* fn, int threads, size_t lds, std::atomic<
   return nb;
 }
 
+hipError_t launch_k0(bool bf16_storage, const void* mask, int batch, int n, int* parts,
+                     hipStream_t st);
 hipError_t launch_k1(bool bf16_storage, const StageArgs& a, hipStream_t st);
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st);
 size_t k2_grid(int np, int batch, int c);  // contraction workgroups per launch

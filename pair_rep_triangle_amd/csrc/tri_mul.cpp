@@ -8,6 +8,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <atomic>
 #include <new>
 #include <vector>
 
@@ -136,6 +137,7 @@ trimul::StageArgs stage_args(const tri_mul_handle* h, const void* z, const void*
   a.num_cus = h->num_cus;
   a.residual = residual ? 1 : 0;
   a.plan = nullptr;
+  a.extents = nullptr;
   return a;
 }
 
@@ -151,9 +153,19 @@ trimul::KernelPlan plan_of(const tri_mul_handle* h, int batch, int n) {
 }
 
 int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out, int batch, int n,
-        int direction, void* ws, size_t ws_bytes, void* stream, bool residual = false) {
+        int direction, void* ws, size_t ws_bytes, void* stream, bool residual = false,
+        const int* extents = nullptr) {
   int rc = validate_call(h, stage, z, mask, out, batch, n, direction, ws, ws_bytes, residual);
   if (rc != TRI_MUL_OK) return rc;
+  if (extents) {
+    // read by the contraction after the input kernel has written the workspace, and never
+    // written by the update
+    const size_t eb = (size_t)batch * TRI_MUL_EXTENT_PARTS * sizeof(int);
+    const size_t zb = (size_t)batch * n * n * h->c_z * (h->bf16 ? 2 : 4);
+    if ((uintptr_t)extents & 3u) return TRI_MUL_ERR_ALIGNMENT;
+    if (overlaps(extents, eb, ws, layout_of(h, batch, n).total) || overlaps(extents, eb, out, zb))
+      return TRI_MUL_ERR_ALIAS;
+  }
   // In place, each pair of z must be read (all c_z channels, for the gate's LayerNorm)
   // before any of it is overwritten. That holds only while one workgroup produces all
   // output channels of a pair; with several channel groups another group may already
@@ -164,6 +176,7 @@ int run(tri_mul_handle* h, int stage, const void* z, const void* mask, void* out
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
   if (dev != h->device) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
   trimul::StageArgs a = stage_args(h, z, mask, out, batch, n, direction, ws, residual);
+  a.extents = extents;
   hipStream_t st = (hipStream_t)stream;
   if (stage == 0 || stage == 1) {
     e = trimul::launch_k1(h->bf16, a, st);
@@ -334,6 +347,44 @@ int tri_mul_forward_residual(tri_mul_handle* h, const void* z, const void* pair_
                              size_t workspace_bytes, void* stream) {
   return run(h, 0, z, pair_mask, z_out, batch, n, direction, workspace, workspace_bytes, stream,
              true);
+}
+
+int tri_mul_mask_extents(int dtype, const void* pair_mask, int batch, int n, int* extents,
+                         void* stream) {
+  if (dtype != TRI_MUL_FP32 && dtype != TRI_MUL_BF16) return TRI_MUL_ERR_UNSUPPORTED;
+  if (!pair_mask || !extents || batch < 1 || batch > 65535 || n < 1 || n > TRI_MUL_MAX_N)
+    return TRI_MUL_ERR_INVALID_ARG;
+  const size_t esz = dtype == TRI_MUL_BF16 ? 2 : 4;
+  if (((uintptr_t)pair_mask & (esz - 1)) || ((uintptr_t)extents & 3u)) return TRI_MUL_ERR_ALIGNMENT;
+  if (overlaps(extents, (size_t)batch * TRI_MUL_EXTENT_PARTS * sizeof(int), pair_mask,
+               (size_t)batch * n * n * esz))
+    return TRI_MUL_ERR_ALIAS;
+  // the current device's architecture, checked once per device (this call runs once per
+  // model forward, next to launches that take microseconds)
+  static std::atomic<int> checked[64];
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
+  if (checked[dev].load() == 0) {
+    int d = -1, cus = 0;
+    const int rc = check_device(&d, &cus);
+    if (rc != TRI_MUL_OK && rc != TRI_MUL_ERR_UNSUPPORTED_DEVICE) return rc;
+    checked[dev].store(rc == TRI_MUL_OK ? 1 : -1);
+  }
+  if (checked[dev].load() < 0) return TRI_MUL_ERR_UNSUPPORTED_DEVICE;
+  e = trimul::launch_k0(dtype == TRI_MUL_BF16, pair_mask, batch, n, extents,
+                                   (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "launch k0_mask_extents");
+  return TRI_MUL_OK;
+}
+
+int tri_mul_forward_extents(tri_mul_handle* h, const void* z, const void* pair_mask,
+                            const int* extents, void* out, int batch, int n, int direction,
+                            int residual, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!extents || !pair_mask || (residual != 0 && residual != 1)) return TRI_MUL_ERR_INVALID_ARG;
+  return run(h, 0, z, pair_mask, out, batch, n, direction, workspace, workspace_bytes, stream,
+             residual == 1, extents);
 }
 
 int tri_mul_forward_stage(tri_mul_handle* h, int stage, const void* z, const void* pair_mask,

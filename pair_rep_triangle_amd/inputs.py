@@ -11,11 +11,13 @@ field order. Weight matrices are N(0, 1/fan_in) (std 1/sqrt(fan_in)), biases 0,
 LayerNorm gamma 1 and beta 0. ``random_affine=True`` also draws non-trivial
 biases, gammas and betas (used by the tests so that every term is exercised).
 
-The five workloads mirror the pair shapes the pages discuss: AlphaFold2/
+The first five workloads mirror the pair shapes the pages discuss: AlphaFold2/
 OpenFold pair width 128 (OpenFold-TRT summary, fixed pair dimension), the
 generative design trunk's 384-wide pair track (RFProteína architecture,
 "Inside the velocity network"), and residue counts from short targets up to
-a large complex.
+a large complex. A sixth, a batch of two items with valid lengths 300 and 512
+padded to one side (the RFProteína page's parity runs include a padded
+two-example batch, "Measured results"), exercises the mask-extent skipping.
 """
 
 import numpy as np
@@ -39,6 +41,10 @@ WORKLOADS = {
     "n768_cz384_c128_b2_bf16": dict(dtype="bf16", batch=2, n=768, c_z=384, c=128, mask="ones"),
     "n2048_cz128_c128_bf16_chains": dict(dtype="bf16", batch=1, n=2048, c_z=128, c=128,
                                          mask="chains", chains=(900, 700, 448)),
+    # two items of different valid lengths padded to one side (a padded batch): the case
+    # the mask-extent skipping is for
+    "n512_cz128_c128_b2_bf16_ragged": dict(dtype="bf16", batch=2, n=512, c_z=128, c=128,
+                                           mask="lengths", lengths=(300, 512)),
 }
 HEADLINE = "n512_cz128_c128_bf16_masked"
 
@@ -133,6 +139,9 @@ def make_workload(name, seed=0, random_affine=False):
         L = int(rng.integers(lo, hi + 1))  # inclusive U[lo, hi], drawn first
         meta["valid_length"] = L
         mask = block_mask(B, n, [L] * B)
+    elif spec["mask"] == "lengths":
+        meta["valid_lengths"] = list(spec["lengths"])
+        mask = block_mask(B, n, list(spec["lengths"]))
     elif spec["mask"] == "chains":
         total = int(sum(spec["chains"]))
         meta["valid_length"] = total  # every chain residue is valid

@@ -32,8 +32,9 @@ ERRORS = {
 }
 EXPORTS = ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
            "tri_mul_query_plan", "tri_mul_forward_static", "tri_mul_forward",
-           "tri_mul_forward_residual", "tri_mul_forward_stage",
-           "tri_mul_destroy", "tri_mul_strerror", "tri_mul_last_hip_error")
+           "tri_mul_forward_residual", "tri_mul_forward_stage", "tri_mul_mask_extents",
+           "tri_mul_forward_extents", "tri_mul_destroy", "tri_mul_strerror",
+           "tri_mul_last_hip_error")
 TRANSITION_EXPORTS = ("pair_transition_create", "pair_transition_forward",
                       "pair_transition_destroy")
 ATTENTION_EXPORTS = ("tri_attn_create", "tri_attn_workspace_bytes", "tri_attn_forward",
@@ -91,6 +92,8 @@ def load_library(path=LIB_PATH):
     lib.tri_mul_forward.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_forward_residual.argtypes = [vp, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_forward_static.argtypes = [vp, vp, vp, vp, i, i, i, vp]
+    lib.tri_mul_mask_extents.argtypes = [i, vp, i, i, vp, vp]
+    lib.tri_mul_forward_extents.argtypes = [vp, vp, vp, vp, vp, i, i, i, i, vp, sz, vp]
     lib.tri_mul_forward_stage.argtypes = [vp, i, vp, vp, vp, i, i, i, vp, sz, vp]
     lib.tri_mul_destroy.argtypes = [vp]
     lib.tri_mul_destroy.restype = None
@@ -112,8 +115,8 @@ def load_library(path=LIB_PATH):
     lib.pair_transition_destroy.restype = None
     for name in ("tri_mul_create", "tri_mul_workspace_bytes", "tri_mul_workspace_layout",
                  "tri_mul_query_plan", "tri_mul_forward_static", "tri_mul_forward",
-           "tri_mul_forward_residual", "tri_mul_forward_stage",
-                 "pair_transition_create", "pair_transition_forward"):
+                 "tri_mul_forward_residual", "tri_mul_forward_stage", "tri_mul_mask_extents",
+                 "tri_mul_forward_extents", "pair_transition_create", "pair_transition_forward"):
         getattr(lib, name).restype = i
     _lib = lib
     return lib
@@ -146,6 +149,35 @@ def _host_f32(v):
     if hasattr(v, "detach"):
         v = v.detach().cpu().numpy()
     return np.ascontiguousarray(np.asarray(v, dtype=np.float32))
+
+
+EXTENT_PARTS = 64  # TRI_MUL_EXTENT_PARTS
+
+
+def mask_extents(mask, out=None, stream=None):
+    """tri_mul_mask_extents: the per-item mask extents of a [B, N, N] bf16 or fp32 CUDA mask,
+    as a [B, 64] int32 tensor of partial maxima (the extent of item b is out[b].max()).
+    Computed once per model forward and passed to every update that shares the mask."""
+    import torch
+    lib = load_library()
+    if mask.dim() != 3 or mask.shape[1] != mask.shape[2] or not mask.is_contiguous():
+        raise ValueError("mask must be a contiguous [B, N, N] tensor")
+    if not mask.is_cuda:
+        raise ValueError("mask must be a CUDA tensor")
+    dt = {torch.bfloat16: TRI_MUL_BF16, torch.float32: TRI_MUL_FP32}.get(mask.dtype)
+    if dt is None:
+        raise ValueError("mask must be bfloat16 or float32")
+    batch, n = int(mask.shape[0]), int(mask.shape[1])
+    if out is None:
+        out = torch.empty((batch, EXTENT_PARTS), dtype=torch.int32, device=mask.device)
+    elif (tuple(out.shape) != (batch, EXTENT_PARTS) or out.dtype != torch.int32
+          or not out.is_contiguous() or out.device != mask.device):
+        raise ValueError("out must be a contiguous int32 [B, 64] tensor on the mask's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(mask.device).cuda_stream
+    _check(lib.tri_mul_mask_extents(dt, mask.data_ptr(), batch, n, out.data_ptr(), stream),
+           "tri_mul_mask_extents")
+    return out
 
 
 class TriMul:
@@ -243,8 +275,25 @@ class TriMul:
         return (z.data_ptr(), None if mask is None else mask.data_ptr(), out.data_ptr(),
                 batch, n, DIRECTIONS[direction], ws_ptr, ws_bytes, stream), out, workspace
 
-    def forward(self, z, mask=None, out=None, direction="outgoing", workspace=None, stream=None):
+    def _extents_ptr(self, extents, z):
+        import torch
+        batch = int(z.shape[0])
+        if (tuple(extents.shape) != (batch, EXTENT_PARTS) or extents.dtype != torch.int32
+                or not extents.is_contiguous()):
+            raise ValueError("extents must be the contiguous int32 [B, 64] tensor of mask_extents")
+        _check_device("extents", extents, z)
+        return extents.data_ptr()
+
+    def forward(self, z, mask=None, out=None, direction="outgoing", workspace=None, stream=None,
+                extents=None):
+        """The update; with `extents` (mask_extents of this mask) the contraction skips the
+        padding past each item's extent (tri_mul_forward_extents)."""
         args, out, _ = self._args(z, mask, out, workspace, direction, stream)
+        if extents is not None:
+            e = self._extents_ptr(extents, z)
+            _check(self.lib.tri_mul_forward_extents(self._h, args[0], args[1], e, *args[2:6], 0,
+                                                    *args[6:]), "tri_mul_forward_extents")
+            return out
         _check(self.lib.tri_mul_forward(self._h, *args), "tri_mul_forward")
         return out
 
@@ -259,9 +308,14 @@ class TriMul:
         return out
 
     def forward_residual(self, z, mask=None, out=None, direction="outgoing", workspace=None,
-                         stream=None):
+                         stream=None, extents=None):
         """out = z + update (out may be z itself for an in-place pair update)."""
         args, out, _ = self._args(z, mask, out, workspace, direction, stream)
+        if extents is not None:
+            e = self._extents_ptr(extents, z)
+            _check(self.lib.tri_mul_forward_extents(self._h, args[0], args[1], e, *args[2:6], 1,
+                                                    *args[6:]), "tri_mul_forward_extents")
+            return out
         _check(self.lib.tri_mul_forward_residual(self._h, *args), "tri_mul_forward_residual")
         return out
 

@@ -46,6 +46,20 @@ def test_library_exports_every_declared_symbol(lib):
         assert hasattr(lib, name), name
 
 
+def test_mask_extents_rejects_bad_arguments_before_touching_the_device(lib):
+    buf = ctypes.c_void_p(64)
+    assert lib.tri_mul_mask_extents(7, buf, 1, 16, buf, None) == -2   # dtype
+    assert lib.tri_mul_mask_extents(1, None, 1, 16, buf, None) == -1  # no mask
+    assert lib.tri_mul_mask_extents(1, buf, 0, 16, buf, None) == -1   # batch
+    assert lib.tri_mul_mask_extents(1, buf, 1, 0, buf, None) == -1    # n
+
+
+def test_forward_extents_rejects_a_null_handle(lib):
+    buf = ctypes.c_void_p(64)
+    assert lib.tri_mul_forward_extents(None, buf, None, buf, buf, 1, 16, 0, 0, buf, 1 << 20,
+                                       None) == -1
+
+
 def test_query_plan_rejects_bad_arguments(lib):
     plan = tm.Plan()
     assert lib.tri_mul_query_plan(None, 1, 16, ctypes.byref(plan)) == -1

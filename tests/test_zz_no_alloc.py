@@ -79,9 +79,9 @@ def test_static_workspace_rejects_sizes_beyond_the_array():
     d = make_random(1, 8, 128, 128, seed=1)
     mod = TriMul(d["weights"], 128, 128, "bf16")
     note("static workspace size limit")
-    # n = 513 pads to 768: 3 * 128 * 768^2 * 2 bytes = 432 MiB > 256 MiB
-    assert mod.workspace_bytes(1, 513) > STATIC_BYTES >= mod.workspace_bytes(1, 512)
-    z = torch.zeros((1, 513, 513, 128), dtype=torch.bfloat16, device="cuda")
+    # n = 600 pads to 640: 3 * 128 * 640^2 * 2 bytes = 300 MiB > 256 MiB (576 fits)
+    assert mod.workspace_bytes(1, 600) > STATIC_BYTES >= mod.workspace_bytes(1, 576)
+    z = torch.zeros((1, 600, 600, 128), dtype=torch.bfloat16, device="cuda")
     out = torch.full_like(z, 3.0)
     assert _static(mod, z, None, out, "outgoing") == -6  # TRI_MUL_ERR_WORKSPACE_TOO_SMALL
     torch.cuda.synchronize()
