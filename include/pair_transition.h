@@ -44,10 +44,16 @@ typedef struct pair_transition_handle pair_transition_handle;
 
 /* Build a handle on the current device (must be gfx950): folds the LayerNorm into W_1
  * and b_1, rounds the weights to `dtype` and stores them on the device in the kernel's
- * order. Supported: c_z a multiple of 32 up to 128 (bf16) or of 16 up to 64 (fp32);
- * hidden >= 1 (padded with zero units to a multiple of 32 / 16), with the padded
- * weights of both layers (16 bytes of padding per row) and the fp32 biases fitting one
- * workgroup's 160 KB of LDS (bf16 c_z = 128: hidden <= 288).
+ * order. Supported, with hidden >= 1 padded with zero units to a multiple of 32 (bf16)
+ * or 16 (fp32):
+ *   - weights resident in LDS: c_z a multiple of 32 up to 128 (bf16) or of 16 up to 64
+ *     (fp32), when the padded weights of both layers (16 bytes of padding per row) and
+ *     the fp32 biases fit one workgroup's 160 KB of LDS (bf16 c_z = 128: hidden <= 288);
+ *   - otherwise, bf16 only, weights streamed through LDS one group of 32 hidden units at
+ *     a time: c_z a multiple of 32 up to 512 (padded with zero channels to 128, 256, 384
+ *     or 512) and hidden with 256 c_z_padded + 4 (hidden_padded + c_z_padded) bytes
+ *     within 160 KB (c_z = 384: hidden <= 15744), which covers the released pair width
+ *     384 with hidden 768.
  * Returns TRI_MUL_ERR_UNSUPPORTED for other shapes, TRI_MUL_ERR_INVALID_ARG for NULL
  * w / w1 / w2 / out or non-positive sizes. On error *out is NULL. */
 int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden, int dtype,

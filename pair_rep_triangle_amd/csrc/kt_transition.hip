@@ -271,6 +271,7 @@ static hipError_t launch_kt_dispatch(const TransitionArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_transition(bool bf16_storage, const TransitionArgs& a, hipStream_t st) {
+  if (a.wide) return bf16_storage ? launch_transition_wide(a, st) : hipErrorInvalidValue;
   return bf16_storage ? launch_kt_dispatch<bf16>(a, st) : launch_kt_dispatch<float>(a, st);
 }
 

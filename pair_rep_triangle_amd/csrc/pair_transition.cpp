@@ -15,7 +15,8 @@
 
 struct pair_transition_handle {
   int c_z, hidden, hp, dtype, device, num_cus;
-  bool bf16;
+  bool bf16, wide;
+  int czp;  // wide form: padded c_z
   void* block;  // LDS image of the weights | one
   const void *image, *one;
   size_t image_bytes;
@@ -43,6 +44,88 @@ int hidden_of_slot(int s, bool bf16) {
   return 32 * g + (j < 4 ? 4 * q + j : 16 + 4 * q + (j - 4));
 }
 
+// Uploads the image and fills the handle; frees nothing on success.
+int upload(const std::vector<unsigned char>& host, pair_transition_handle* h, size_t image,
+           void** dptr) {
+  hipError_t e = hipMalloc(dptr, host.size());
+  if (e != hipSuccess) {
+    if (e == hipErrorOutOfMemory) return TRI_MUL_ERR_OUT_OF_MEMORY;
+    return hip_fail(e, "hipMalloc(transition weights)");
+  }
+  e = hipMemcpy(*dptr, host.data(), host.size(), hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    (void)hipFree(*dptr);
+    return hip_fail(e, "hipMemcpy(transition weights)");
+  }
+  unsigned char* d = (unsigned char*)*dptr;
+  h->block = *dptr;
+  h->image = d;
+  h->image_bytes = image;
+  h->one = d + align256(image);
+  return TRI_MUL_OK;
+}
+
+// The wide form's image (bf16): per hidden group g of 32 units, W_1' rows 32g..32g+31
+// ([32][czp], chunk c of row r at position c ^ (r & 15)) and W_2's columns of the group
+// ([czp][32] in the kernel's row and slot order, chunk q of row R at q ^ ((R >> 2) & 3));
+// then b_1' [hp] and b_2 [czp] (kernel row order); then the one-element mask `one`.
+int create_wide(const pair_transition_weights* w, int c_z, int hidden, int hp, int dev, int cus,
+                pair_transition_handle** out) {
+  const int czp = trimul::transition_wide_czp(c_z), groups = hp / 32;
+  const size_t gb = (size_t)128 * czp;
+  const size_t image = (size_t)groups * gb + ((size_t)hp + czp) * 4;
+  std::vector<unsigned char> host(align256(image) + 256, 0);
+  unsigned char* const base = host.data();
+  float* hb1 = (float*)(base + (size_t)groups * gb);
+  float* hb2 = hb1 + hp;
+  store_elem(base + align256(image), 1.0f, true);
+  for (int hu = 0; hu < hidden; ++hu) {
+    double t = w->b1 ? (double)w->b1[hu] : 0.0;
+    const int g = hu / 32, r = hu % 32;
+    unsigned char* row = base + (size_t)g * gb + (size_t)r * czp * 2;
+    for (int k = 0; k < c_z; ++k) {
+      const double wk = w->w1[(size_t)hu * c_z + k];
+      const int c = k / 8, e = k % 8, pos = c ^ (r & 15);
+      store_elem(row + ((size_t)pos * 8 + e) * 2,
+                 (float)(wk * (w->ln_gamma ? (double)w->ln_gamma[k] : 1.0)), true);
+      if (w->ln_beta) t += wk * (double)w->ln_beta[k];
+    }
+    hb1[hu] = (float)t;
+  }
+  for (int R = 0; R < czp; ++R) {
+    const int ch = out_channel(R, true);
+    if (ch >= c_z) continue;  // padded output rows stay zero
+    hb2[R] = w->b2 ? w->b2[ch] : 0.f;
+    for (int s = 0; s < hp; ++s) {
+      const int hu = hidden_of_slot(s, true);
+      if (hu >= hidden) continue;
+      const int g = s / 32, slot = s % 32, qq = slot / 8, e = slot % 8;
+      const int pos = qq ^ ((R >> 2) & 3);
+      unsigned char* w2g = base + (size_t)g * gb + (size_t)64 * czp;
+      store_elem(w2g + ((size_t)R * 32 + pos * 8 + e) * 2, w->w2[(size_t)ch * hidden + hu], true);
+    }
+  }
+  pair_transition_handle* h = new (std::nothrow) pair_transition_handle();
+  if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
+  void* dptr = nullptr;
+  const int urc = upload(host, h, image, &dptr);
+  if (urc != TRI_MUL_OK) {
+    delete h;
+    return urc;
+  }
+  h->c_z = c_z;
+  h->hidden = hidden;
+  h->hp = hp;
+  h->dtype = TRI_MUL_BF16;
+  h->device = dev;
+  h->num_cus = cus;
+  h->bf16 = true;
+  h->wide = true;
+  h->czp = czp;
+  *out = h;
+  return TRI_MUL_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -57,10 +140,13 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
   const int kg = bf16 ? 32 : 16;
   if (hidden > 1 << 20) return TRI_MUL_ERR_UNSUPPORTED;
   const int hp = (hidden + kg - 1) / kg * kg;
-  if (!trimul::transition_supported(bf16, c_z, hp)) return TRI_MUL_ERR_UNSUPPORTED;
+  // the weights in one workgroup's LDS if they fit, else streamed through it (bf16)
+  const bool wide = !trimul::transition_supported(bf16, c_z, hp);
+  if (wide && !trimul::transition_wide_supported(bf16, c_z, hp)) return TRI_MUL_ERR_UNSUPPORTED;
   int dev = -1, cus = 0;
   int rc = check_device(&dev, &cus);
   if (rc != TRI_MUL_OK) return rc;
+  if (wide) return create_wide(w, c_z, hidden, hp, dev, cus, out);
 
   // the kernel's LDS image: W_1' [hp][c_z + pad] | W_2 [c_z][hp + pad] | b_1' [hp] | b_2 [c_z]
   // (pad: one 16-byte chunk of zeros per row), then the one-element mask `one`
@@ -122,6 +208,8 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
   h->device = dev;
   h->num_cus = cus;
   h->bf16 = bf16;
+  h->wide = false;
+  h->czp = c_z;
   h->block = dptr;
   h->image = d;
   h->image_bytes = image;
@@ -157,6 +245,8 @@ int pair_transition_forward(pair_transition_handle* h, const void* z, const void
   a.hp = h->hp;
   a.mask_all = pair_mask ? 0 : 1;
   a.num_cus = h->num_cus;
+  a.wide = h->wide ? 1 : 0;
+  a.czp = h->czp;
   e = trimul::launch_transition(h->bf16, a, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "launch pair_transition");
   return TRI_MUL_OK;

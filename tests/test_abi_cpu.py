@@ -127,7 +127,7 @@ def _transition_struct(w):
 
 
 @pytest.mark.parametrize("c_z,hidden,dtype,code", [
-    (48, 96, tm.TRI_MUL_BF16, -2), (160, 320, tm.TRI_MUL_BF16, -2), (128, 512, tm.TRI_MUL_BF16, -2),
+    (48, 96, tm.TRI_MUL_BF16, -2), (544, 1088, tm.TRI_MUL_BF16, -2), (512, 8192, tm.TRI_MUL_BF16, -2),
     (24, 48, tm.TRI_MUL_FP32, -2), (128, 256, tm.TRI_MUL_FP32, -2), (64, 64, 9, -2),
     (0, 64, tm.TRI_MUL_BF16, -1), (64, 0, tm.TRI_MUL_BF16, -1),
 ])

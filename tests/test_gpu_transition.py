@@ -61,6 +61,46 @@ def test_transition_full_output(dtype, B, n, c_z, hidden, mask):
     _run(dtype, B, n, c_z, hidden, mask, seed=n + c_z)
 
 
+# Widths whose weights do not fit one workgroup's LDS: the bf16 form that streams them
+# through LDS one hidden group of 32 units at a time (c_z padded to 128/256/384/512).
+@pytest.mark.parametrize("B,n,c_z,hidden,mask", [
+    (1, 64, 384, 768, "random_pairs"),    # the released pair width, expansion 2
+    (2, 37, 256, 512, "block"),           # ragged last 128-pair tile
+    (1, 45, 320, 640, "random_residues"), # c_z padded to 384 with zero channels
+    (1, 33, 512, 1024, "ones"),
+    (1, 50, 128, 1024, "random_pairs"),   # narrow width, hidden too wide for resident weights
+    (1, 40, 384, 700, "block"),           # hidden padded to 704
+])
+def test_transition_streamed_weights_full_output(B, n, c_z, hidden, mask):
+    note(f"transition streamed bf16 B={B} n={n} cz={c_z} hidden={hidden} {mask}")
+    _run("bf16", B, n, c_z, hidden, mask, seed=n + c_z)
+
+
+def test_transition_released_shape_n512():
+    """c_z = 384, hidden 768, N = 512, block mask: every pair (about 0.3 TFLOP of fp64 work in
+    the oracle), the shape and launch of its benchmark line."""
+    note("transition streamed N=512 c_z=384 hidden 768")
+    _run("bf16", 1, 512, 384, 768, "block", seed=1)
+
+
+def test_transition_streamed_in_place_and_guard_band():
+    """In place equals out of place; nothing past the output changes (last tile of 128 pairs
+    holds 25 pairs)."""
+    note("transition streamed in place and guard band")
+    n, c_z, hidden = 39, 384, 768
+    out, z, m, mod = _run("bf16", 1, n, c_z, hidden, "random_pairs", seed=5)
+    zi = z.clone()
+    mod.forward(zi, m, out=zi)
+    torch.cuda.synchronize()
+    assert torch.equal(zi, out)
+    count = z.numel()
+    big = torch.full((count + 256 * c_z,), 7.0, dtype=torch.bfloat16, device="cuda")
+    mod.forward(z, m, out=big[:count].view_as(z))
+    torch.cuda.synchronize()
+    assert torch.all(big[count:] == 7.0)
+    assert torch.equal(big[:count].view_as(z), out)
+
+
 @pytest.mark.parametrize("dtype", ["fp32", "bf16"])
 def test_transition_in_place_matches_out_of_place(dtype):
     note(f"transition in place {dtype}")
