@@ -292,12 +292,15 @@ __device__ __forceinline__ void progress_priority(int level) {
   else __builtin_amdgcn_s_setprio(0);
 }
 
-template <class T>
+// XM: 0 without mask extents; 1 with extents, every tile visited and the ones outside
+// skipped; 2 with extents and the compact list of the tiles inside them. (A template
+// parameter, so the plain form carries none of the extent bookkeeping in registers.)
+template <class T, int XM>
 __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     const T* __restrict__ z, const T* __restrict__ mask, T* __restrict__ a_out,
     T* __restrict__ b_out, const chunk_t* __restrict__ image, int n, int np, int cz, int c,
-    int incoming, int mask_all, int ug, int total_tiles, const int* __restrict__ extents,
-    int compact) {
+    int incoming, int mask_all, int ug, int total_tiles, const int* __restrict__ extents) {
+  constexpr bool compact = XM == 2;
   constexpr int E = Traits<T>::E;
   constexpr int KG = Traits<T>::KG;
   constexpr int KZ = 4;               // chunk groups along c_z
@@ -326,13 +329,13 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   // those inside each item's extent only, so every wave gets an equal share of the work
   // that is left.
   ActiveTiles sched;
-  if (compact) {
+  if constexpr (compact) {
     sched.init(extents, n, total_tiles / (np * ntx), K1W_TP);
     total_tiles = sched.total();
     if (total_tiles == 0) return;  // workgroup-uniform: no item has a valid pair
   }
   auto coords = [&](int t, int& bb, int& r, int& s0) {
-    if (compact) {
+    if constexpr (compact) {
       sched.at(t, bb, r, s0);
       return;
     }
@@ -366,7 +369,7 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   auto fetch = [&](int t, Pre& f) {
     int bb, r, s0;
     coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);  // waves past the end refetch
-    const int lim = item_bound(extents, bb, n, ecache);
+    const int lim = XM ? item_bound(extents, bb, n, ecache) : n;
     const bool row_ok = r < lim && s0 < lim;
     const size_t p0 = row_ok ? (incoming ? ((size_t)bb * n + s0) * n + r : ((size_t)bb * n + r) * n + s0) : 0;
     // pairs of the storage row from the tile's first one to the last real one
@@ -418,7 +421,7 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
   auto prepare = [&](int t) {
     int bb, r, s0;
     coords(t < total_tiles ? t : total_tiles - 1, bb, r, s0);
-    const int lim = item_bound(extents, bb, n, ecache);
+    const int lim = XM ? item_bound(extents, bb, n, ecache) : n;
     int opaque;  // keeps the loop-invariant masks inside the loop
     asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
     float mv[ST];
@@ -581,8 +584,8 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
       fetch(t + nw, f);  // za is dead: the next tile's z loads go out now
       emit(unit_dst(ug - 1), accb, masked);
     };
-    const int lim = item_bound(extents, bb, n, ecache);
-    if (extents && !(r < lim && s0 < lim)) {
+    const int lim = XM ? item_bound(extents, bb, n, ecache) : n;
+    if (XM && !(r < lim && s0 < lim)) {
       fetch(t + nw, f);  // inactive (outside the item's extent): nothing to compute or write
     } else if (zeros) {
       // a tile wholly outside the mask: no MFMA and no epilogue, its unit rows are zeros
@@ -602,6 +605,28 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
 
 // Launches the wave-independent form if the units split into groups that fit LDS;
 // *done = false leaves the launch to the tile-shared form.
+template <class T, int XM>
+static hipError_t launch_k1w_x(const StageArgs& a, hipStream_t st, int ug, int total) {
+  const size_t lds = k1w_lds_bytes(ug);
+  auto fn = k1_input_gate_waves<T, XM>;
+  static std::atomic<int> granted{0};
+  hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
+  if (e != hipSuccess) return e;
+  const int groups = 2 * (a.c / 16) / ug;
+  static std::atomic<int> occ{0};
+  static std::atomic<size_t> occ_lds{0};
+  const int per_cu = resident_blocks((const void*)fn, K1W_THREADS, lds, occ, occ_lds);
+  const int cap = a.num_cus * per_cu / groups > 0 ? a.num_cus * per_cu / groups : 1;
+  const int need = (total + K1W_WAVES - 1) / K1W_WAVES;
+  const int blocks = need < cap ? need : cap;
+  const int mask_all = a.mask == nullptr;
+  hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K1W_THREADS), lds, st, (const T*)a.z,
+                     (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b,
+                     (const chunk_t*)a.k1w_image, a.n, a.np, a.cz, a.c, a.incoming, mask_all, ug,
+                     total, a.extents);
+  return hipGetLastError();
+}
+
 template <class T>
 static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
   *done = false;
@@ -620,25 +645,11 @@ static hipError_t launch_k1w(const StageArgs& a, hipStream_t st, bool* done) {
     *done = true;
     return hipSuccess;
   }
-  const size_t lds = k1w_lds_bytes(ug);
-  auto fn = k1_input_gate_waves<T>;
-  static std::atomic<int> granted{0};
-  hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
-  if (e != hipSuccess) return e;
-  const int groups = units / ug;
-  static std::atomic<int> occ{0};
-  static std::atomic<size_t> occ_lds{0};
-  const int per_cu = resident_blocks((const void*)fn, K1W_THREADS, lds, occ, occ_lds);
-  const int cap = a.num_cus * per_cu / groups > 0 ? a.num_cus * per_cu / groups : 1;
-  const int need = (total + K1W_WAVES - 1) / K1W_WAVES;
-  const int blocks = need < cap ? need : cap;
-  const int mask_all = a.mask == nullptr;
-  hipLaunchKernelGGL(fn, dim3(blocks, groups), dim3(K1W_THREADS), lds, st, (const T*)a.z,
-                     (const T*)(mask_all ? a.one : a.mask), (T*)a.a, (T*)a.b,
-                     (const chunk_t*)a.k1w_image, a.n, a.np, a.cz, a.c, a.incoming, mask_all, ug,
-                     total, a.extents, a.extents && a.batch <= COMPACT_MAX_ITEMS ? 1 : 0);
+  (void)units;
   *done = true;
-  return hipGetLastError();
+  if (!a.extents) return launch_k1w_x<T, 0>(a, st, ug, total);
+  if (a.batch <= COMPACT_MAX_ITEMS) return launch_k1w_x<T, 2>(a, st, ug, total);
+  return launch_k1w_x<T, 1>(a, st, ug, total);
 }
 
 // ---------------------------------------------------------------------------------------
