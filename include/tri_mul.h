@@ -90,10 +90,12 @@ typedef struct tri_mul_layout {
 /* Which kernel forms a call of (batch, n) takes (tri_mul_query_plan). The input and the
  * output kernel each come in a wave-independent form (weights in LDS, every wave runs its
  * own tiles) and a tile-shared form (weights in registers, tiles shared through LDS); the
+ * output kernel also in a streamed form for wide pair tracks (bf16, c_z above 128: its
+ * weights stream through LDS, one workgroup produces every channel of its pairs). The
  * choice depends on the widths and on the size of one batch item's operands. */
 typedef struct tri_mul_plan {
   int input_form;    /* 0 wave-independent, 1 tile-shared                        */
-  int output_form;   /* 0 wave-independent, 1 tile-shared                        */
+  int output_form;   /* 0 wave-independent, 1 tile-shared, 2 streamed weights    */
   int output_groups; /* output-channel groups the output kernel splits c_z into  */
   int in_place_ok;   /* 1 when tri_mul_forward_residual may take z_out == z      */
   int n_pad;         /* padded side of the workspace planes                      */

@@ -14,7 +14,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libtrimul.so")
-SOURCES = ("k0_mask_extents.hip", "k1_input_gate.hip", "k2_contract.hip", "k3_output_gate.hip", "kt_transition.hip", "kt_transition_wide.hip",
+SOURCES = ("k0_mask_extents.hip", "k1_input_gate.hip", "k2_contract.hip", "k3_output_gate.hip", "k3_stream.hip", "kt_transition.hip", "kt_transition_wide.hip",
            "ka_attention.hip", "tri_mul.cpp", "tri_mul_static.hip", "pair_transition.cpp",
            "tri_attention.cpp")
 

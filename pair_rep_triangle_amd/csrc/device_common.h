@@ -3,6 +3,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "launch.h"
 
 namespace trimul {
@@ -14,6 +16,13 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(4))) unsigned int chunk_t;  // 16 bytes
 typedef __attribute__((ext_vector_type(2))) unsigned int half_t;   // 8 bytes
+
+// z and out are distinct buffers (restrict-qualified) unless the kernel adds the update
+// to z, where out may be z itself.
+template <class T, bool RESID>
+using ZIn = std::conditional_t<RESID, const T*, const T* __restrict__>;
+template <class T, bool RESID>
+using ZOut = std::conditional_t<RESID, T*, T* __restrict__>;
 
 // E = elements of T per 16-byte chunk; KG = k covered by one 16x16 MFMA chunk group
 // (4 lane groups x one chunk each).

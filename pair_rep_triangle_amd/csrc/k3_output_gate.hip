@@ -22,12 +22,6 @@
 
 namespace trimul {
 
-// z and out are distinct buffers (restrict-qualified) unless the kernel adds the update
-// to z, where out may be z itself.
-template <class T, bool RESID>
-using ZIn = std::conditional_t<RESID, const T*, const T* __restrict__>;
-template <class T, bool RESID>
-using ZOut = std::conditional_t<RESID, T*, T* __restrict__>;
 
 constexpr int K3_TP = 64;
 constexpr int K3_WAVES = 4;
@@ -806,6 +800,11 @@ static hipError_t launch_k3_dispatch(const StageArgs& a, hipStream_t st) {
 }
 
 hipError_t launch_k3(bool bf16_storage, const StageArgs& a, hipStream_t st) {
+  if (bf16_storage) {
+    bool done = false;
+    hipError_t e = launch_k3_stream(a, st, &done);
+    if (e != hipSuccess || done) return e;
+  }
   if (a.residual)
     return bf16_storage ? launch_k3_dispatch<bf16, true>(a, st)
                         : launch_k3_dispatch<float, true>(a, st);

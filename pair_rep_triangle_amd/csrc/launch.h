@@ -41,6 +41,7 @@ struct StageArgs {
   KernelPlan* plan;  // when set, the k1 / k3 launchers record their choice and launch nothing
   const int* extents;  // [batch][64] partial mask extents (k0) or nullptr: the contraction
                        // then covers the whole padded side
+  const void* k3s_image;  // the streamed output gate's weights (k3_stream.hip), or nullptr
 };
 
 // k extent of one 16x16 MFMA chunk group: 32 (bf16) or 16 (fp32).
@@ -103,5 +104,23 @@ hipError_t launch_k1(bool bf16_storage, const StageArgs& a, hipStream_t st);
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st);
 size_t k2_grid(int np, int batch, int c);  // contraction workgroups per launch
 hipError_t launch_k3(bool bf16_storage, const StageArgs& a, hipStream_t st);
+
+// The output gate with its weights streamed through LDS (bf16, c_z above 128), compiled
+// for these padded (KX, KZ) chunk-group pairs; its weight image per unit pair k of 32
+// output rows: W_o rows [32][cp] then W_g rows [32][czp] (row R of the kernel is channel
+// 32 (R / 32) + 8 ((R % 16) / 4) + 4 ((R % 32) / 16) + R % 4; chunk c of row r at position
+// c ^ (r & 15)), then the start values of W_o and W_g [czp] each, in kernel row order.
+#define TRIMUL_K3S_VARIANTS(X) X(4, 8) X(4, 12) X(4, 16)
+size_t k3_stream_lds(int cp, int czp);
+inline bool k3_stream_variant(int kx, int kz) {
+#define TRIMUL_K3S_IS(X_, Z_) if (kx == X_ && kz == Z_) return true;
+  TRIMUL_K3S_VARIANTS(TRIMUL_K3S_IS)
+#undef TRIMUL_K3S_IS
+  return false;
+}
+inline int k3_stream_channel(int R) {
+  return 32 * (R / 32) + 8 * ((R % 16) / 4) + 4 * ((R % 32) / 16) + R % 4;
+}
+hipError_t launch_k3_stream(const StageArgs& a, hipStream_t st, bool* done);
 
 }  // namespace trimul

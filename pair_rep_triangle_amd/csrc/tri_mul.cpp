@@ -78,6 +78,31 @@ void build_k1w_images(const unsigned char* w1, const float* t1, int c, int ug, i
   (void)esz;
 }
 
+// The streamed output gate's weight image (launch.h): per unit pair k, W_o rows then W_g
+// rows of kernel rows 32k .. 32k + 31, chunk c of row r at position c ^ (r & 15); then the
+// start values in kernel row order. wo [c_z][cp] and wg [c_z][czp] are the folded bf16
+// matrices in channel order; rows of padding channels stay zero.
+void build_k3s_image(const unsigned char* wo, const unsigned char* wg, const float* to,
+                     const float* tg, int c_z, int cp, int czp, unsigned char* dst) {
+  const int steps = czp / 32;
+  const size_t gb = (size_t)64 * (cp + czp);
+  float* tos = (float*)(dst + (size_t)steps * gb);
+  float* tgs = tos + czp;
+  for (int R = 0; R < czp; ++R) {
+    const int ch = trimul::k3_stream_channel(R);
+    const int k = R / 32, r = R % 32;
+    unsigned char* blk = dst + (size_t)k * gb;
+    if (ch >= c_z) continue;
+    tos[R] = to[ch];
+    tgs[R] = tg[ch];
+    for (int cc = 0; cc < cp / 8; ++cc)
+      memcpy(blk + ((size_t)r * cp + (size_t)(cc ^ (r & 15)) * 8) * 2, wo + ((size_t)ch * cp + cc * 8) * 2, 16);
+    unsigned char* gblk = blk + (size_t)64 * cp;
+    for (int cc = 0; cc < czp / 8; ++cc)
+      memcpy(gblk + ((size_t)r * czp + (size_t)(cc ^ (r & 15)) * 8) * 2, wg + ((size_t)ch * czp + cc * 8) * 2, 16);
+  }
+}
+
 struct Layout {
   size_t a, b, x, total;
   int np, esz;
@@ -236,7 +261,12 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   const int k1w_ug = czp == 4 * kg ? trimul::k1w_group_units(c) : 0;
   const int k1w_groups = k1w_ug ? 2 * (c / 16) / k1w_ug : 0;
   const size_t k1wb = align256((size_t)k1w_groups * (k1w_ug ? trimul::k1w_image_bytes(k1w_ug) : 0));
-  const size_t total = w1b + wob + wgb + t1b + 2 * tob + oneb + k1wb;
+  // the streamed output gate (bf16, c_z above 128) reads its weights as a stream of unit
+  // pairs (launch.h)
+  const bool k3s = bf16 && czp > 128 && trimul::k3_stream_variant(kx, kz) &&
+                   trimul::k3_stream_lds(cp, czp) <= trimul::LDS_PER_CU;
+  const size_t k3sb = k3s ? align256((size_t)(czp / 32) * 64 * (cp + czp) + (size_t)2 * czp * 4) : 0;
+  const size_t total = w1b + wob + wgb + t1b + 2 * tob + oneb + k1wb + k3sb;
   std::vector<unsigned char> host(total, 0);
   unsigned char* hw1 = host.data();
   unsigned char* hwo = hw1 + w1b;
@@ -261,6 +291,8 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   fold(w->w_gate, w->ln_in_gamma, w->ln_in_beta, w->b_gate, c_z, c_z, czp, bf16, ng, hwg, htg);
   unsigned char* himg = hone + oneb;
   build_k1w_images(hw1, ht1, c, k1w_ug, k1w_groups, esz, himg);  // rows of czp * esz = 256 bytes
+  unsigned char* hk3s = himg + k1wb;
+  if (k3s) build_k3s_image(hwo, hwg, hto, htg, c_z, cp, czp, hk3s);
 
   tri_mul_handle* h = new (std::nothrow) tri_mul_handle();
   if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
@@ -297,6 +329,7 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   a.tg = (const float*)(d + ((unsigned char*)htg - hw1));
   a.one = d + (hone - hw1);
   a.k1w_image = k1w_ug ? d + (himg - hw1) : nullptr;
+  a.k3s_image = k3s ? d + (hk3s - hw1) : nullptr;
   a.cz = c_z;
   a.czp = czp;
   a.c = c;

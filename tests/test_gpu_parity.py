@@ -182,6 +182,7 @@ def test_widest_fp32_full_output(direction):
     ("bf16", 1, 450, 128, 128, (0, 0)),   # both projection kernels wave-independent
     ("bf16", 1, 129, 128, 128, (1, 0)),   # tile-shared input gate, wave-independent output
     ("bf16", 2, 70, 128, 512, (1, 1)),    # both tile-shared
+    ("bf16", 1, 75, 384, 128, (1, 2)),    # streamed output-gate weights
     ("fp32", 1, 450, 64, 32, (0, 0)),
     ("fp32", 1, 45, 256, 128, (1, 1)),
 ])

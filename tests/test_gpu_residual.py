@@ -78,7 +78,6 @@ def test_in_place_many_tiles_per_wave_is_bitwise_out_of_place(dtype, c_z, c):
 
 @pytest.mark.parametrize("dtype,N,c_z,c", [
     ("fp32", 512, 128, 128),   # wave-independent output kernel, 2 channel groups
-    ("bf16", 768, 384, 128),   # the wide pair track: wave-independent, 4 channel groups
     ("fp32", 64, 256, 128),    # tile-shared output kernel, 2 channel groups
     ("bf16", 64, 512, 512),    # tile-shared, 4 channel groups
 ])
@@ -119,6 +118,35 @@ def test_residual_tile_shared_output_kernel(dtype, N, c_z, c, in_place):
             mod.forward_residual(zi, m, out=zi, direction=direction)
             torch.cuda.synchronize()
             assert torch.equal(zi, out)
+
+
+@pytest.mark.parametrize("B,N,c_z,c", [
+    (2, 70, 384, 128),   # the wide pair track
+    (1, 45, 256, 128),
+    (1, 33, 512, 64),    # c padded to 128
+    (1, 100, 320, 96),   # c_z padded to 384, c to 128
+])
+def test_streamed_output_gate(B, N, c_z, c):
+    """bf16 c_z above 128: the output gate streams its weights and one workgroup writes every
+    channel of its pairs, so in place is allowed and must equal out of place."""
+    d = make_random(B, N, c_z, c, seed=N + c_z, mask="random_pairs", random_affine=True)
+    z, m, z_host, m_host = to_device(d, "bf16")
+    mod = TriMul(d["weights"], c_z, c, "bf16")
+    plan = mod.plan(B, N)
+    assert plan["output_form"] == 2 and plan["output_groups"] == 1 and plan["in_place_ok"] == 1
+    for direction in ("outgoing", "incoming"):
+        note(f"streamed output gate B={B} N={N} c_z={c_z} c={c} {direction}")
+        want = tri_mul_ref(z_host, m_host, d["weights"], direction)
+        out = mod.forward(z, m, direction=direction)
+        torch.cuda.synchronize()
+        assert rel_err(_host(out), want) <= TOL["bf16"]
+        res = mod.forward_residual(z, m, direction=direction)
+        torch.cuda.synchronize()
+        check_residual_update(_host(res), z_host, want, "bf16")
+        zi = z.clone()
+        mod.forward_residual(zi, m, out=zi, direction=direction)
+        torch.cuda.synchronize()
+        assert torch.equal(zi, res)
 
 
 @pytest.mark.parametrize("dtype,B,N,c_z,c", [
