@@ -69,7 +69,7 @@ int upload(const std::vector<unsigned char>& host, pair_transition_handle* h, si
 // ([32][czp], chunk c of row r at position c ^ (r & 15)) and W_2's columns of the group
 // ([czp][32] in the kernel's row and slot order, chunk q of row R at q ^ ((R >> 2) & 3));
 // then b_1' [hp] and b_2 [czp] (kernel row order); then the one-element mask `one`.
-int create_wide(const pair_transition_weights* w, int c_z, int hidden, int hp, int dev, int cus,
+int create_wide(const pair_transition_weights* w, int c_z, int hidden, int hp,
                 pair_transition_handle** out) {
   const int czp = trimul::transition_wide_czp(c_z), groups = hp / 32;
   const size_t gb = (size_t)128 * czp;
@@ -105,6 +105,9 @@ int create_wide(const pair_transition_weights* w, int c_z, int hidden, int hp, i
       store_elem(w2g + ((size_t)R * 32 + pos * 8 + e) * 2, w->w2[(size_t)ch * hidden + hu], true);
     }
   }
+  int dev = -1, cus = 0;
+  const int rc = check_device(&dev, &cus);
+  if (rc != TRI_MUL_OK) return rc;
   pair_transition_handle* h = new (std::nothrow) pair_transition_handle();
   if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
   void* dptr = nullptr;
@@ -143,10 +146,8 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
   // the weights in one workgroup's LDS if they fit, else streamed through it (bf16)
   const bool wide = !trimul::transition_supported(bf16, c_z, hp);
   if (wide && !trimul::transition_wide_supported(bf16, c_z, hp)) return TRI_MUL_ERR_UNSUPPORTED;
-  int dev = -1, cus = 0;
-  int rc = check_device(&dev, &cus);
-  if (rc != TRI_MUL_OK) return rc;
-  if (wide) return create_wide(w, c_z, hidden, hp, dev, cus, out);
+  // the host image first (no device needed), then the device
+  if (wide) return create_wide(w, c_z, hidden, hp, out);
 
   // the kernel's LDS image: W_1' [hp][c_z + pad] | W_2 [c_z][hp + pad] | b_1' [hp] | b_2 [c_z]
   // (pad: one 16-byte chunk of zeros per row), then the one-element mask `one`
@@ -185,6 +186,9 @@ int pair_transition_create(const pair_transition_weights* w, int c_z, int hidden
     }
   }
 
+  int dev = -1, cus = 0;
+  const int rc = check_device(&dev, &cus);
+  if (rc != TRI_MUL_OK) return rc;
   pair_transition_handle* h = new (std::nothrow) pair_transition_handle();
   if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
   void* dptr = nullptr;

@@ -52,10 +52,7 @@ int tri_attn_create(const tri_attn_weights* w, int c_z, int heads, int head_dim,
   if (c_z < 1 || heads < 1 || head_dim < 1) return TRI_MUL_ERR_INVALID_ARG;
   if (dtype != TRI_MUL_BF16) return TRI_MUL_ERR_UNSUPPORTED;
   if (!trimul::attention_supported(c_z, heads, head_dim)) return TRI_MUL_ERR_UNSUPPORTED;
-  int dev = -1, cus = 0;
-  int rc = check_device(&dev, &cus);
-  if (rc != TRI_MUL_OK) return rc;
-
+  // the host image first (no device needed), then the device
   const int hd = heads * head_dim, rows = trimul::att_proj_rows(heads);
   const size_t rs = (size_t)c_z + 8, ors = (size_t)hd + 8;  // row strides (bf16 elements)
   const size_t pimg = trimul::att_proj_image_bytes(c_z, heads);
@@ -102,6 +99,9 @@ int tri_attn_create(const tri_attn_weights* w, int c_z, int heads, int head_dim,
     hob[c] = w->b_o ? w->b_o[src] : 0.f;
   }
 
+  int dev = -1, cus = 0;
+  const int rc = check_device(&dev, &cus);
+  if (rc != TRI_MUL_OK) return rc;
   tri_attn_handle* h = new (std::nothrow) tri_attn_handle();
   if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
   void* dptr = nullptr;

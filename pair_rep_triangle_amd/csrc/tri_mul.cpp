@@ -235,14 +235,7 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   if (bf16 ? (c_z > TRI_MUL_MAX_WIDTH || c > TRI_MUL_MAX_WIDTH)
            : (c_z > TRI_MUL_MAX_WIDTH_FP32_CZ || c > TRI_MUL_MAX_WIDTH_FP32_C))
     return TRI_MUL_ERR_UNSUPPORTED;
-  int dev = -1, cus = 0;
-  int rc = check_device(&dev, &cus);
-  if (rc != TRI_MUL_OK) return rc;
-  // set-up of the allocation-free entry point on this device: the lookup's result is kept
-  // per device and a failure is reported by tri_mul_forward_static itself
-  void* static_ws = nullptr;
-  (void)static_workspace(dev, &static_ws);
-
+  // the host image first (no device needed), then the device
   const int kg = trimul::k_group(bf16);
   int kx = 0, kz = 0;
   if (!trimul::padded_ksteps(c, c_z, bf16, &kx, &kz)) return TRI_MUL_ERR_UNSUPPORTED;
@@ -293,6 +286,14 @@ int tri_mul_create(const tri_mul_weights* w, int c_z, int c, int dtype, tri_mul_
   build_k1w_images(hw1, ht1, c, k1w_ug, k1w_groups, esz, himg);  // rows of czp * esz = 256 bytes
   unsigned char* hk3s = himg + k1wb;
   if (k3s) build_k3s_image(hwo, hwg, hto, htg, c_z, cp, czp, hk3s);
+
+  int dev = -1, cus = 0;
+  int rc = check_device(&dev, &cus);
+  if (rc != TRI_MUL_OK) return rc;
+  // set-up of the allocation-free entry point on this device: the lookup's result is kept
+  // per device and a failure is reported by tri_mul_forward_static itself
+  void* static_ws = nullptr;
+  (void)static_workspace(dev, &static_ws);
 
   tri_mul_handle* h = new (std::nothrow) tri_mul_handle();
   if (!h) return TRI_MUL_ERR_OUT_OF_MEMORY;
