@@ -11,13 +11,16 @@ In order, the run
      GPU busy so that the headline runs at the clocks of sustained work;
   3. times the headline workload: W untimed warm-up steps, then exactly K steps
      between two HIP events -> ms_per_step and value;
-  4. times each kernel and each step of the headline with their own HIP events;
+  4. times each kernel of the headline alone (K back-to-back launches of its stage
+     between two HIP events, per direction), each kernel in the real K1 -> K2 -> K3
+     order (a HIP event after every kernel), and each step with its own HIP events;
   5. times the fp64 oracle on this host.
 Prints ONE JSON line:
   value         TFLOP/s over the step (matmul flops of both directions)
   roofline      the dominant kernel's algorithmic GB/s (or TFLOP/s) against the
-                MI355X peak (and against the measured peak); its duration from HIP
-                events recorded after every kernel in a separate region of K steps
+                MI355X peak (and against the measured peak); its duration from the
+                back-to-back launches of step 4 (an event between two kernels adds the
+                marker's own gap to each; the in-order figures are `kernels_in_order`)
   cpu_baseline  the fp64 oracle timed on this host (rank 0, N=1 only)
 With --chained the step is the pair update in model order instead (outgoing with
 its residual add, then incoming on that result with its residual add); the
@@ -29,7 +32,8 @@ reported in both cases). The per-kernel region always launches eagerly.
 
 With --op attention the step is triangular attention around the starting node, then
 around the ending node (each with its own weights, 4 heads of width 32) on the same
-workload's z and mask; per-kernel events time its two kernels (projection, attention).
+workload's z and mask; back-to-back launches of each stage time its two kernels
+(projection, attention).
 With --op transition the step is the pair transition instead (one kernel: LayerNorm,
 c_z -> 2 c_z -> c_z with ReLU, masked residual) on the same workload's z and mask; its
 line reports pair-updates/s with the same roofline and cpu_baseline objects.
@@ -202,7 +206,9 @@ def bench_transition(args):
         ms_step, wall = timed_steps(graph.replay, args.steps, stream)
         launch = "hipgraph"
 
-    # the kernel alone: a HIP event before and after each launch
+    # the kernel alone: the step is one launch, so the eager timed region (K back-to-back
+    # launches between two HIP events) is the kernel's own duration; per-launch events give
+    # the median
     kernels, roofline = {}, None
     pairs = B * n * n
     wk = transition_work(c_z, hidden, esz)
@@ -215,7 +221,7 @@ def bench_transition(args):
             b.record(stream)
         torch.cuda.synchronize()
         per = np.array([a.elapsed_time(b) for a, b in evs])
-        avg_ms = float(per.mean())
+        avg_ms = ms_eager
         bytes_l, flops_l = wk["bytes"] * pairs, wk["flops"] * pairs
         roofline = roofline_of("pair_transition", avg_ms, bytes_l, flops_l, dtype,
                                measured_traffic(name, "pair_transition"))
@@ -312,20 +318,23 @@ def bench_attention(args):
     work = attention_work(n, c_z, heads, hdim, 2)
     kernels, roofline = {}, None
     if not args.no_kernel_events:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-        for k in range(args.steps):
-            evs[k][0].record(stream)
-            e = 1
-            for node, mod in mods.items():
-                for st in (1, 2):
+        # each kernel alone: K back-to-back launches of its stage between two HIP events,
+        # the stages in order per node (the projection leaves what the attention reads)
+        regions = []
+        for node, mod in mods.items():
+            for st in (1, 2):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                for _ in range(args.steps):
                     mod.stage(st, z, mask, out=outs[node], node=node, workspace=ws)
-                    evs[k][e].record(stream)
-                    e += 1
+                b.record(stream)
+                regions.append((st - 1, a, b))
         torch.cuda.synchronize()
-        per = np.array([[evs[k][j].elapsed_time(evs[k][j + 1]) for j in range(4)]
-                        for k in range(args.steps)])
+        per = {0: [], 1: []}
+        for idx, a, b in regions:
+            per[idx].append(a.elapsed_time(b) / args.steps)
         for idx, kname in enumerate(("ka_project", "ka_core")):
-            samples = np.concatenate([per[:, idx], per[:, idx + 2]])  # both nodes
+            samples = np.array(per[idx])  # one average per node
             avg_ms = float(samples.mean())
             wk = work[kname]
             gbps = wk["bytes"] * pairs / (avg_ms * 1e-3) / 1e9
@@ -490,6 +499,30 @@ class TriMulBench:
                      wk["flops"] * self.pairs / (peak * 1e12))
         return 2 * t * 1e3
 
+    def kernel_times_isolated(self, reps):
+        """Each kernel alone: `reps` back-to-back launches of its stage between two HIP
+        events on the launch stream, the stages in order per direction (K1 leaves the
+        operands K2 reads, K2 the product K3 reads), all regions enqueued before one
+        synchronisation so the GPU stays busy. No event sits between two launches of a
+        region. {kernel: the per-direction average durations in ms}."""
+        import numpy as np
+        import torch
+        regions = []
+        for (direction, mod), out in zip(self.mods, self.outs):
+            for s_idx, kname in zip((1, 2, 3), KERNELS):
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(self.stream)
+                for _ in range(reps):
+                    mod.stage(s_idx, self.z, self.mask, out=out, direction=direction,
+                              workspace=self.ws)
+                b.record(self.stream)
+                regions.append((kname, a, b))
+        torch.cuda.synchronize()
+        res = {k: [] for k in KERNELS}
+        for kname, a, b in regions:
+            res[kname].append(a.elapsed_time(b) / reps)
+        return {k: np.array(v) for k, v in res.items()}
+
     def kernel_times(self, steps):
         """Each kernel's duration in the real K1 -> K2 -> K3 order: a HIP event after every
         kernel on the launch stream. The host enqueues a step (six launches, seven events)
@@ -625,7 +658,7 @@ def main():
                 wb.step()
             ms, _ = timed_steps(wb.step, args.steps, wb.stream)
             table[other] = wb.summary(ms, wb.step_times(args.steps),
-                                      wb.kernel_report(wb.kernel_times(args.steps)))
+                                      wb.kernel_report(wb.kernel_times_isolated(args.steps)))
             if wb.spec["mask"] in ("block", "lengths"):
                 table[other].update(skip_summary(wb, args))
             wb.close()
@@ -647,9 +680,11 @@ def main():
 
     # 4. per-kernel and per-step event regions of the same workload (kept apart from the
     #    timed region: every event adds a marker packet to the stream)
-    kernels, step_samples = {}, None
+    kernels, kernels_in_order, step_samples = {}, {}, None
     if not args.no_kernel_events:
-        kernels = hb.kernel_report(hb.kernel_times(args.steps))
+        kernels = hb.kernel_report(hb.kernel_times_isolated(args.steps))
+        kernels_in_order = {k: {f: v[f] for f in ("avg_us", "median_us", "hbm_frac", "mfma_frac")}
+                            for k, v in hb.kernel_report(hb.kernel_times(args.steps)).items()}
         step_samples = hb.step_times(args.steps)
 
     roofline = None
@@ -704,6 +739,7 @@ def main():
         "wall_s": round(wall, 3),
         "roofline": roofline,
         "kernels": kernels,
+        "kernels_in_order": kernels_in_order,
         "measured_peaks": peaks,
         "workloads": table,
         "cpu_baseline": cpu,
@@ -728,18 +764,25 @@ def cpu_thread_note(threads, affinity):
 
 def measured_traffic(workload, kernel):
     """HBM bytes per launch from the committed rocprofv3 FETCH_SIZE + WRITE_SIZE table,
-    or None when there is no row or the kernel source changed since it was taken."""
+    or None when there is no row or the kernel source changed since it was taken. A
+    kernel with a second form (the streamed output gate, the wide transition) has its
+    own row under that form's name; a workload runs one form, so the first row found
+    for the workload among the kernel's names is the one."""
     from pair_rep_triangle_amd.profile_summary import source_sha
+    names = {"k3_output_gate": ("k3_output_gate_stream", "k3_output_gate"),
+             "pair_transition": ("pair_transition_wide", "pair_transition")}.get(kernel, (kernel,))
     try:
         with open(TRAFFIC_FILE) as f:
-            for line in f:
-                cells = [c.strip() for c in line.strip().strip("|").split("|")]
-                if len(cells) == 6 and cells[0] == workload and cells[1] == kernel:
-                    if cells[2] != source_sha(kernel):
-                        return None
-                    return int(float(cells[5]))
+            lines = f.read().splitlines()
     except OSError:
         return None
+    for name in names:
+        for line in lines:
+            cells = [c.strip() for c in line.strip().strip("|").split("|")]
+            if len(cells) == 6 and cells[0] == workload and cells[1] == name:
+                if cells[2] != source_sha(name):
+                    return None
+                return int(float(cells[5]))
     return None
 
 
