@@ -236,12 +236,14 @@ __global__ __launch_bounds__(K3S_THREADS) void k3_output_gate_stream(
     // weight step k of the item; the buffers take the steps of all items in turn
 #pragma unroll 1
     for (int k = 0; k < STEPS; ++k, buf = buf == K3S_BUFS - 1 ? 0 : buf + 1) {
-      const unsigned int voff = k < klim ? ooff : OUT_OF_RANGE;
+      // this lane's output chunk of the step (the whole offset per lane: a store's data
+      // registers are guarded against the next write only without a scalar offset)
+      const unsigned int voff = k < klim ? ooff + 64u * (unsigned int)k : OUT_OF_RANGE;
       // with the residual: the raw z chunk this lane's output of the step is added to (out
       // may be z: it is read before the store below, by the same lane), issued before the
       // wait so that it overlaps the barrier
       chunk_t zres = {0u, 0u, 0u, 0u};
-      if constexpr (RESID) zres = load16(rzr, voff, k * 64);
+      if constexpr (RESID) zres = load16(rzr, voff, 0);
       asm volatile("" ::: "memory");
       // This step's weights are in LDS once this thread's loads of them are done and every
       // wave is past the barrier; every wave is then also done reading the previous step's
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(K3S_THREADS) void k3_output_gate_stream(
       }
       chunk_t v = pack(o, T());
       if constexpr (RESID) v = add_chunks(v, zres, T());
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)voff, k * 64, 2 /* nt */);
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)voff, 0, 2 /* nt */);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // the stream's one extra step lands before exit
