@@ -300,11 +300,11 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
       auto load_kbm = [&](int ks) {
         const int k0 = (ks < ksteps ? ks : ksteps - 1) * KT;
         if constexpr (KB == 2) {
-          mw = __builtin_amdgcn_readfirstlane(mwrow[k0 / 32]);
+          mw = (unsigned int)__builtin_amdgcn_readfirstlane(mwrow[k0 / 32]);  // zero-extended
         } else {
           const u32x2 w2 = *(const u32x2*)(mwrow + k0 / 32);
-          mw = (unsigned long long)__builtin_amdgcn_readfirstlane(w2[0]) |
-               ((unsigned long long)__builtin_amdgcn_readfirstlane(w2[1]) << 32);
+          mw = (unsigned long long)(unsigned int)__builtin_amdgcn_readfirstlane(w2[0]) |
+               ((unsigned long long)(unsigned int)__builtin_amdgcn_readfirstlane(w2[1]) << 32);
         }
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb) {
@@ -346,59 +346,58 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
                               __uint_as_float(b23 << 16), __uint_as_float(b23 & 0xffff0000u)};
             s[kb][qb] = mma16(b0, kf[kb], qf[qb], bf16());
           }
-        bool valid[KB][4];  // keys 4 KB q + 4 kb + e (read on the masked path only)
-        const unsigned long long wl = w >> (4 * KB * q);
-#pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) valid[kb][e] = (wl >> (4 * kb + e)) & 1u;
         load_kbm(ks + 1);  // the last step reloads itself (unused)
-        // The common case (every key of the step valid) runs without selects; the
-        // probabilities use the raw base-2 exponential (results below 2^-126 flush to 0).
+        // A step with masked keys first turns their scores into -inf, so that their
+        // exponentials below are exactly 0; the common case (every key of the step valid)
+        // runs no select at all (the key word is wave-uniform: a scalar branch).
+        if (w != (KB == 2 ? 0xffffffffull : ~0ull)) {
+          const unsigned long long wl = w >> (4 * KB * q);  // keys 4 KB q + 4 kb + e
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool valid = (wl >> (4 * kb + e)) & 1u;
+#pragma unroll
+              for (int qb = 0; qb < QB; ++qb) s[kb][qb][e] = valid ? s[kb][qb][e] : NEG;
+            }
+        }
+        // online softmax; the probabilities use the raw base-2 exponential (results below
+        // 2^-126 flush to 0)
         chunk_t pb[KB / 2][QB];
-        auto softmax_step = [&](auto masked) {
-          constexpr bool MASKED = decltype(masked)::value;
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            float tmax = (!MASKED || valid[0][0]) ? s[0][qb][0] : NEG;
+        for (int qb = 0; qb < QB; ++qb) {
+          float tmax = s[0][qb][0];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-              for (int e = 0; e < 4; ++e)
-                if (kb + e > 0) tmax = fmaxf(tmax, (!MASKED || valid[kb][e]) ? s[kb][qb][e] : NEG);
-            tmax = fmaxf(tmax, lane_value(tmax, lane ^ 16));
-            tmax = fmaxf(tmax, lane_value(tmax, lane ^ 32));
-            const float mnew = fmaxf(mrun[qb], tmax);
-            const float msafe = mnew == NEG ? 0.f : mnew;  // no valid key yet: every p is 0
-            // the accumulated sums follow the new maximum: 2^(old - new), 1 when it did not
-            // grow, 0 before the first valid key (old = -inf); no branch, no copies
-            const float scale = __builtin_amdgcn_exp2f(mrun[qb] - msafe);
-            lsum[qb] *= scale;
+            for (int e = 0; e < 4; ++e)
+              if (kb + e > 0) tmax = fmaxf(tmax, s[kb][qb][e]);
+          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 16));
+          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 32));
+          const float mnew = fmaxf(mrun[qb], tmax);
+          const float msafe = mnew == NEG ? 0.f : mnew;  // no valid key yet: every p is 0
+          // the accumulated sums follow the new maximum: 2^(old - new), 1 when it did not
+          // grow, 0 before the first valid key (old = -inf); no branch, no copies
+          const float scale = __builtin_amdgcn_exp2f(mrun[qb] - msafe);
+          lsum[qb] *= scale;
 #pragma unroll
-            for (int db = 0; db < 2; ++db)
+          for (int db = 0; db < 2; ++db)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) o[db][qb][e] *= scale;
-            mrun[qb] = mnew;
-            float pv[4 * KB];
+            for (int e = 0; e < 4; ++e) o[db][qb][e] *= scale;
+          mrun[qb] = mnew;
+          float pv[4 * KB];
 #pragma unroll
-            for (int kb = 0; kb < KB; ++kb)
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                const float ex = __builtin_amdgcn_exp2f(s[kb][qb][e] - msafe);
-                pv[4 * kb + e] = (!MASKED || valid[kb][e]) ? ex : 0.f;
-              }
-            float ps = pv[0];
+            for (int e = 0; e < 4; ++e)
+              pv[4 * kb + e] = __builtin_amdgcn_exp2f(s[kb][qb][e] - msafe);
+          float ps = pv[0];
 #pragma unroll
-            for (int e = 1; e < 4 * KB; ++e) ps += pv[e];
-            lsum[qb] += ps;
+          for (int e = 1; e < 4 * KB; ++e) ps += pv[e];
+          lsum[qb] += ps;
 #pragma unroll
-            for (int kh = 0; kh < KB / 2; ++kh) pb[kh][qb] = pack(pv + 8 * kh, bf16());
-          }
-        };
-        if (w == (KB == 2 ? 0xffffffffull : ~0ull))
-          softmax_step(std::false_type());
-        else
-          softmax_step(std::true_type());
+          for (int kh = 0; kh < KB / 2; ++kh) pb[kh][qb] = pack(pv + 8 * kh, bf16());
+        }
 #pragma unroll
         for (int kh = 0; kh < KB / 2; ++kh)
 #pragma unroll
