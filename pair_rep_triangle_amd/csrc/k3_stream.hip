@@ -299,7 +299,10 @@ __global__ __launch_bounds__(K3S_THREADS) void k3_output_gate_stream(
       }
       chunk_t v = pack(o, T());
       if constexpr (RESID) v = add_chunks(v, zres, T());
-      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)voff, 0, 2 /* nt */);
+      // default cache policy: a pair's 128-byte line is written in two halves one step
+      // apart, which L2 joins before it writes the line back (non-temporal stores reached
+      // HBM as half lines: 1.2x the output's bytes)
+      __builtin_amdgcn_raw_buffer_store_b128(v, ro, (int)voff, 0, 0);
     }
   }
   __builtin_amdgcn_s_waitcnt(0x0070);  // the stream's one extra step lands before exit
