@@ -61,6 +61,7 @@ def test_mask_extents_are_exact(dtype, batch, n):
     ("bf16", 2, 520, 32, 32, (257, 33)),       # extents across 256-row contraction tiles
     ("fp32", 2, 200, 64, 48, (64, 199)),
     ("fp32", 1, 45, 16, 16, (45,)),
+    ("bf16", 2, 70, 384, 128, (40, 70)),      # the wide pair track: streamed output gate
 ])
 def test_forward_with_extents_equals_plain_forward(dtype, B, n, c_z, c, lengths):
     d = make_random(B, n, c_z, c, seed=n + c, mask="block", valid=list(lengths),
