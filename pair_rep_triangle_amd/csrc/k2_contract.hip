@@ -9,6 +9,17 @@
 
 namespace trimul {
 
+// A 16-byte store through a buffer resource with device scope (cache policy sc1): the line
+// is written through this XCD's L2 as it is produced, rather than left dirty there for the
+// end-of-kernel release to write back (each XCD has its own L2, and the next kernel may read
+// X from any of them). The scalar offset stays 0: a 16-byte store still reads its data
+// registers after it issues, and the compiler only guards those registers against the next
+// write when the store has no scalar offset register.
+__device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, chunk_t v, unsigned int voff) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, 0x10);
+}
+
 // Workgroup tile 256 (i) x 128 (j), 4 waves as 2 x 2, each 128 x 64 (4 x 2 MFMA 32x32
 // tiles, 128 fp32 accumulators per lane). k advances 64 bytes per row and stage; stages
 // move from global memory straight into LDS (buffer loads with the LDS bit, no registers
@@ -228,11 +239,14 @@ __global__ __launch_bounds__(K2_THREADS, 2) void k2_contract(const T* __restrict
     constexpr int CPR = K2_BN / E;
     // the tile's part inside the padded plane (a partial last tile row or column)
     const int vrows = min(np - ti * K2_BM, K2_BM), vchunks = min(np - tj * K2_BN, K2_BN) / E;
+    // whole rows with device-scope stores (byte offsets stay below 2^25)
+    const __amdgpu_buffer_rsrc_t rx = buffer_rsrc_u32(Xb, 0xffffffffu);
 #pragma unroll 4
     for (int idx = tid; idx < K2_BM * CPR; idx += K2_THREADS) {
       const int row = idx / CPR, cc = idx - row * CPR;
       if (row < vrows && cc < vchunks)
-        st16(Xb + (size_t)row * np + cc * E, ld16(xs + row * XROW + cc * E));
+        store16_sc1(rx, ld16(xs + row * XROW + cc * E),
+                    (unsigned int)((row * np + cc * E) * (int)sizeof(T)));
     }
   } else {
     // fp32: four consecutive j per lane are one 16-byte store (inside the padded plane)

@@ -28,6 +28,9 @@ constexpr int KC_THREADS = 64 * KC_WAVES;
 constexpr int KC_QB = 4;                     // 16-query blocks per attention tile
 constexpr int KC_KB = 2;                     // 16-key blocks per attention step (2 or 4)
 constexpr int KC_MIN_SPLIT = 4;              // workgroups per stored row, at least
+// A query's softmax reference moves only when a score exceeds it by more than this (base
+// 2), so the unnormalised probabilities stay below 2^8: exact in fp32, well inside bf16.
+constexpr float KC_REBASE = 8.f;
 
 // The bias planes and the v^T planes are stored in tiles of 16 rows x 32 columns (1 KB in
 // bf16, row-major inside the tile): element (row, col) of a plane with np columns sits at
@@ -218,13 +221,15 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 // split, ...); the four waves of a workgroup take the heads (wave w: heads
 // w, w + 4). Per tile of 16 QB query columns and head, a wave runs the keys in steps of
 // 16 KB, with the step's keys permuted so that lane q owns 4 KB consecutive ones:
-//   S^T = K Q^T (key rows, query columns) with the pair bias as the accumulator start:
-//     lane (p, q) of block kb holds keys 4 KB q + 4 kb + e (e < 4) of query 16 qb + p
-//     (the K operand's row p is key 4 KB (p / 4) + 4 kb + p % 4);
+//   S^T = K Q^T (key rows, query columns) with the pair bias minus the query's softmax
+//     reference as the accumulator start: lane (p, q) of block kb holds keys
+//     4 KB q + 4 kb + e (e < 4) of query 16 qb + p (the K operand's row p is key
+//     4 KB (p / 4) + 4 kb + p % 4);
 //   online softmax per query in base 2 (log2(e) / sqrt(d) is folded into W_q and
-//     log2(e) into the bias rows), masked keys left out; the four lanes p, p^16, p^32,
-//     p^48 hold all keys of a query, so the running maximum is reduced across them and
-//     the sum is kept per lane until the end;
+//     log2(e) into the bias rows), masked keys left out. The reference is the query's
+//     largest score when it was last set and moves only when a score exceeds it by more
+//     than KC_REBASE (then the four lanes p, p^16, p^32, p^48, which hold all keys of a
+//     query, agree on the new one); the sum is kept per lane until the end;
 //   O^T += V^T P^T: each run of eight of the lane's probabilities of a query ARE its
 //     B-operand chunk once V^T's A chunk holds the same eight keys, one 16-byte run of
 //     the transposed v.
@@ -278,11 +283,17 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
       chunk_t qf[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) qf[qb] = ld16(qrow + (size_t)(qc0 + 16 * qb + p) * ATT_D + 8 * q);
+      // Per query (the same on its four lanes): the reference mref that every score is
+      // taken relative to, and whether it has been set (bit `lane` of hasref: the query
+      // has seen a valid key). lsum and o are the sum of the probabilities and O^T, both
+      // relative to 2^mref.
       f32x4 o[2][QB];
-      float mrun[QB], lsum[QB];
+      float mref[QB], lsum[QB];
+      unsigned long long hasref[QB];  // wave-uniform
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        mrun[qb] = NEG;
+        mref[qb] = 0.f;
+        hasref[qb] = 0ull;
         lsum[qb] = 0.f;
 #pragma unroll
         for (int db = 0; db < 2; ++db) o[db][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -297,6 +308,34 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
       chunk_t kf[KB], vf[KB / 2][2];
       chunk_t sb[KB / 2][QB];  // eight bf16 bias values per chunk and lane
       unsigned long long mw;  // the step's key-valid bits (bit k: key k0 + k), wave-uniform
+      // Every load of a step is a step-uniform base plus a per-lane byte offset that is the
+      // same in every step (keys advance in whole bias and V^T tiles: KT is a multiple of
+      // 32): a step adds the new bases to offsets computed once per tile.
+      // K: A row p of block kb is key 4 KB (p / 4) + 4 kb + p % 4 (block kb: + 8 kb rows of
+      // ATT_D bf16)
+      const unsigned int ko = (unsigned int)(((4 * KB * (p >> 2) + (p & 3)) * ATT_D + 8 * q) * 2);
+      // bias of query 16 qb + p, keys 4 KB q + 8 j .. + 7: tile row p of query tile row
+      // qc0 / 16 + qb, tile column k0 / 32 + c / 32 (c = 4 KB q + 8 j)
+      unsigned int bo[KB / 2];
+#pragma unroll
+      for (int j = 0; j < KB / 2; ++j) {
+        const int c = 4 * KB * q + 8 * j;
+        bo[j] = (unsigned int)(((c >> 5) * 512 + p * 32 + (c & 31)) * 2);
+      }
+      // V^T row p of block db is channel 8 (p / 4) + 4 db + p % 4, so that O^T lane (p, q)
+      // ends with channels 8q .. 8q + 7 of its query across the two blocks (one 16-byte
+      // gate load and one 16-byte staging store); half kh of the step: keys 4 KB q + 8 kh
+      // .. + 7 (the keys of the lane's probabilities pv[8 kh .. 8 kh + 7])
+      unsigned int vo[KB / 2][2];
+#pragma unroll
+      for (int kh = 0; kh < KB / 2; ++kh)
+#pragma unroll
+        for (int db = 0; db < 2; ++db) {
+          const int vr = 8 * (p >> 2) + 4 * db + (p & 3), c = 4 * KB * q + 8 * kh;
+          vo[kh][db] = (unsigned int)((((vr >> 4) * (np >> 5) + (c >> 5)) * 512 + (vr & 15) * 32 + (c & 31)) * 2);
+        }
+      const size_t bq = (size_t)np * 32;  // bytes from one query tile row of the bias to the next
+      const unsigned char* const bq0 = (const unsigned char*)(brow + (size_t)(qc0 >> 4) * (np >> 5) * 512);
       auto load_kbm = [&](int ks) {
         const int k0 = (ks < ksteps ? ks : ksteps - 1) * KT;
         if constexpr (KB == 2) {
@@ -306,35 +345,29 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
           mw = (unsigned long long)(unsigned int)__builtin_amdgcn_readfirstlane(w2[0]) |
                ((unsigned long long)(unsigned int)__builtin_amdgcn_readfirstlane(w2[1]) << 32);
         }
+        const unsigned char* const kbase = (const unsigned char*)(krow + (size_t)k0 * ATT_D);
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb) {
-          // A row p of block kb: key 4 KB (p / 4) + 4 kb + p % 4
-          kf[kb] = ld16(krow + (size_t)(k0 + 4 * KB * (p >> 2) + 4 * kb + (p & 3)) * ATT_D + 8 * q);
-        }
+        for (int kb = 0; kb < KB; ++kb) kf[kb] = ld16(kbase + ko + kb * 8 * ATT_D);
+        const unsigned char* const bbase = bq0 + (size_t)k0 * 32;  // k0 / 32 tiles of 1 KB
 #pragma unroll
         for (int j = 0; j < KB / 2; ++j)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            sb[j][qb] = ld16(brow + tile_off(qc0 + 16 * qb + p, k0 + 4 * KB * q + 8 * j, np));
+          for (int qb = 0; qb < QB; ++qb) sb[j][qb] = ld16(bbase + qb * bq + bo[j]);
       };
-      // V^T row p of block db is channel 8 (p / 4) + 4 db + p % 4, so that O^T lane (p, q)
-      // ends with channels 8q .. 8q + 7 of its query across the two blocks (one 16-byte
-      // gate load and one 16-byte staging store); half kh of the step: keys 4 KB q + 8 kh
-      // .. + 7 (the keys of the lane's probabilities pv[8 kh .. 8 kh + 7])
       auto load_v = [&](int ks) {
         const int k0 = (ks < ksteps ? ks : ksteps - 1) * KT;
+        const unsigned char* const vbase = (const unsigned char*)(vrow + (size_t)k0 * 16);
 #pragma unroll
         for (int kh = 0; kh < KB / 2; ++kh)
 #pragma unroll
-          for (int db = 0; db < 2; ++db)
-            vf[kh][db] = ld16(vrow + tile_off(8 * (p >> 2) + 4 * db + (p & 3),
-                                              k0 + 4 * KB * q + 8 * kh, np));
+          for (int db = 0; db < 2; ++db) vf[kh][db] = ld16(vbase + vo[kh][db]);
       };
       load_kbm(0);
       load_v(0);
 #pragma unroll 1
       for (int ks = 0; ks < kend; ++ks) {
         const unsigned long long w = mw;
+        // S^T relative to the reference: the accumulator starts at bias - mref
         f32x4 s[KB][QB];
 #pragma unroll
         for (int kb = 0; kb < KB; ++kb)
@@ -342,8 +375,9 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
           for (int qb = 0; qb < QB; ++qb) {
             const unsigned int b01 = sb[kb >> 1][qb][2 * (kb & 1)];
             const unsigned int b23 = sb[kb >> 1][qb][2 * (kb & 1) + 1];
-            const f32x4 b0 = {__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u),
-                              __uint_as_float(b23 << 16), __uint_as_float(b23 & 0xffff0000u)};
+            const float m = mref[qb];
+            const f32x4 b0 = {__uint_as_float(b01 << 16) - m, __uint_as_float(b01 & 0xffff0000u) - m,
+                              __uint_as_float(b23 << 16) - m, __uint_as_float(b23 & 0xffff0000u) - m};
             s[kb][qb] = mma16(b0, kf[kb], qf[qb], bf16());
           }
         load_kbm(ks + 1);  // the last step reloads itself (unused)
@@ -361,36 +395,64 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
               for (int qb = 0; qb < QB; ++qb) s[kb][qb][e] = valid ? s[kb][qb][e] : NEG;
             }
         }
-        // online softmax; the probabilities use the raw base-2 exponential (results below
-        // 2^-126 flush to 0)
-        chunk_t pb[KB / 2][QB];
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          float tmax = s[0][qb][0];
+        // Online softmax with a reference that moves only when it must: a score more than
+        // KC_REBASE above it (or the first valid key of a query) moves the query's
+        // reference to its largest score of the step and scales what it has summed so
+        // far. Otherwise the step's probabilities are 2^s directly, at most 2^KC_REBASE,
+        // with no maximum across lanes and no rescaling. The test is per lane, the branch
+        // per wave (rare after the first step). The result is the same softmax: o and l
+        // carry the same factor 2^-mref, which the division at the end removes.
+        // The lane's largest score of query block qb in this step:
+        auto lane_max = [&](int qb) {
+          float v = s[0][qb][0];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-              if (kb + e > 0) tmax = fmaxf(tmax, s[kb][qb][e]);
-          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 16));
-          tmax = fmaxf(tmax, lane_value(tmax, lane ^ 32));
-          const float mnew = fmaxf(mrun[qb], tmax);
-          const float msafe = mnew == NEG ? 0.f : mnew;  // no valid key yet: every p is 0
-          // the accumulated sums follow the new maximum: 2^(old - new), 1 when it did not
-          // grow, 0 before the first valid key (old = -inf); no branch, no copies
-          const float scale = __builtin_amdgcn_exp2f(mrun[qb] - msafe);
-          lsum[qb] *= scale;
+              if (kb + e > 0) v = fmaxf(v, s[kb][qb][e]);
+          return v;
+        };
+        bool move = false, unset = false;
 #pragma unroll
-          for (int db = 0; db < 2; ++db)
+        for (int qb = 0; qb < QB; ++qb) {
+          move |= lane_max(qb) > KC_REBASE;
+          unset |= hasref[qb] != ~0ull;
+        }
+        if (unset || __any(move)) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[db][qb][e] *= scale;
-          mrun[qb] = mnew;
+          for (int qb = 0; qb < QB; ++qb) {
+            // the query's largest score of the step relative to its reference (-inf when
+            // every key of the step is masked)
+            const float lm = lane_max(qb);
+            float rm = fmaxf(lm, lane_value(lm, lane ^ 16));
+            rm = fmaxf(rm, lane_value(rm, lane ^ 32));
+            const bool has = (hasref[qb] >> lane) & 1ull;  // a reference, and what was summed
+            const bool mv = rm > (has ? KC_REBASE : NEG);
+            const float delta = mv ? rm : 0.f;
+            // before the first valid key nothing was summed: o and lsum are 0
+            const float f = has ? __builtin_amdgcn_exp2f(-delta) : 0.f;
+            lsum[qb] *= f;
+#pragma unroll
+            for (int db = 0; db < 2; ++db)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) o[db][qb][e] *= f;
+#pragma unroll
+            for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) s[kb][qb][e] -= delta;
+            mref[qb] += delta;
+            hasref[qb] = __ballot(has || mv);
+          }
+        }
+        // probabilities in base 2 (results below 2^-126 flush to 0)
+        chunk_t pb[KB / 2][QB];
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
           float pv[4 * KB];
 #pragma unroll
           for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              pv[4 * kb + e] = __builtin_amdgcn_exp2f(s[kb][qb][e] - msafe);
+            for (int e = 0; e < 4; ++e) pv[4 * kb + e] = __builtin_amdgcn_exp2f(s[kb][qb][e]);
           float ps = pv[0];
 #pragma unroll
           for (int e = 1; e < 4 * KB; ++e) ps += pv[e];
