@@ -66,6 +66,48 @@ def test_attention_repeatable(node):
     assert torch.equal(out, again)
 
 
+@pytest.mark.parametrize("node", NODES)
+@pytest.mark.parametrize("case", ["rising", "leading_keys_masked"])
+def test_attention_moving_softmax_reference(node, case):
+    """The softmax reference of a query is set at its first valid key and moves only when
+    a score exceeds it by more than a threshold. "rising": a pair channel that grows along
+    the key index, with a large bias weight on it, makes every query's scores rise from
+    key step to key step, so the reference has to move later in the row (about once per
+    query here) with the sums scaled. "leading_keys_masked": the first 70 keys of every
+    row are masked, so the first two key steps have no valid key and the reference is set
+    in the third. The result is the plain softmax either way."""
+    n, c_z, heads = 160, 64, 2
+    note(f"attention softmax reference {case} {node} n={n}")
+    d = make_random(1, n, c_z, 16, seed=11, mask="block")
+    w = make_attention_weights(np.random.default_rng(111), c_z, heads, 32, random_affine=True)
+    z, mask = d["z"].copy(), d["mask"].copy()
+    # keys of the starting node are (i, k) with bias (j, k) and key mask (i, k); of the
+    # ending node (k, j) with bias (k, i) and key mask (k, j): the key index is the second
+    # residue axis, or the first
+    if case == "rising":
+        ramp = np.linspace(-3.0, 3.0, n, dtype=np.float32)
+        if node == "starting":
+            z[0, :, :, 0] += ramp[None, :]
+        else:
+            z[0, :, :, 0] += ramp[:, None]
+        w["w_b"] = w["w_b"].copy()
+        w["w_b"][:, 0] = 2.0
+    else:
+        if node == "starting":
+            mask[0, :, :70] = 0.0
+        else:
+            mask[0, :70, :] = 0.0
+    zt, m, z_host, m_host = to_device(dict(z=z, mask=mask), "bf16")
+    out = TriAttention(w, c_z, heads).forward(zt, m, node=node)
+    torch.cuda.synchronize()
+    got = out.to(torch.float64).cpu().numpy()
+    want = tri_attention_ref(z_host, m_host, w, node)
+    err = rel_err(got, want)
+    note(f"  rel err {err:.3e}")
+    assert np.isfinite(got).all()
+    assert err <= TOL["bf16"]
+
+
 def test_attention_writes_nothing_past_the_output():
     note("attention guard band")
     d = make_random(1, 37, 64, 16, seed=7, mask="block")
