@@ -282,6 +282,13 @@ __global__ __launch_bounds__(64 * W) void k1_input_gate(
 //     issued alongside the epilogue of the previous one.
 // In LDS a weight row is sixteen chunks with chunk c at position c ^ (row & 15), which
 // keeps the reads free of bank conflicts without padding.
+// Cache policy of the bf16 output stores: device scope (sc1). Each store instruction
+// writes whole 128-byte lines, so the lines go through this XCD's L2 to memory as they are
+// produced instead of waiting, dirty, for the end-of-kernel release (K1 51.2 against 53.8
+// us at N = 512 with the default policy; with half-lines per instruction, as before the
+// lane exchange, written-through stores took 78 us).
+constexpr int K1_STORE_POLICY = 0x10;
+
 // Issue priority from a wave's progress (level = half tiles done): the wave of a SIMD that
 // is behind issues first, so the two waves sharing a SIMD finish together instead of the
 // younger one running alone at the end.
@@ -393,6 +400,14 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
 
   const int gw = blockIdx.x * K1W_WAVES + wave;
   const int nw = gridDim.x * K1W_WAVES;
+  // this lane's output offset from its unit's row block at the tile's first pair: bf16,
+  // in bytes, channel p % 8, pairs 16q + 8 (p / 8) (the second store 8 channels on, hofs
+  // bytes further); fp32, in elements, channel p, pairs 16q. Both below 2^32: one batch
+  // item of z is under 2 GiB.
+  const unsigned int lofs =
+      sizeof(T) == 2 ? (unsigned int)((((size_t)(p & 7)) * plane + 16 * q + 8 * (p >> 3)) * 2)
+                     : (unsigned int)((size_t)p * plane + 16 * q);
+  const unsigned int hofs = (unsigned int)(8 * plane * sizeof(T));
   Pre f;
   // ---- the group's weights -> LDS. The handle keeps each group's weights as the LDS
   // image itself (swizzled rows, then their start values), so the copy is flat: each
@@ -455,8 +470,9 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
     coords(t, bb, r, s0);
     int opaque;  // keeps the loop-invariant LDS reads inside the loop
     asm volatile("s_mov_b32 %0, 0" : "=s"(opaque));
-    // this lane's 16 pairs of channel p (the unit's channel block is added per unit)
-    const size_t tbase = (size_t)bb * c * plane + (size_t)p * plane + (size_t)r * np + s0 + 16 * q;
+    // the tile's first pair in channel 0 (wave-uniform; the unit's channel block is added
+    // per unit, the lane's channel and pairs in store16)
+    const size_t tbase = (size_t)bb * c * plane + (size_t)r * np + s0;
     const T* const wlt = wl + opaque;
     const float* const tlt = tl + opaque;
 
@@ -492,14 +508,34 @@ __global__ __launch_bounds__(K1W_THREADS) void k1_input_gate_waves(
       const bool isb = u >= cblocks;  // units 0 .. c/16-1 are a, the rest b
       return (isb ? b_out : a_out) + tbase + (size_t)((isb ? u - cblocks : u) * 16) * plane;
     };
-    // 16 outputs (pairs 16q .. 16q+15 of channel p) -> two (bf16) or four (fp32) 16-byte
-    // stores
-    auto store16 = [&](T* dst, const float (&o)[16]) {
+    // 16 outputs (pairs 16q .. 16q+15 of channel p) of the unit whose row block starts at
+    // ub. bf16: lanes p and p + 8 of a row swap a chunk, so that each of the two stores
+    // writes whole 128-byte lines: the first holds channel p % 8 (pairs 16q .. +7 from
+    // lanes p < 8, 16q + 8 .. +15 from lanes p >= 8), the second channel p % 8 + 8.
+    // fp32: four 16-byte stores of the lane's own pairs.
+    auto store16 = [&](T* ub, const float (&o)[16]) {
       T ot[16];
 #pragma unroll
       for (int j = 0; j < 16; j += 4) store4(ot + j, o[j], o[j + 1], o[j + 2], o[j + 3]);
+      if constexpr (sizeof(T) == 2) {
+        const chunk_t c0 = ld16(ot), c1 = ld16(ot + 8);
+        chunk_t lo, hi;
+        constexpr int kRowRor8 = 0x128;  // DPP: lane i of a row of 16 reads lane i ^ 8
 #pragma unroll
-      for (int k = 0; k < NOUT; ++k) st16(dst + k * E, ld16(ot + k * E));
+        for (int d = 0; d < 4; ++d) {
+          // lanes p >= 8 (banks 2, 3) take chunk 1 of lane p - 8; lanes p < 8 chunk 0 of p + 8
+          lo[d] = (unsigned int)__builtin_amdgcn_update_dpp((int)c0[d], (int)c1[d], kRowRor8, 0xf, 0xc, false);
+          hi[d] = (unsigned int)__builtin_amdgcn_update_dpp((int)c1[d], (int)c0[d], kRowRor8, 0xf, 0x3, false);
+        }
+        const __amdgpu_buffer_rsrc_t rd = buffer_rsrc_u32(ub, 0xffffffffu);
+        typedef __attribute__((ext_vector_type(4))) int i32x4;
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, lo), rd, (int)lofs, 0, K1_STORE_POLICY);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, hi), rd, (int)(lofs + hofs), 0, K1_STORE_POLICY);
+      } else {
+        T* const dst = ub + lofs;
+#pragma unroll
+        for (int k = 0; k < NOUT; ++k) st16(dst + k * E, ld16(ot + k * E));
+      }
     };
     // m * p / (1 + 2^g) of one unit, on its own (the last unit of a tile)
     auto emit = [&](T* dst, const AUnit& acc, auto masked) {
