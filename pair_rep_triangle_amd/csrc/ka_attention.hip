@@ -39,6 +39,16 @@ __device__ __forceinline__ size_t tile_off(int row, int col, int np) {
   return ((size_t)(row >> 4) * (np >> 5) + (col >> 5)) * 512 + (row & 15) * 32 + (col & 31);
 }
 
+// A 16-byte store with device scope (cache policy sc1) through a resource on a
+// wave-uniform base: written through this XCD's L2 as produced rather than left dirty for
+// the end-of-kernel release (every store instruction of ka_project writes whole lines).
+// The scalar offset stays 0 (a 16-byte store reads its data registers after it issues; the
+// compiler guards them only for stores without a scalar offset register).
+__device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, chunk_t v, unsigned int voff) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, 0x10);
+}
+
 // ---------------------------------------------------------------------------------------
 // ka_project. A wave tile is 32 consecutive stored columns (two 16-pair subtiles) of one
 // stored row; row p of subtile st is the tile's pair 8 (p / 4) + 4 st + p % 4. z arrives
@@ -160,7 +170,8 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
           if (which == 2) v[e] = __builtin_amdgcn_rcpf(1.f + exp2f(v[e]));
         }
         const int c = c0 + pair_of(st);
-        st16(dst + ((rowbase + h) * np + c) * ATT_D + 8 * q, pack(v, bf16()));
+        store16_sc1(buffer_rsrc_u32(dst + (rowbase + h) * np * ATT_D, 0xffffffffu),
+                    pack(v, bf16()), (unsigned int)((c * ATT_D + 8 * q) * 2));
       }
     };
     // v and bias units: W rows as B. Lane (p, q): pairs c0 + 8q + 4 st .. +3 (rows 4q .. 4q
@@ -172,8 +183,10 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 #pragma unroll
       for (int ks = 0; ks < KZ; ++ks) wb[ks] = ld16(wrow + ks * KG);
       const float t0 = tl[row0 + p + opaque];
-      const int o = bias ? p : row0 - 3 * hd + p;
-      const int h = o / ATT_D, dd = o - h * ATT_D;
+      // v output row0 - 3 hd + p: its head is the same for the block's 16 rows (row0 - 3 hd
+      // is a multiple of 16, a head 32 rows), so the store's base stays wave-uniform
+      const int o0 = row0 - 3 * hd;
+      const int h = o0 / ATT_D, dd = o0 - h * ATT_D + p;
       float v[8];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
@@ -188,7 +201,8 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
         if (p < heads)
           st16(bo + ((size_t)b * heads + p) * np * np + tile_off(r, c, np), pack(v, bf16()));
       } else {
-        st16(vto + (rowbase + h) * ATT_D * np + tile_off(dd, c, np), pack(v, bf16()));
+        store16_sc1(buffer_rsrc_u32(vto + (rowbase + h) * ATT_D * np, 0xffffffffu),
+                    pack(v, bf16()), (unsigned int)(tile_off(dd, c, np) * 2));
       }
     };
 #pragma unroll 1
