@@ -38,13 +38,47 @@ inline AttnWorkspace att_workspace(int batch, int n, int heads) {
   return w;
 }
 
-// Projection weights as the projection kernel's LDS image: rows [q | k | g | v] (H*d each)
-// then 16 bias rows (H used), each c_z + 8 bf16 (one 16-byte chunk of padding); then the
-// fp32 start value of every row (W beta, plus b_g for the gate rows).
+// Projection weights as the projection kernel's LDS images: rows [q | k | g | v] (H*d each)
+// then 16 bias rows (H used), each c_z + 8 bf16 (one 16-byte chunk of padding), and the
+// fp32 start value of every row (W beta, plus b_g for the gate rows). The rows are cut
+// into parts that each fit one workgroup's LDS (one part up to c_z = 128 at 4 heads); a
+// part is a contiguous row range [lo, hi) of whole heads of q, k and g (32 rows) and whole
+// 16-row units of v and the bias, stored as its rows then its start values, and the
+// projection kernel runs once per part (each run reads z again).
 inline int att_proj_rows(int heads) { return 4 * heads * ATT_D + 16; }
+constexpr size_t ATT_LDS_MAX = 160 * 1024;
+inline size_t att_part_bytes(int cz, int rows) {
+  return ((size_t)rows * (cz + 8) * 2 + (size_t)rows * 4 + 15) / 16 * 16;
+}
+// The parts' row boundaries, lo of part i at bounds[i] (bounds[count] = all rows); count 0
+// when a single block does not fit.
+struct AttnParts {
+  int count;
+  int bounds[64];
+};
+inline AttnParts att_proj_parts(int cz, int heads) {
+  AttnParts pt{};
+  const int hd = heads * ATT_D, rows = att_proj_rows(heads);
+  int lo = 0, at = 0;
+  pt.bounds[0] = 0;
+  while (at < rows) {
+    const int block = at < 3 * hd ? 32 : 16;  // a q, k or gate head; a v unit or the bias
+    if (att_part_bytes(cz, at + block - lo) > ATT_LDS_MAX) {
+      if (at == lo || pt.count + 1 >= 63) return AttnParts{};
+      pt.bounds[++pt.count] = at;
+      lo = at;
+      continue;
+    }
+    at += block;
+  }
+  pt.bounds[++pt.count] = rows;
+  return pt;
+}
 inline size_t att_proj_image_bytes(int cz, int heads) {
-  const size_t rows = (size_t)att_proj_rows(heads);
-  return rows * (cz + 8) * 2 + rows * 4;
+  const AttnParts pt = att_proj_parts(cz, heads);
+  size_t total = 0;
+  for (int i = 0; i < pt.count; ++i) total += att_part_bytes(cz, pt.bounds[i + 1] - pt.bounds[i]);
+  return total;
 }
 // Output weights as the attention kernel's LDS image: W_o [c_z][H*d + 8] bf16, then b_o
 // [c_z] fp32; the attention kernel adds its staging rows [64][H*d + 8] bf16 after them.
@@ -67,9 +101,8 @@ struct AttnArgs {
 
 inline bool attention_supported(int cz, int heads, int d) {
   if (d != ATT_D || heads < 1 || heads > 8) return false;
-  if (cz % 32 || cz < 32 || cz > 128) return false;
-  return att_proj_image_bytes(cz, heads) <= 160 * 1024 &&
-         att_core_lds_bytes(cz, heads) <= 160 * 1024;
+  if (cz % 32 || cz < 32 || cz > 384) return false;
+  return att_proj_parts(cz, heads).count > 0 && att_core_lds_bytes(cz, heads) <= ATT_LDS_MAX;
 }
 
 // stages: 1 = projection, 2 = attention and output, 3 = both

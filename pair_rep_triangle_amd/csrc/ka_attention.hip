@@ -63,11 +63,15 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
     const bf16* __restrict__ z, const bf16* __restrict__ mask, const chunk_t* __restrict__ image,
     int image_chunks, bf16* __restrict__ qo, bf16* __restrict__ ko, bf16* __restrict__ go,
     bf16* __restrict__ vto, bf16* __restrict__ bo, unsigned int* __restrict__ mwo, int batch, int n,
-    int np, int heads, int ending, int mask_all) {
+    int np, int heads, int ending, int mask_all, int lo, int hi) {
   constexpr int E = 8, KG = 32, CZ = KZ * KG, RS = CZ + 8;  // LDS row stride (elements)
+  // up to four chunk groups the next tile's z is fetched while this one computes; wider
+  // pairs fetch it after the tile (both copies would not fit the registers)
+  constexpr bool PREFETCH = KZ <= 4;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int hd = heads * ATT_D;
-  const int rows = 4 * hd + 16;
+  // this launch's part of the projection rows: [lo, hi), as rows then start values
+  const int rows = hi - lo;
   const bf16* const wl = (const bf16*)smem;
   const float* const tl = (const float*)(smem + (size_t)rows * RS * 2);  // start values
 
@@ -133,7 +137,7 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
       for (int ks = 0; ks < KZ; ++ks) za[st][ks] = f.zv[st][ks];
       normalize_operand_row<KZ>(za[st], CZ, lane, bf16());
     }
-    fetch(t + nw, f);  // the next tile's loads have this tile's MFMAs to land
+    if constexpr (PREFETCH) fetch(t + nw, f);  // the next tile's loads have this tile's MFMAs to land
 
     const size_t rowbase = ((size_t)b * np + r) * heads;  // [b][r][h] of q, k, g, v^T
     int opaque;  // keeps the loop-invariant LDS reads inside the tile loop
@@ -144,15 +148,17 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
     // so after both halves lane (p, q) holds channels 8q .. 8q + 7 of the head for pair
     // c0 + 16 st + p, and one 16-byte store per lane writes the pair's whole 64-byte row.
     auto head_a = [&](int row0, int which, bf16* dst) {
+      if (row0 < lo || row0 + 32 > hi) return;  // another part's head (uniform)
       const int h = (row0 - which * hd) / ATT_D;
+      const int lr = row0 - lo;  // the head's first row in this part's image
       f32x4 acc[2][2];  // [half][st]
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
-        const bf16* const wrow = wl + (row0 + 16 * hf + p) * RS + q * E + opaque;
+        const bf16* const wrow = wl + (lr + 16 * hf + p) * RS + q * E + opaque;
         chunk_t wa[KZ];
 #pragma unroll
         for (int ks = 0; ks < KZ; ++ks) wa[ks] = ld16(wrow + ks * KG);
-        const f32x4 t0 = ld16f(tl + row0 + 16 * hf + 4 * q + opaque);
+        const f32x4 t0 = ld16f(tl + lr + 16 * hf + 4 * q + opaque);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           acc[hf][st] = t0;
@@ -178,11 +184,13 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
     // + 3 of subtile st), output 16u' + p of the block; the two subtiles leave as one
     // 16-byte store of pairs c0 + 8q .. c0 + 8q + 7.
     auto unit_b = [&](int row0, bool bias) {
-      const bf16* const wrow = wl + (row0 + p) * RS + q * E + opaque;
+      if (row0 < lo || row0 + 16 > hi) return;  // another part's unit (uniform)
+      const int lr = row0 - lo;
+      const bf16* const wrow = wl + (lr + p) * RS + q * E + opaque;
       chunk_t wb[KZ];
 #pragma unroll
       for (int ks = 0; ks < KZ; ++ks) wb[ks] = ld16(wrow + ks * KG);
-      const float t0 = tl[row0 + p + opaque];
+      const float t0 = tl[lr + p + opaque];
       // v output row0 - 3 hd + p: its head is the same for the block's 16 rows (row0 - 3 hd
       // is a multiple of 16, a head 32 rows), so the store's base stays wave-uniform
       const int o0 = row0 - 3 * hd;
@@ -227,6 +235,7 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
       word |= (unsigned int)((v0 >> (4 * g)) & 0xfu) << (8 * g) |
               (unsigned int)((v1 >> (4 * g)) & 0xfu) << (8 * g + 4);
     if (lane == 0) mwo[((size_t)b * np + r) * (np / 32) + c0 / 32] = word;
+    if constexpr (!PREFETCH) fetch(t + nw, f);
   }
 }
 
@@ -548,27 +557,40 @@ static hipError_t launch_attention_kz(const AttnArgs& a, int stages, hipStream_t
   bf16* bias = (bf16*)(ws + L.bias);
   unsigned int* mw = (unsigned int*)(ws + L.ms);
 
-  // projection: persistent waves over 32-pair tiles of the padded stored grid
+  // projection: persistent waves over 32-pair tiles of the padded stored grid, one launch
+  // per part of the projection rows
   if (stages & 1) {
-    const size_t lds = att_proj_image_bytes(a.cz, a.heads);
-    if (lds % 16) return hipErrorInvalidValue;
+    const AttnParts parts = att_proj_parts(a.cz, a.heads);
+    if (parts.count < 1) return hipErrorInvalidValue;
+    size_t lds_max = 0;
+    for (int i = 0; i < parts.count; ++i) {
+      const size_t b = att_part_bytes(a.cz, parts.bounds[i + 1] - parts.bounds[i]);
+      lds_max = b > lds_max ? b : lds_max;
+    }
+    if (lds_max > ATT_LDS_MAX) return hipErrorInvalidValue;
     auto fn = ka_project<KZ>;
     static std::atomic<int> granted{0};
-    hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds);
+    hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds_max);
     if (e != hipSuccess) return e;
-    static std::atomic<int> occ{0};
-    static std::atomic<size_t> occ_lds{0};
-    const int per_cu = resident_blocks((const void*)fn, KA_THREADS, lds, occ, occ_lds);
     const long long tiles = (long long)a.batch * np * (np / KA_TW);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    const long long need = (tiles + KA_WAVES - 1) / KA_WAVES;
-    const long long cap = (long long)a.num_cus * per_cu;
-    const int blocks = (int)(need < cap ? need : cap);
-    hipLaunchKernelGGL(fn, dim3(blocks), dim3(KA_THREADS), lds, st, (const bf16*)a.z,
-                       (const bf16*)a.mask, (const chunk_t*)a.proj_image, (int)(lds / 16), q, k,
-                       g, vt, bias, mw, a.batch, a.n, np, a.heads, a.node, a.mask_all);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    const unsigned char* image = (const unsigned char*)a.proj_image;
+    for (int i = 0; i < parts.count; ++i) {
+      const size_t lds = att_part_bytes(a.cz, parts.bounds[i + 1] - parts.bounds[i]);
+      static std::atomic<int> occ{0};
+      static std::atomic<size_t> occ_lds{0};
+      const int per_cu = resident_blocks((const void*)fn, KA_THREADS, lds, occ, occ_lds);
+      const long long need = (tiles + KA_WAVES - 1) / KA_WAVES;
+      const long long cap = (long long)a.num_cus * per_cu;
+      const int blocks = (int)(need < cap ? need : cap);
+      hipLaunchKernelGGL(fn, dim3(blocks), dim3(KA_THREADS), lds, st, (const bf16*)a.z,
+                         (const bf16*)a.mask, (const chunk_t*)image, (int)(lds / 16), q, k, g, vt,
+                         bias, mw, a.batch, a.n, np, a.heads, a.node, a.mask_all,
+                         parts.bounds[i], parts.bounds[i + 1]);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+      image += lds;
+    }
   }
   // attention: one workgroup per stored row
   if (stages & 2) {
@@ -607,6 +629,14 @@ hipError_t launch_attention(const AttnArgs& a, int stages, hipStream_t st) {
     case 2: return launch_attention_kz<2>(a, stages, st);
     case 3: return launch_attention_kz<3>(a, stages, st);
     case 4: return launch_attention_kz<4>(a, stages, st);
+    case 5: return launch_attention_kz<5>(a, stages, st);
+    case 6: return launch_attention_kz<6>(a, stages, st);
+    case 7: return launch_attention_kz<7>(a, stages, st);
+    case 8: return launch_attention_kz<8>(a, stages, st);
+    case 9: return launch_attention_kz<9>(a, stages, st);
+    case 10: return launch_attention_kz<10>(a, stages, st);
+    case 11: return launch_attention_kz<11>(a, stages, st);
+    case 12: return launch_attention_kz<12>(a, stages, st);
     default: return hipErrorInvalidValue;
   }
 }

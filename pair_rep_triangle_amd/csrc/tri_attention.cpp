@@ -53,14 +53,35 @@ int tri_attn_create(const tri_attn_weights* w, int c_z, int heads, int head_dim,
   if (dtype != TRI_MUL_BF16) return TRI_MUL_ERR_UNSUPPORTED;
   if (!trimul::attention_supported(c_z, heads, head_dim)) return TRI_MUL_ERR_UNSUPPORTED;
   // the host image first (no device needed), then the device
-  const int hd = heads * head_dim, rows = trimul::att_proj_rows(heads);
+  const int hd = heads * head_dim;
   const size_t rs = (size_t)c_z + 8, ors = (size_t)hd + 8;  // row strides (bf16 elements)
+  const trimul::AttnParts parts = trimul::att_proj_parts(c_z, heads);
   const size_t pimg = trimul::att_proj_image_bytes(c_z, heads);
   const size_t oimg = trimul::att_out_image_bytes(c_z, heads);
   const size_t total = align256(pimg) + align256(oimg) + 256;
   std::vector<unsigned char> host(total, 0);
   unsigned char* hp = host.data();
-  float* hpt = (float*)(hp + (size_t)rows * rs * 2);  // projection start values
+  // projection row o and its start value, in the image of the part that holds it: the
+  // part's rows, then its start values
+  auto prow = [&](int o) {
+    size_t base = 0;
+    int i = 0;
+    while (o >= parts.bounds[i + 1]) {
+      base += trimul::att_part_bytes(c_z, parts.bounds[i + 1] - parts.bounds[i]);
+      ++i;
+    }
+    return hp + base + (size_t)(o - parts.bounds[i]) * rs * 2;
+  };
+  auto pstart = [&](int o) {
+    size_t base = 0;
+    int i = 0;
+    while (o >= parts.bounds[i + 1]) {
+      base += trimul::att_part_bytes(c_z, parts.bounds[i + 1] - parts.bounds[i]);
+      ++i;
+    }
+    const size_t prows = (size_t)(parts.bounds[i + 1] - parts.bounds[i]);
+    return (float*)(hp + base + prows * rs * 2) + (o - parts.bounds[i]);
+  };
   unsigned char* ho = hp + align256(pimg);
   float* hob = (float*)(ho + (size_t)c_z * ors * 2);  // b_o
   unsigned char* hone = ho + align256(oimg);
@@ -76,18 +97,17 @@ int tri_attn_create(const tri_attn_weights* w, int c_z, int heads, int head_dim,
     const int i = o % 16, hf = (o / 16) % 2;
     const int src = o / head_dim * head_dim + 8 * (i >> 2) + 4 * hf + (i & 3);
     const size_t W = (size_t)src * c_z;
-    fold_row(w->w_q + W, w->ln_gamma, w->ln_beta, 0.0, c_z, qs, hp + (size_t)o * rs * 2, hpt + o);
-    fold_row(w->w_k + W, w->ln_gamma, w->ln_beta, 0.0, c_z, 1.0, hp + (size_t)(hd + o) * rs * 2,
-             hpt + hd + o);
+    fold_row(w->w_q + W, w->ln_gamma, w->ln_beta, 0.0, c_z, qs, prow(o), pstart(o));
+    fold_row(w->w_k + W, w->ln_gamma, w->ln_beta, 0.0, c_z, 1.0, prow(hd + o), pstart(hd + o));
     fold_row(w->w_g + W, w->ln_gamma, w->ln_beta, w->b_g ? (double)w->b_g[src] : 0.0, c_z,
-             -kLog2e, hp + (size_t)(2 * hd + o) * rs * 2, hpt + 2 * hd + o);
+             -kLog2e, prow(2 * hd + o), pstart(2 * hd + o));
     // v rows in channel order (the v^T unit stores one channel per lane)
-    fold_row(w->w_v + (size_t)o * c_z, w->ln_gamma, w->ln_beta, 0.0, c_z, 1.0,
-             hp + (size_t)(3 * hd + o) * rs * 2, hpt + 3 * hd + o);
+    fold_row(w->w_v + (size_t)o * c_z, w->ln_gamma, w->ln_beta, 0.0, c_z, 1.0, prow(3 * hd + o),
+             pstart(3 * hd + o));
   }
   for (int h = 0; h < heads; ++h)
     fold_row(w->w_b + (size_t)h * c_z, w->ln_gamma, w->ln_beta, 0.0, c_z, kLog2e,
-             hp + (size_t)(4 * hd + h) * rs * 2, hpt + 4 * hd + h);
+             prow(4 * hd + h), pstart(4 * hd + h));
   // output image: W_o [c_z][hd] rows and b_o, permuted per group of 32 output channels
   // as the attention kernel's output projection reads them: image row 16 hf + i of a
   // group (half hf, MFMA row i = 4q + rr) is channel 8q + 4 hf + rr of the group

@@ -36,6 +36,11 @@ def _run(B, n, c_z, heads, mask, seed, node, use_mask=True):
     (1, 70, 32, 1, "random_residues"),   # fully padded residues: queries with no valid key
     (1, 64, 96, 3, "ones"),              # three heads (a wave of the workgroup idles)
     (1, 129, 64, 8, "random_pairs"),     # eight heads: each wave runs two
+    (1, 45, 128, 8, "ones"),             # projection weights in two parts
+    (1, 70, 160, 2, "random_residues"),  # five chunk groups: no z prefetch
+    (2, 33, 256, 4, "block"),            # projection weights in two parts
+    (1, 40, 384, 4, "random_pairs"),     # the wide pair track: three parts, twelve groups
+    (1, 160, 384, 4, "block"),           # the same over several tiles and key steps
 ])
 def test_attention_full_output(node, B, n, c_z, heads, mask):
     note(f"attention {node} B={B} n={n} cz={c_z} heads={heads} {mask}")
