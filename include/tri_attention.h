@@ -57,10 +57,9 @@ typedef struct tri_attn_handle tri_attn_handle;
  * softmax runs in base 2), and stores the weights on the device in the kernels' order.
  * Supported: dtype TRI_MUL_BF16 (storage of z, out and the intermediates; fp32
  * accumulation and softmax); c_z a multiple of 32 up to 384; head width d = 32;
- * heads 1..8, with the output projection's weights and staging (2 (c_z + 64)(32 H + 8)
- * + 4 c_z bytes) within 160 KB (so 4 heads at c_z = 384, 8 heads up to c_z = 224). The
- * projection weights that do not fit one workgroup's LDS are split into parts, and the
- * projection runs once per part. The weights are copied: the host arrays may be freed on
+ * heads 1..8. Projection weights that do not fit one workgroup's LDS are split into
+ * parts, and the projection runs once per part; the output projection's weights pass
+ * through LDS 128 rows at a time. The weights are copied: the host arrays may be freed on
  * return.
  * Errors: INVALID_ARG (NULL w / matrix / out, sizes < 1), UNSUPPORTED (other shapes or
  * dtype), UNSUPPORTED_DEVICE, OUT_OF_MEMORY, HIP. On error *out is NULL. */

@@ -80,13 +80,17 @@ inline size_t att_proj_image_bytes(int cz, int heads) {
   for (int i = 0; i < pt.count; ++i) total += att_part_bytes(cz, pt.bounds[i + 1] - pt.bounds[i]);
   return total;
 }
-// Output weights as the attention kernel's LDS image: W_o [c_z][H*d + 8] bf16, then b_o
-// [c_z] fp32; the attention kernel adds its staging rows [64][H*d + 8] bf16 after them.
+// Output weights as the attention kernel's image: W_o [c_z][H*d + 8] bf16, then b_o
+// [c_z] fp32. The kernel holds at most ATT_WO_ROWS rows of it (and their b_o) in LDS at a
+// time (all of it up to c_z = 128, copied once), followed by its staging rows
+// [64][H*d + 8] bf16.
+constexpr int ATT_WO_ROWS = 128;
 inline size_t att_out_image_bytes(int cz, int heads) {
   return (size_t)cz * (heads * ATT_D + 8) * 2 + (size_t)cz * 4;
 }
 inline size_t att_core_lds_bytes(int cz, int heads) {
-  return att_out_image_bytes(cz, heads) + (size_t)64 * (heads * ATT_D + 8) * 2;
+  const size_t rows = cz < ATT_WO_ROWS ? (size_t)cz : (size_t)ATT_WO_ROWS;
+  return rows * (heads * ATT_D + 8) * 2 + rows * 4 + (size_t)64 * (heads * ATT_D + 8) * 2;
 }
 
 struct AttnArgs {

@@ -259,18 +259,22 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 // Then o = O^T / l * gate goes to LDS as [query][h*d + channel]; after a barrier the
 // waves split the output channels: out^T = W_o o^T + b_o with W_o rows from LDS as A.
 template <int KZ, int QB, int KB>
-__global__ __launch_bounds__(KC_THREADS) void ka_core(
+__global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void ka_core(
     const bf16* __restrict__ qi, const bf16* __restrict__ ki, const bf16* __restrict__ gi,
     const bf16* __restrict__ vti, const bf16* __restrict__ bi, const unsigned int* __restrict__ mwi,
     const chunk_t* __restrict__ image, int image_chunks, bf16* __restrict__ out, int n, int np,
     int heads, int ending, int rows, int split) {
   constexpr int CZ = KZ * 32;
   constexpr int QT = 16 * QB;  // queries per tile
+  // W_o lives in LDS a slice of ATT_WO_ROWS output rows at a time: the whole matrix up to
+  // c_z = 128 (copied once), else slice after slice for every query tile
+  constexpr int SROWS = CZ < ATT_WO_ROWS ? CZ : ATT_WO_ROWS;
+  constexpr int NSLICE = (CZ + SROWS - 1) / SROWS;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int hd = heads * ATT_D, os_stride = hd + 8;
-  const bf16* const wo = (const bf16*)smem;                                 // [CZ][hd + 8]
-  const float* const bo = (const float*)(smem + (size_t)CZ * os_stride * 2);  // [CZ]
-  bf16* const os = (bf16*)(smem + (size_t)CZ * os_stride * 2 + CZ * 4);       // [64][hd + 8]
+  const bf16* const wo = (const bf16*)smem;                                    // [SROWS][hd + 8]
+  const float* const bo = (const float*)(smem + (size_t)SROWS * os_stride * 2);  // [SROWS]
+  bf16* const os = (bf16*)(smem + (size_t)SROWS * os_stride * 2 + SROWS * 4);    // [64][hd + 8]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -282,8 +286,10 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
   const int share = w8 >> 3, row = grp * 8 + (w8 & 7);
   if (row >= rows) return;  // the last group of eight may be partial (whole workgroup)
   const int b = row / n, r = row - b * n;
-  copy_image<KC_THREADS>(image, (chunk_t*)smem, image_chunks, tid, []() {});
-  __syncthreads();
+  if constexpr (NSLICE == 1) {
+    copy_image<KC_THREADS>(image, (chunk_t*)smem, image_chunks, tid, []() {});
+    __syncthreads();
+  }
 
   constexpr int KT = 16 * KB;  // keys per step
   const int ksteps = (n + KT - 1) / KT;  // key steps past n would be all masked
@@ -514,13 +520,30 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
     // handle stores W_o's rows (and b_o) permuted per group: row 4q + rr of half hf is
     // channel 8q + 4 hf + rr, so lane (p, q) ends with channels 32g + 8q .. + 7 of query
     // 16 qb + p and writes them as one 16-byte store.
-    for (int g = wave; g < CZ / 32; g += KC_WAVES) {
+#pragma unroll 1
+    for (int sl = 0; sl < NSLICE; ++sl) {
+      const int g0 = sl * (SROWS / 32);  // the slice's first group
+      if constexpr (NSLICE > 1) {
+        // the slice's W_o rows and b_o values into LDS (after every wave is done with the
+        // previous slice)
+        if (sl > 0) __syncthreads();
+        const int srows = CZ - 32 * g0 < SROWS ? CZ - 32 * g0 : SROWS;
+        const chunk_t* const src = (const chunk_t*)((const unsigned char*)image +
+                                                    (size_t)32 * g0 * os_stride * 2);
+        const int wchunks = srows * os_stride * 2 / 16;
+        for (int i = tid; i < wchunks; i += KC_THREADS) ((chunk_t*)smem)[i] = src[i];
+        const chunk_t* const bsrc = (const chunk_t*)((const unsigned char*)image +
+                                                     (size_t)CZ * os_stride * 2 + 32 * g0 * 4);
+        for (int i = tid; i < srows / 4; i += KC_THREADS) ((chunk_t*)bo)[i] = bsrc[i];
+        __syncthreads();
+      }
+    for (int g = g0 + wave; g < g0 + SROWS / 32 && g < CZ / 32; g += KC_WAVES) {
 #pragma unroll 1
       for (int qb = 0; qb < QB; ++qb) {  // one query block at a time: few live registers
         f32x4 acc[2];
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          const int u = 2 * g + hf;
+          const int u = 2 * (g - g0) + hf;  // the unit's rows in the slice
           acc[hf] = ld16f(bo + 16 * u + 4 * q);
           for (int kk = 0; kk < hd / 32; ++kk)
             acc[hf] = mma16(acc[hf], ld16(wo + (16 * u + p) * os_stride + 32 * kk + 8 * q),
@@ -538,6 +561,7 @@ __global__ __launch_bounds__(KC_THREADS) void ka_core(
               pack(v, bf16()), (chunk_t*)(out + (((size_t)b * n + x) * n + y) * CZ + 32 * g + 8 * q));
         }
       }
+    }
     }
     __syncthreads();
   }

@@ -41,6 +41,7 @@ def _run(B, n, c_z, heads, mask, seed, node, use_mask=True):
     (2, 33, 256, 4, "block"),            # projection weights in two parts
     (1, 40, 384, 4, "random_pairs"),     # the wide pair track: three parts, twelve groups
     (1, 160, 384, 4, "block"),           # the same over several tiles and key steps
+    (1, 50, 384, 8, "random_residues"),  # eight heads: six parts; W_o in three slices
 ])
 def test_attention_full_output(node, B, n, c_z, heads, mask):
     note(f"attention {node} B={B} n={n} cz={c_z} heads={heads} {mask}")

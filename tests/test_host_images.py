@@ -66,7 +66,8 @@ def test_transition_create_builds_images(lib, c_z, hidden, dtype):
 
 
 @pytest.mark.parametrize("c_z,heads,d", [(64, 2, 32), (128, 4, 32), (96, 1, 32), (128, 8, 32),
-                                          (160, 2, 32), (256, 4, 32), (384, 4, 32)])
+                                          (160, 2, 32), (256, 4, 32), (384, 4, 32),
+                                          (384, 8, 32)])
 def test_attention_create_builds_images(lib, c_z, heads, d):
     s, keep = _struct(tm.AttentionWeights,
                       make_attention_weights(np.random.default_rng(c_z), c_z, heads, d,
