@@ -57,23 +57,28 @@ __device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, chunk_t v,
 // permuted per head: lane (p, q) ends with channels 8q..8q+7 of its pair) and the A
 // operand of the v and bias units (W rows as B: lane (p, q) ends with stored columns
 // 8q..8q+7 of output p). Every result leaves as one 16-byte store per lane.
-// The weights (LDS image, rows padded by 16 bytes) are loaded once per workgroup.
-template <int KZ>
+// The weights (LDS image, rows padded by 16 bytes) are loaded once per workgroup. When
+// they come in several parts (STREAM), the workgroup's waves take their tiles together
+// and the parts pass through LDS one after the other for every round of tiles, with a
+// barrier before and after each part's copy; z is read once.
+template <int KZ, bool STREAM>
 __global__ __launch_bounds__(KA_THREADS) void ka_project(
     const bf16* __restrict__ z, const bf16* __restrict__ mask, const chunk_t* __restrict__ image,
-    int image_chunks, bf16* __restrict__ qo, bf16* __restrict__ ko, bf16* __restrict__ go,
-    bf16* __restrict__ vto, bf16* __restrict__ bo, unsigned int* __restrict__ mwo, int batch, int n,
-    int np, int heads, int ending, int mask_all, int lo, int hi) {
+    bf16* __restrict__ qo, bf16* __restrict__ ko, bf16* __restrict__ go, bf16* __restrict__ vto,
+    bf16* __restrict__ bo, unsigned int* __restrict__ mwo, int batch, int n, int np, int heads,
+    int ending, int mask_all, AttnParts parts) {
   constexpr int E = 8, KG = 32, CZ = KZ * KG, RS = CZ + 8;  // LDS row stride (elements)
   // up to four chunk groups the next tile's z is fetched while this one computes; wider
   // pairs fetch it after the tile (both copies would not fit the registers)
-  constexpr bool PREFETCH = KZ <= 4;
+  constexpr bool PREFETCH = KZ <= 4 && !STREAM;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int hd = heads * ATT_D;
-  // this launch's part of the projection rows: [lo, hi), as rows then start values
-  const int rows = hi - lo;
+  // the part of the projection rows in LDS: [lo, hi), as rows then start values
+  int lo = parts.bounds[0], hi = parts.bounds[1];
   const bf16* const wl = (const bf16*)smem;
-  const float* const tl = (const float*)(smem + (size_t)rows * RS * 2);  // start values
+  const float* tl = (const float*)(smem + (size_t)(hi - lo) * RS * 2);  // start values
+  // 16-byte chunks of a part's image
+  auto part_chunks = [&](int rows) { return (rows * (CZ + 8) * 2 + rows * 4 + 15) / 16; };
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -122,12 +127,20 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
   };
 
   Pre f;
-  copy_image<KA_THREADS>(image, (chunk_t*)smem, image_chunks, tid, [&]() { fetch(gw, f); });
-  __syncthreads();
+  if constexpr (!STREAM) {
+    copy_image<KA_THREADS>(image, (chunk_t*)smem, part_chunks(hi - lo), tid, [&]() { fetch(gw, f); });
+    __syncthreads();
+  }
 
-  for (int t = gw; t < tiles; t += nw) {
+  // a workgroup-uniform trip count: with STREAM every wave of the workgroup takes part in
+  // each round's barriers, also past the last tile
+  for (int t0 = blockIdx.x * KA_WAVES; t0 < tiles; t0 += nw) {
+    const int t = t0 + wave;
+    const bool active = t < tiles;  // wave-uniform
+    if (!STREAM && !active) break;
+    if constexpr (STREAM) fetch(t, f);  // clamped to the last tile when past it
     int b, r, c0;
-    coords(t, b, r, c0);
+    coords(active ? t : tiles - 1, b, r, c0);
     chunk_t za[2][KZ];
     float mv[2];
 #pragma unroll
@@ -213,15 +226,36 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
                     pack(v, bf16()), (unsigned int)(tile_off(dd, c, np) * 2));
       }
     };
+    // the heads and units of the rows in LDS ([lo, hi))
+    auto compute_rows = [&]() {
 #pragma unroll 1
-    for (int hh = 0; hh < heads; ++hh) head_a(ATT_D * hh, 0, qo);
+      for (int hh = 0; hh < heads; ++hh) head_a(ATT_D * hh, 0, qo);
 #pragma unroll 1
-    for (int hh = 0; hh < heads; ++hh) head_a(hd + ATT_D * hh, 1, ko);
+      for (int hh = 0; hh < heads; ++hh) head_a(hd + ATT_D * hh, 1, ko);
 #pragma unroll 1
-    for (int hh = 0; hh < heads; ++hh) head_a(2 * hd + ATT_D * hh, 2, go);
+      for (int hh = 0; hh < heads; ++hh) head_a(2 * hd + ATT_D * hh, 2, go);
 #pragma unroll 1
-    for (int u = 0; u < hd / 16; ++u) unit_b(3 * hd + 16 * u, false);
-    unit_b(4 * hd, true);
+      for (int u = 0; u < hd / 16; ++u) unit_b(3 * hd + 16 * u, false);
+      unit_b(4 * hd, true);
+    };
+    if constexpr (STREAM) {
+      const chunk_t* src = image;
+#pragma unroll 1
+      for (int pi = 0; pi < parts.count; ++pi) {
+        lo = parts.bounds[pi];
+        hi = parts.bounds[pi + 1];
+        tl = (const float*)(smem + (size_t)(hi - lo) * RS * 2);
+        const int chunks = part_chunks(hi - lo);
+        __syncthreads();  // every wave is done with the previous part
+        copy_image<KA_THREADS>(src, (chunk_t*)smem, chunks, tid, []() {});
+        __syncthreads();
+        if (active) compute_rows();
+        src += chunks;
+      }
+      if (!active) continue;
+    } else {
+      compute_rows();
+    }
     // key-valid bits in stored coordinates (0 on padding): bit k of word c0 / 32 of
     // stored row r is column c0 + k (nonzero mask value); lanes q = 0 hold the tile's
     // 32 values
@@ -235,7 +269,7 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
       word |= (unsigned int)((v0 >> (4 * g)) & 0xfu) << (8 * g) |
               (unsigned int)((v1 >> (4 * g)) & 0xfu) << (8 * g + 4);
     if (lane == 0) mwo[((size_t)b * np + r) * (np / 32) + c0 / 32] = word;
-    if constexpr (!PREFETCH) fetch(t + nw, f);
+    if constexpr (!PREFETCH && !STREAM) fetch(t + nw, f);
   }
 }
 
@@ -584,40 +618,36 @@ static hipError_t launch_attention_kz(const AttnArgs& a, int stages, hipStream_t
   bf16* bias = (bf16*)(ws + L.bias);
   unsigned int* mw = (unsigned int*)(ws + L.ms);
 
-  // projection: persistent waves over 32-pair tiles of the padded stored grid, one launch
-  // per part of the projection rows
+  // projection: persistent waves over 32-pair tiles of the padded stored grid; weights in
+  // several parts pass through LDS part after part
   if (stages & 1) {
     const AttnParts parts = att_proj_parts(a.cz, a.heads);
     if (parts.count < 1) return hipErrorInvalidValue;
-    size_t lds_max = 0;
+    size_t lds = 0;
     for (int i = 0; i < parts.count; ++i) {
       const size_t b = att_part_bytes(a.cz, parts.bounds[i + 1] - parts.bounds[i]);
-      lds_max = b > lds_max ? b : lds_max;
+      lds = b > lds ? b : lds;
     }
-    if (lds_max > ATT_LDS_MAX) return hipErrorInvalidValue;
-    auto fn = ka_project<KZ>;
-    static std::atomic<int> granted{0};
-    hipError_t e = ensure_dynamic_lds((const void*)fn, granted, lds_max);
+    if (lds > ATT_LDS_MAX) return hipErrorInvalidValue;
+    auto fn = parts.count == 1 ? ka_project<KZ, false> : ka_project<KZ, true>;
+    static std::atomic<int> granted1{0}, granted2{0};
+    hipError_t e = ensure_dynamic_lds((const void*)fn, parts.count == 1 ? granted1 : granted2, lds);
     if (e != hipSuccess) return e;
     const long long tiles = (long long)a.batch * np * (np / KA_TW);
     if (tiles > 0x7fffffffLL) return hipErrorInvalidValue;
-    const unsigned char* image = (const unsigned char*)a.proj_image;
-    for (int i = 0; i < parts.count; ++i) {
-      const size_t lds = att_part_bytes(a.cz, parts.bounds[i + 1] - parts.bounds[i]);
-      static std::atomic<int> occ{0};
-      static std::atomic<size_t> occ_lds{0};
-      const int per_cu = resident_blocks((const void*)fn, KA_THREADS, lds, occ, occ_lds);
-      const long long need = (tiles + KA_WAVES - 1) / KA_WAVES;
-      const long long cap = (long long)a.num_cus * per_cu;
-      const int blocks = (int)(need < cap ? need : cap);
-      hipLaunchKernelGGL(fn, dim3(blocks), dim3(KA_THREADS), lds, st, (const bf16*)a.z,
-                         (const bf16*)a.mask, (const chunk_t*)image, (int)(lds / 16), q, k, g, vt,
-                         bias, mw, a.batch, a.n, np, a.heads, a.node, a.mask_all,
-                         parts.bounds[i], parts.bounds[i + 1]);
-      e = hipGetLastError();
-      if (e != hipSuccess) return e;
-      image += lds;
-    }
+    static std::atomic<int> occ1{0}, occ2{0};
+    static std::atomic<size_t> occ_lds1{0}, occ_lds2{0};
+    const int per_cu = parts.count == 1
+                           ? resident_blocks((const void*)fn, KA_THREADS, lds, occ1, occ_lds1)
+                           : resident_blocks((const void*)fn, KA_THREADS, lds, occ2, occ_lds2);
+    const long long need = (tiles + KA_WAVES - 1) / KA_WAVES;
+    const long long cap = (long long)a.num_cus * per_cu;
+    const int blocks = (int)(need < cap ? need : cap);
+    hipLaunchKernelGGL(fn, dim3(blocks), dim3(KA_THREADS), lds, st, (const bf16*)a.z,
+                       (const bf16*)a.mask, (const chunk_t*)a.proj_image, q, k, g, vt, bias, mw,
+                       a.batch, a.n, np, a.heads, a.node, a.mask_all, parts);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
   // attention: one workgroup per stored row
   if (stages & 2) {
