@@ -28,9 +28,14 @@ constexpr int KC_THREADS = 64 * KC_WAVES;
 constexpr int KC_QB = 4;                     // 16-query blocks per attention tile
 constexpr int KC_KB = 2;                     // 16-key blocks per attention step (2 or 4)
 constexpr int KC_MIN_SPLIT = 4;              // workgroups per stored row, at least
-// A query's softmax reference moves only when a score exceeds it by more than this (base
-// 2), so the unnormalised probabilities stay below 2^8: exact in fp32, well inside bf16.
-constexpr float KC_REBASE = 8.f;
+// A query's softmax reference starts at 0 and moves up only when a score exceeds it by more
+// than KC_HI (base 2), so the unnormalised probabilities stay below 2^16, far inside the
+// range of fp32 and bf16 (both keep 8 exponent bits: their relative precision does not
+// depend on the scale). At its first valid key a query whose largest score lies below
+// KC_LO takes that score as its reference instead, so that a row of very small scores
+// cannot underflow.
+constexpr float KC_HI = 16.f;
+constexpr float KC_LO = -16.f;
 
 // The bias planes and the v^T planes are stored in tiles of 16 rows x 32 columns (1 KB in
 // bf16, row-major inside the tile): element (row, col) of a plane with np columns sits at
@@ -283,10 +288,11 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 //     4 KB q + 4 kb + e (e < 4) of query 16 qb + p (the K operand's row p is key
 //     4 KB (p / 4) + 4 kb + p % 4);
 //   online softmax per query in base 2 (log2(e) / sqrt(d) is folded into W_q and
-//     log2(e) into the bias rows), masked keys left out. The reference is the query's
-//     largest score when it was last set and moves only when a score exceeds it by more
-//     than KC_REBASE (then the four lanes p, p^16, p^32, p^48, which hold all keys of a
-//     query, agree on the new one); the sum is kept per lane until the end;
+//     log2(e) into the bias rows), masked keys left out. The reference starts at 0 and
+//     moves only when a score exceeds it by more than KC_HI, or when the query's first
+//     valid scores all lie below KC_LO (then the four lanes p, p^16, p^32, p^48, which
+//     hold all keys of a query, agree on the new one); the sum is kept per lane until the
+//     end;
 //   O^T += V^T P^T: each run of eight of the lane's probabilities of a query ARE its
 //     B-operand chunk once V^T's A chunk holds the same eight keys, one 16-byte run of
 //     the transposed v.
@@ -350,12 +356,13 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) qf[qb] = ld16(qrow + (size_t)(qc0 + 16 * qb + p) * ATT_D + 8 * q);
       // Per query (the same on its four lanes): the reference mref that every score is
-      // taken relative to, and whether it has been set (bit `lane` of hasref: the query
-      // has seen a valid key). lsum and o are the sum of the probabilities and O^T, both
-      // relative to 2^mref.
+      // taken relative to, and whether the query has seen a valid key (bit `lane` of
+      // hasref). lsum and o are the sum of the probabilities and O^T, both relative to
+      // 2^mref.
       f32x4 o[2][QB];
       float mref[QB], lsum[QB];
       unsigned long long hasref[QB];  // wave-uniform
+      bool zref = true;               // every mref of the wave is 0 (wave-uniform)
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
         mref[qb] = 0.f;
@@ -433,19 +440,29 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 #pragma unroll 1
       for (int ks = 0; ks < kend; ++ks) {
         const unsigned long long w = mw;
-        // S^T relative to the reference: the accumulator starts at bias - mref
+        // S^T relative to the reference: the accumulator starts at bias - mref, or at the
+        // bias itself while every reference of the wave is 0 (the common case)
         f32x4 s[KB][QB];
+        auto scores = [&](auto zero_ref) {
 #pragma unroll
-        for (int kb = 0; kb < KB; ++kb)
+          for (int kb = 0; kb < KB; ++kb)
 #pragma unroll
-          for (int qb = 0; qb < QB; ++qb) {
-            const unsigned int b01 = sb[kb >> 1][qb][2 * (kb & 1)];
-            const unsigned int b23 = sb[kb >> 1][qb][2 * (kb & 1) + 1];
-            const float m = mref[qb];
-            const f32x4 b0 = {__uint_as_float(b01 << 16) - m, __uint_as_float(b01 & 0xffff0000u) - m,
-                              __uint_as_float(b23 << 16) - m, __uint_as_float(b23 & 0xffff0000u) - m};
-            s[kb][qb] = mma16(b0, kf[kb], qf[qb], bf16());
-          }
+            for (int qb = 0; qb < QB; ++qb) {
+              const unsigned int b01 = sb[kb >> 1][qb][2 * (kb & 1)];
+              const unsigned int b23 = sb[kb >> 1][qb][2 * (kb & 1) + 1];
+              f32x4 b0 = {__uint_as_float(b01 << 16), __uint_as_float(b01 & 0xffff0000u),
+                          __uint_as_float(b23 << 16), __uint_as_float(b23 & 0xffff0000u)};
+              if constexpr (!decltype(zero_ref)::value) {
+                const float m = mref[qb];
+                b0 = f32x4{b0[0] - m, b0[1] - m, b0[2] - m, b0[3] - m};
+              }
+              s[kb][qb] = mma16(b0, kf[kb], qf[qb], bf16());
+            }
+        };
+        if (zref)
+          scores(std::true_type{});
+        else
+          scores(std::false_type{});
         load_kbm(ks + 1);  // the last step reloads itself (unused)
         // A step with masked keys first turns their scores into -inf, so that their
         // exponentials below are exactly 0; the common case (every key of the step valid)
@@ -462,12 +479,12 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
             }
         }
         // Online softmax with a reference that moves only when it must: a score more than
-        // KC_REBASE above it (or the first valid key of a query) moves the query's
-        // reference to its largest score of the step and scales what it has summed so
-        // far. Otherwise the step's probabilities are 2^s directly, at most 2^KC_REBASE,
-        // with no maximum across lanes and no rescaling. The test is per lane, the branch
-        // per wave (rare after the first step). The result is the same softmax: o and l
-        // carry the same factor 2^-mref, which the division at the end removes.
+        // KC_HI above it (or, at the query's first valid key, a largest score below KC_LO)
+        // moves the query's reference to its largest score of the step and scales what it
+        // has summed so far. Otherwise the step's probabilities are 2^s directly, at most
+        // 2^KC_HI, with no maximum across lanes and no rescaling. The test is per lane, the
+        // branch per wave (rare after the first step). The result is the same softmax: o
+        // and l carry the same factor 2^-mref, which the division at the end removes.
         // The lane's largest score of query block qb in this step:
         auto lane_max = [&](int qb) {
           float v = s[0][qb][0];
@@ -481,10 +498,11 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         bool move = false, unset = false;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          move |= lane_max(qb) > KC_REBASE;
+          move |= lane_max(qb) > KC_HI;
           unset |= hasref[qb] != ~0ull;
         }
         if (unset || __any(move)) {
+          bool moved = false;
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb) {
             // the query's largest score of the step relative to its reference (-inf when
@@ -492,8 +510,9 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
             const float lm = lane_max(qb);
             float rm = fmaxf(lm, lane_value(lm, lane ^ 16));
             rm = fmaxf(rm, lane_value(rm, lane ^ 32));
-            const bool has = (hasref[qb] >> lane) & 1ull;  // a reference, and what was summed
-            const bool mv = rm > (has ? KC_REBASE : NEG);
+            const bool has = (hasref[qb] >> lane) & 1ull;  // a valid key was seen before
+            const bool valid = rm > NEG;                   // the step has a valid key
+            const bool mv = has ? rm > KC_HI : valid && (rm > KC_HI || rm < KC_LO);
             const float delta = mv ? rm : 0.f;
             // before the first valid key nothing was summed: o and lsum are 0
             const float f = has ? __builtin_amdgcn_exp2f(-delta) : 0.f;
@@ -507,8 +526,10 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
 #pragma unroll
               for (int e = 0; e < 4; ++e) s[kb][qb][e] -= delta;
             mref[qb] += delta;
-            hasref[qb] = __ballot(has || mv);
+            moved |= mv;
+            hasref[qb] = __ballot(has || valid);
           }
+          zref = zref && !__any(moved);
         }
         // probabilities in base 2 (results below 2^-126 flush to 0)
         chunk_t pb[KB / 2][QB];

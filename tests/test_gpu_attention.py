@@ -75,13 +75,14 @@ def test_attention_repeatable(node):
 @pytest.mark.parametrize("node", NODES)
 @pytest.mark.parametrize("case", ["rising", "sinking", "leading_keys_masked"])
 def test_attention_moving_softmax_reference(node, case):
-    """Each query's softmax reference is set at its first valid key step and moves only
-    when a later score lies more than 8 (base 2) above it. A pair channel that grows along
-    the key index, with a large bias weight on it, shapes the scores: "rising" (about -18
-    to +20) moves the reference up later in the row for about 95% of the queries, with
-    the sums scaled; "sinking" (about -29 to -2) sets it far below 0 and moves it up for
-    about 8% of them as the scores climb. "leading_keys_masked": the first 70 keys of every row are masked, so the first
-    two key steps have no valid key at all and the reference is set in the third. The
+    """Each query's softmax reference starts at 0 and moves up only when a score lies
+    more than 16 (base 2) above it; at the query's first valid key step it drops to the
+    step's largest score when that lies below -16. A pair channel that grows along the key
+    index, with a large bias weight on it, shapes the scores: "rising" (about -18 to +22)
+    moves the reference up later in the row for about 4% of the queries, with the sums
+    scaled; "sinking" (about -29 to -2) drops it below 0 at the first key step for 25-60%
+    of them. "leading_keys_masked": the first 70 keys of every row are masked, so the
+    first two key steps have no valid key at all and the third is the first one summed. The
     result is the plain softmax every time. The scores are large, so the bf16 storage of
     z-hat, the weights, q, k, v, the gate, the bias and the probabilities costs more here
     than elsewhere: a CPU model of exactly those roundings, with the textbook softmax,
