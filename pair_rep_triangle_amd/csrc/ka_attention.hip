@@ -53,6 +53,11 @@ __device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, chunk_t v,
   typedef __attribute__((ext_vector_type(4))) int i32x4;
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, 0x10);
 }
+// The same store non-temporal (cache policy nt): for output that nothing here reads again.
+__device__ __forceinline__ void store16_nt(__amdgpu_buffer_rsrc_t r, chunk_t v, unsigned int voff) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, 0x2);
+}
 
 // ---------------------------------------------------------------------------------------
 // ka_project. A wave tile is 32 consecutive stored columns (two 16-pair subtiles) of one
@@ -578,15 +583,24 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
     // out^T = W_o o^T + b_o per group of 32 output channels, as two 16-row halves. The
     // handle stores W_o's rows (and b_o) permuted per group: row 4q + rr of half hf is
     // channel 8q + 4 hf + rr, so lane (p, q) ends with channels 32g + 8q .. + 7 of query
-    // 16 qb + p and writes them as one 16-byte store.
+    // 16 qb + p. Each wave takes one block of 16 queries and runs the groups two at a
+    // time: after a swap of one 16-byte chunk between lanes p and p ^ 8 of each row of 16
+    // lanes (a DPP rotation by 8 written to half of the row), each of the two store
+    // instructions writes whole 128-byte lines (one query's 64 channels from 8 lanes),
+    // non-temporal: the output is not read again here and would only displace K, V^T and
+    // the bias from the caches (ka_core 156.3 -> 154.7 us, wide 1403 -> 1340 us, against
+    // half lines from two waves; device-scope or default-policy stores of the same lines
+    // made the step slower). A group left over (c_z an odd number of groups) is written
+    // in half lines.
 #pragma unroll 1
     for (int sl = 0; sl < NSLICE; ++sl) {
       const int g0 = sl * (SROWS / 32);  // the slice's first group
+      const int ng = CZ / 32 - g0 < SROWS / 32 ? CZ / 32 - g0 : SROWS / 32;  // its groups
       if constexpr (NSLICE > 1) {
         // the slice's W_o rows and b_o values into LDS (after every wave is done with the
         // previous slice)
         if (sl > 0) __syncthreads();
-        const int srows = CZ - 32 * g0 < SROWS ? CZ - 32 * g0 : SROWS;
+        const int srows = 32 * ng;
         const chunk_t* const src = (const chunk_t*)((const unsigned char*)image +
                                                     (size_t)32 * g0 * os_stride * 2);
         const int wchunks = srows * os_stride * 2 / 16;
@@ -596,31 +610,61 @@ __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3)))
         for (int i = tid; i < srows / 4; i += KC_THREADS) ((chunk_t*)bo)[i] = bsrc[i];
         __syncthreads();
       }
-    for (int g = g0 + wave; g < g0 + SROWS / 32 && g < CZ / 32; g += KC_WAVES) {
-#pragma unroll 1
-      for (int qb = 0; qb < QB; ++qb) {  // one query block at a time: few live registers
-        f32x4 acc[2];
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
+      for (int qb = wave; qb < QB; qb += KC_WAVES) {
+        const int qbase = qc0 + 16 * qb;
+        // the block's first query is the stores' (wave-uniform) base: the offsets of its 16
+        // queries stay below 15 n c_z + c_z elements, inside 32 bits at any supported n
+        const size_t x0 = ending ? (size_t)qbase : (size_t)r, y0 = ending ? (size_t)r : (size_t)qbase;
+        const __amdgpu_buffer_rsrc_t ro =
+            buffer_rsrc_u32(out + (((size_t)b * n + x0) * n + y0) * CZ, 0xffffffffu);
+        const unsigned int qstride = (unsigned int)(ending ? n * CZ : CZ) * 2u;  // bytes per query
+        auto unit = [&](int g, int hf) {
           const int u = 2 * (g - g0) + hf;  // the unit's rows in the slice
-          acc[hf] = ld16f(bo + 16 * u + 4 * q);
+          f32x4 acc = ld16f(bo + 16 * u + 4 * q);
           for (int kk = 0; kk < hd / 32; ++kk)
-            acc[hf] = mma16(acc[hf], ld16(wo + (16 * u + p) * os_stride + 32 * kk + 8 * q),
-                            ld16(os + (16 * qb + p) * os_stride + 32 * kk + 8 * q), bf16());
-        }
-        const int qc = qc0 + 16 * qb + p;
-        if (qc < n) {
+            acc = mma16(acc, ld16(wo + (16 * u + p) * os_stride + 32 * kk + 8 * q),
+                        ld16(os + (16 * qb + p) * os_stride + 32 * kk + 8 * q), bf16());
+          return acc;
+        };
+        auto chunk = [&](const f32x4& h0, const f32x4& h1) {
           float v[8];
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v[e] = acc[e >> 2][e & 3];
-          const size_t x = ending ? (size_t)qc : (size_t)r, y = ending ? (size_t)r : (size_t)qc;
-          // non-temporal: the output is not read again here and would only displace
-          // K, V^T and the bias from the caches (ka_core 235 -> 229 us)
-          __builtin_nontemporal_store(
-              pack(v, bf16()), (chunk_t*)(out + (((size_t)b * n + x) * n + y) * CZ + 32 * g + 8 * q));
+          for (int e = 0; e < 4; ++e) {
+            v[e] = h0[e];
+            v[4 + e] = h1[e];
+          }
+          return pack(v, bf16());
+        };
+        int gi = 0;
+#pragma unroll 1
+        for (; gi + 1 < ng; gi += 2) {
+          const int g = g0 + gi;
+          const chunk_t c0 = chunk(unit(g, 0), unit(g, 1));
+          const chunk_t c1 = chunk(unit(g + 1, 0), unit(g + 1, 1));
+          // lo: lanes p < 8 keep group g of query p, lanes p >= 8 take group g + 1 of query
+          // p - 8 from lane p - 8; hi: lanes p < 8 take group g of query p + 8 from lane
+          // p + 8, lanes p >= 8 keep group g + 1 of query p
+          chunk_t lo, hi;
+#pragma unroll
+          for (int d = 0; d < 4; ++d) {
+            lo[d] = (unsigned int)__builtin_amdgcn_update_dpp((int)c0[d], (int)c1[d], 0x128, 0xf, 0xc, false);
+            hi[d] = (unsigned int)__builtin_amdgcn_update_dpp((int)c1[d], (int)c0[d], 0x128, 0xf, 0x3, false);
+          }
+          const int qa = p & 7;  // query of lo (hi: qa + 8)
+          const unsigned int off = (unsigned int)qa * qstride + (unsigned int)(32 * (g + (p >> 3)) + 8 * q) * 2u;
+          if (qbase + qa < n) store16_nt(ro, lo, off);
+          if (qbase + qa + 8 < n) store16_nt(ro, hi, off + 8u * qstride);
+        }
+        if (gi < ng) {
+          const int g = g0 + gi;
+          const chunk_t c0 = chunk(unit(g, 0), unit(g, 1));
+          const int qc = qbase + p;
+          if (qc < n) {
+            const size_t x = ending ? (size_t)qc : (size_t)r, y = ending ? (size_t)r : (size_t)qc;
+            __builtin_nontemporal_store(c0, (chunk_t*)(out + (((size_t)b * n + x) * n + y) * CZ + 32 * g + 8 * q));
+          }
         }
       }
-    }
     }
     __syncthreads();
   }
