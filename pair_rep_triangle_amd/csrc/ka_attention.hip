@@ -303,10 +303,10 @@ __global__ __launch_bounds__(KA_THREADS) void ka_project(
 //     the transposed v.
 // Then o = O^T / l * gate goes to LDS as [query][h*d + channel]; after a barrier the
 // waves split the output channels: out^T = W_o o^T + b_o with W_o rows from LDS as A.
-// Three waves per SIMD: up to c_z = 128 the kernel needs 166 registers; wider, the W_o
-// slice copies would take it past 170 (two waves), and the registers that spill instead
-// (4 at c_z = 256 and 384, about 18 at the other widths, none inside the key loop) cost
-// less (wide ka_core 1484 -> 1370 us).
+// Three waves per SIMD (at most 170 registers): at c_z = 128 the kernel needs 166 with no
+// spills; at the other widths 2 to 20 registers spill, all outside the key loop, which
+// costs less than the third wave would (wide ka_core 1484 -> 1370 us when the W_o slices
+// came in).
 template <int KZ, int QB, int KB>
 __global__ __launch_bounds__(KC_THREADS) __attribute__((amdgpu_waves_per_eu(3))) void ka_core(
     const bf16* __restrict__ qi, const bf16* __restrict__ ki, const bf16* __restrict__ gi,
