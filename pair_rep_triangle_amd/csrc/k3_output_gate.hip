@@ -254,6 +254,14 @@ __global__ __launch_bounds__(K3_THREADS) void k3_output_gate(
   }
 }
 
+// A 16-byte store through a resource on a wave-uniform base (32-bit lane offsets instead
+// of 64-bit addresses), non-temporal (cache policy nt). The scalar offset stays 0.
+constexpr int K3_STORE_POLICY = 0x2;
+__device__ __forceinline__ void k3_store16(__amdgpu_buffer_rsrc_t r, chunk_t v, unsigned int voff) {
+  typedef __attribute__((ext_vector_type(4))) int i32x4;
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(i32x4, v), r, (int)voff, 0, K3_STORE_POLICY);
+}
+
 // ---------------------------------------------------------------------------------------
 // Wave-independent form (used whenever the weight slice and the per-wave staging fit
 // LDS). Workgroup = 8 waves; blockIdx.y selects a group of `ug` output units (16 output
@@ -589,7 +597,9 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
     const int last = n - 1 - j0;        // last real pair of the tile (< TW when ragged)
     const size_t row0 = ((size_t)bb * n + i) * n + j0;
     constexpr int NOUT = (TW * CPPM + 63) / 64;
-    size_t goff[NOUT];
+    // chunk k of the lane: element offset from the tile's first output element (pair j0,
+    // channel ch0), the same for out and z
+    unsigned int goff[NOUT];
     int soff[NOUT];
 #pragma unroll
     for (int k = 0; k < NOUT; ++k) {
@@ -598,12 +608,15 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
       pr = pr < last ? pr : last;
       pr = pr < TW ? pr : TW - 1;
       cc = cc < cpp ? cc : cpp - 1;
-      goff[k] = (row0 + pr) * cz + ch0 + cc * E;
+      goff[k] = (unsigned int)(pr * cz + cc * E);
       soff[k] = pr * sst + cc * E;
     }
     // The output is the last thing the update writes and nothing in the update reads it
     // again: non-temporal stores keep it from displacing x and z in the caches (K3 took
-    // 52.7 instead of 55.2 us at N = 512, c_z = c = 128).
+    // 52.7 instead of 55.2 us at N = 512, c_z = c = 128). Device-scope stores of the same
+    // whole lines made K3 alone 0.3 us faster but the two-direction step 8% slower.
+    const size_t obase = row0 * cz + ch0;
+    const __amdgpu_buffer_rsrc_t ro = buffer_rsrc_u32(out + obase, 0xffffffffu);
     // a skipped tile's update is zero: its staging rows are not read
     const chunk_t zero = {0u, 0u, 0u, 0u};
     if constexpr (RESID) {
@@ -612,15 +625,14 @@ __global__ __launch_bounds__(64 * W) void k3_output_gate_waves(
       // be z itself: each pair is read and written only by this wave, in this tile).
       chunk_t zr[NOUT];
 #pragma unroll
-      for (int k = 0; k < NOUT; ++k) zr[k] = ld16(z + goff[k]);
+      for (int k = 0; k < NOUT; ++k) zr[k] = ld16(z + obase + goff[k]);
 #pragma unroll
       for (int k = 0; k < NOUT; ++k)
-        __builtin_nontemporal_store(add_chunks(skip ? zero : ld16(stg + soff[k]), zr[k], T()),
-                                    (chunk_t*)(out + goff[k]));
+        k3_store16(ro, add_chunks(skip ? zero : ld16(stg + soff[k]), zr[k], T()), goff[k] * (unsigned int)sizeof(T));
     } else {
 #pragma unroll
       for (int k = 0; k < NOUT; ++k)
-        __builtin_nontemporal_store(skip ? zero : ld16(stg + soff[k]), (chunk_t*)(out + goff[k]));
+        k3_store16(ro, skip ? zero : ld16(stg + soff[k]), goff[k] * (unsigned int)sizeof(T));
     }
   }
 }
