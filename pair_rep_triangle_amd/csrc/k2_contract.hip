@@ -39,13 +39,13 @@ __device__ __forceinline__ void store16_sc1(__amdgpu_buffer_rsrc_t r, chunk_t v,
 // Flat grid of ceil(np/256) * ceil(np/BN) * batch*c workgroups, remapped so that the
 // tiles of one channel land on the same XCD and share its L2.
 constexpr int K2_BM = 256;
-constexpr int K2_STAGES = 3;
 constexpr int K2_KC = 4;                                   // 16-byte chunks per row and stage
 constexpr int K2_A_BYTES = K2_BM * K2_KC * 16;             // 16 KB
 static_assert(N_PAD % 64 == 0, "operand rows of whole 128-byte lines; 64-pair input tiles");
 
-template <int WN, int NTW>
+template <int WN, int NTW, int ST>
 struct K2Shape {
+  static constexpr int STAGES = ST;                        // LDS ring buffers
   static constexpr int WCOLS = 32 * NTW;                   // tile columns per wave
   static constexpr int BN = WCOLS * WN;
   static constexpr int WAVES = 2 * WN;
@@ -55,7 +55,7 @@ struct K2Shape {
   static constexpr int LOADS_A = K2_BM / 16 / WAVES;       // 1 KB blocks per wave and stage
   static constexpr int LOADS = LOADS_A + BN / 16 / WAVES;
   static constexpr int OUT_ROWS = BN == 128 ? K2_BM : 128; // output rows staged at a time
-  static constexpr int RING_BYTES = K2_STAGES * STAGE_BYTES;
+  static constexpr int RING_BYTES = ST * STAGE_BYTES;
   static constexpr int OUT_BYTES = OUT_ROWS * (BN + 8) * 2;
   static constexpr int LDS_BYTES = RING_BYTES > OUT_BYTES ? RING_BYTES : OUT_BYTES;
   static constexpr int MIN_BLOCKS = 2 * LDS_BYTES <= 160 * 1024 ? 2 : 1;  // per CU
@@ -103,12 +103,12 @@ __device__ __forceinline__ void mfma_load_groups() {
 // and stores zeros. The padded side np is a multiple of 64, not of the tile: the last tile
 // row and column may be partial, and their stores past np are dropped.
 // Both forms keep two waves per SIMD (256 registers per lane).
-template <class T, int WN, int NTW>
-__global__ __launch_bounds__((K2Shape<WN, NTW>::THREADS), (K2Shape<WN, NTW>::MIN_BLOCKS))
+template <class T, int WN, int NTW, int ST>
+__global__ __launch_bounds__((K2Shape<WN, NTW, ST>::THREADS), (K2Shape<WN, NTW, ST>::MIN_BLOCKS))
 void k2_contract(
     const T* __restrict__ A, const T* __restrict__ B, T* __restrict__ X, int n, int np,
     const int* __restrict__ extents, int c) {
-  using S = K2Shape<WN, NTW>;
+  using S = K2Shape<WN, NTW, ST>;
   constexpr int BN = S::BN, NW = S::WAVES, NT = S::THREADS;
   constexpr int LOADS = S::LOADS, LOADS_A = S::LOADS_A;
   constexpr int E = Traits<T>::E;
@@ -157,7 +157,7 @@ void k2_contract(
     voff[q] = (unsigned int)(((size_t)row * np + c * E) * sizeof(T));
   }
   auto issue_one = [&](int s, int q) {
-    unsigned char* base = lds + (s % K2_STAGES) * S::STAGE_BYTES;
+    unsigned char* base = lds + (s % ST) * S::STAGE_BYTES;
     const int soff = s * KT * (int)sizeof(T);
     if (q < LOADS_A)
       lds_dma16_buf(ra, voff[q], soff, base + (wave + NW * q) * 1024);
@@ -183,8 +183,8 @@ void k2_contract(
   // One stage: all operand reads first, then the MFMAs; with `next` >= 0 the loads of
   // stage `next` are placed between the MFMAs (sched_group_barrier: 2 or 3 MFMAs, one
   // load, six times).
-  auto compute = [&](int s, int next) {
-    const unsigned char* cur = lds + (s % K2_STAGES) * S::STAGE_BYTES;
+  auto compute = [&](int s, int next, int next2 = -1) {
+    const unsigned char* cur = lds + (s % ST) * S::STAGE_BYTES;
     chunk_t fa[2][4], fb[2][NTW];
 #pragma unroll
     for (int step = 0; step < K2_KC / 2; ++step) {
@@ -205,48 +205,76 @@ void k2_contract(
 #pragma unroll
         for (int nt = 0; nt < NTW; ++nt)
           acc[mt][nt] = mma32(acc[mt][nt], fb[step][nt], fa[step][mt], T());
-    if (next >= 0) {
+    if (next2 >= 0) {
+      issue(next);
+      issue(next2);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2 * (4 + NTW), 0);  // the operand reads
+      mfma_load_groups<MFMAS, 2 * LOADS>();
+    } else if (next >= 0) {
       issue(next);
       __builtin_amdgcn_sched_group_barrier(0x100, 2 * (4 + NTW), 0);  // the operand reads
       mfma_load_groups<MFMAS, LOADS>();
     }
   };
-  // stage s's loads are done once at most the next stage's remain; every wave's part of
-  // stage s is then in LDS after the barrier, and every wave is done with stage s-1, whose
-  // buffer the loads of stage s+2 overwrite. A bare s_barrier: __syncthreads() would also
-  // wait for the stage s+1 loads still in flight. The empty asm statements keep the
-  // compiler from moving LDS accesses across it.
+  // Stage s's loads are done once at most the later stages' loads (P of them) remain;
+  // every wave's part of stage s is then in LDS after the barrier, and every wave is done
+  // with the stages whose buffers the next loads overwrite. A bare s_barrier:
+  // __syncthreads() would also wait for the later stages' loads still in flight. The empty
+  // asm statements keep the compiler from moving LDS accesses across it.
   // The wait also covers this wave's LDS reads (lgkmcnt(0)), so none of stage s-1 is still
   // pending when another wave's loads start to overwrite its buffer.
-  auto arrive = [&](bool last) {
-    if (!last)
-      __builtin_amdgcn_s_waitcnt(0x0070 | LOADS);  // vmcnt(LOADS) lgkmcnt(0)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0070);  // vmcnt(0) lgkmcnt(0)
+  auto arrive = [&](auto pending) {
+    constexpr int P = decltype(pending)::value;
+    static_assert(P * LOADS < 16, "vmcnt in the low field");
+    __builtin_amdgcn_s_waitcnt(0x0070 | (P * LOADS));  // vmcnt(P * LOADS) lgkmcnt(0)
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
   };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  static_assert(ST == 3 || ST == 4, "three buffers one stage at a time, or four in pairs");
 
   // stages of the k loop: up to the bound rounded up to a stage (np is a multiple of the
   // stage), none when the tile lies past the bound
   const int nst = (rows_a == 0 || rows_b == 0) ? 0 : (ext + KT - 1) / KT;
-  if (nst >= 2) {
-    issue(0);
-    issue(1);
+  if constexpr (ST == 3) {
+    // one barrier per stage, two stages ahead
+    if (nst >= 2) {
+      issue(0);
+      issue(1);
 #pragma unroll 1
-    for (int s = 0; s + 2 < nst; ++s) {
-      arrive(false);
-      compute(s, s + 2);
+      for (int s = 0; s + 2 < nst; ++s) {
+        arrive(P1());
+        compute(s, s + 2);
+      }
+      arrive(P1());
+      compute(nst - 2, -1);
+      arrive(P0());
+      compute(nst - 1, -1);
+    } else if (nst == 1) {
+      issue(0);
+      arrive(P0());
+      compute(0, -1);
     }
-    arrive(false);
-    compute(nst - 2, -1);
-    arrive(true);
-    compute(nst - 1, -1);
-  } else if (nst == 1) {
-    issue(0);
-    arrive(true);
-    compute(0, -1);
+  } else {
+    // one barrier per pair of stages (buffers 0-1 and 2-3 alternate): the first stage of a
+    // pair issues the loads of both stages of the next pair between its MFMAs, so they
+    // have the second stage's compute to arrive
+    if (nst > 0) {
+      issue(0);
+      if (nst > 1) issue(1);
+      int s = 0;
+#pragma unroll 1
+      for (; s + 2 < nst; s += 2) {
+        arrive(P0());
+        compute(s, s + 2, s + 3 < nst ? s + 3 : -1);
+        compute(s + 1, -1);
+      }
+      arrive(P0());
+      compute(s, -1);
+      if (s + 1 < nst) compute(s + 1, -1);
+    }
   }
   __syncthreads();  // all waves are done reading the ring before it holds the output
 
@@ -306,8 +334,12 @@ void k2_contract(
 
 // bf16 storage: 256 x 256 tiles, 8 waves of 128 x 64 (at N = 2048 the matrix unit time
 // per tile is 9% lower than with 256 x 128 tiles; 4 waves of 128 x 128 each run as fast but
-// move accumulators between register files inside the loop)
-constexpr int K2_BF16_WN = 4, K2_BF16_NTW = 2;
+// move accumulators between register files inside the loop). Up to a padded side of 1024
+// the operands come back from the last-level cache quickly and one barrier per pair of
+// stages is faster (N = 512: 39.7 against 42.1 us); at N = 2048 they stream from HBM, and
+// a pair's eight loads bunched into one stage's MFMAs cost more than the barriers saved
+// (2254 against 2039 us), so there one stage at a time, two ahead.
+constexpr int K2_BF16_WN = 4, K2_BF16_NTW = 2, K2_PAIRED_MAX_NP = 1024;
 
 template <int BN>
 static size_t k2_grid_of(int np, int batch, int c) {
@@ -317,21 +349,23 @@ static size_t k2_grid_of(int np, int batch, int c) {
 // the larger of the two forms' grids (the narrow form's)
 size_t k2_grid(int np, int batch, int c) { return k2_grid_of<128>(np, batch, c); }
 
-template <class T, int WN, int NTW>
+template <class T, int WN, int NTW, int ST>
 static void launch_k2_form(const StageArgs& a, hipStream_t st) {
-  using S = K2Shape<WN, NTW>;
+  using S = K2Shape<WN, NTW, ST>;
   dim3 grid((unsigned)k2_grid_of<S::BN>(a.np, a.batch, a.c));
-  hipLaunchKernelGGL((k2_contract<T, WN, NTW>), grid, dim3(S::THREADS), 0, st,
+  hipLaunchKernelGGL((k2_contract<T, WN, NTW, ST>), grid, dim3(S::THREADS), 0, st,
                      (const T*)a.a, (const T*)a.b, (T*)a.x, a.n, a.np, a.extents, a.c);
 }
 
 // fp32 storage keeps the 256 x 128 form (its stage holds four times the MFMAs of a bf16
 // stage, so its loads are already a smaller share)
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st) {
-  if (bf16_storage)
-    launch_k2_form<bf16, K2_BF16_WN, K2_BF16_NTW>(a, st);
+  if (bf16_storage && a.np <= K2_PAIRED_MAX_NP)
+    launch_k2_form<bf16, K2_BF16_WN, K2_BF16_NTW, 4>(a, st);
+  else if (bf16_storage)
+    launch_k2_form<bf16, K2_BF16_WN, K2_BF16_NTW, 3>(a, st);
   else
-    launch_k2_form<float, 2, 2>(a, st);
+    launch_k2_form<float, 2, 2, 3>(a, st);
   return hipGetLastError();
 }
 
