@@ -334,12 +334,14 @@ void k2_contract(
 
 // bf16 storage: 256 x 256 tiles, 8 waves of 128 x 64 (at N = 2048 the matrix unit time
 // per tile is 9% lower than with 256 x 128 tiles; 4 waves of 128 x 128 each run as fast but
-// move accumulators between register files inside the loop). Up to a padded side of 1024
-// the operands come back from the last-level cache quickly and one barrier per pair of
-// stages is faster (N = 512: 39.7 against 42.1 us); at N = 2048 they stream from HBM, and
-// a pair's eight loads bunched into one stage's MFMAs cost more than the barriers saved
-// (2254 against 2039 us), so there one stage at a time, two ahead.
-constexpr int K2_BF16_WN = 4, K2_BF16_NTW = 2, K2_PAIRED_MAX_NP = 1024;
+// move accumulators between register files inside the loop). While a and b (all planes
+// of the launch) fit the 256 MiB last-level cache, the operands come back quickly and one
+// barrier per pair of stages is faster (N = 512, 134 MB: 39.7 against 42.1 us); when they
+// stream from HBM, a pair's eight loads bunched into one stage's MFMAs cost more than the
+// barriers saved (B = 2, N = 768, 604 MB: 322 against 286 us; N = 2048: 2254 against
+// 2039 us), so there one stage at a time, two ahead.
+constexpr int K2_BF16_WN = 4, K2_BF16_NTW = 2;
+constexpr size_t K2_PAIRED_MAX_OPERAND_BYTES = size_t(256) << 20;
 
 template <int BN>
 static size_t k2_grid_of(int np, int batch, int c) {
@@ -360,7 +362,8 @@ static void launch_k2_form(const StageArgs& a, hipStream_t st) {
 // fp32 storage keeps the 256 x 128 form (its stage holds four times the MFMAs of a bf16
 // stage, so its loads are already a smaller share)
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st) {
-  if (bf16_storage && a.np <= K2_PAIRED_MAX_NP)
+  const size_t operand_bytes = 2 * (size_t)a.batch * a.c * a.np * a.np * sizeof(bf16);
+  if (bf16_storage && operand_bytes <= K2_PAIRED_MAX_OPERAND_BYTES)
     launch_k2_form<bf16, K2_BF16_WN, K2_BF16_NTW, 4>(a, st);
   else if (bf16_storage)
     launch_k2_form<bf16, K2_BF16_WN, K2_BF16_NTW, 3>(a, st);
