@@ -363,7 +363,12 @@ static void launch_k2_form(const StageArgs& a, hipStream_t st) {
 // stage, so its loads are already a smaller share)
 hipError_t launch_k2(bool bf16_storage, const StageArgs& a, hipStream_t st) {
   const size_t operand_bytes = 2 * (size_t)a.batch * a.c * a.np * a.np * sizeof(bf16);
-  if (bf16_storage && operand_bytes <= K2_PAIRED_MAX_OPERAND_BYTES)
+  // fewer 256 x 256 tiles than two per CU leave CUs idle (N = 256: 128 tiles): there the
+  // 256 x 128 form, two workgroups per CU
+  const bool wide_fills = k2_grid_of<256>(a.np, a.batch, a.c) >= 2 * (size_t)a.num_cus;
+  if (bf16_storage && !wide_fills)
+    launch_k2_form<bf16, 2, 2, 3>(a, st);
+  else if (bf16_storage && operand_bytes <= K2_PAIRED_MAX_OPERAND_BYTES)
     launch_k2_form<bf16, K2_BF16_WN, K2_BF16_NTW, 4>(a, st);
   else if (bf16_storage)
     launch_k2_form<bf16, K2_BF16_WN, K2_BF16_NTW, 3>(a, st);
