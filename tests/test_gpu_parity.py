@@ -49,9 +49,10 @@ def test_wide_pair_track_workload_full_output(direction):
 
 
 def _line_set(rng, n, valid=None):
-    """Complete rows and columns that pass through every 256 x 128 tile of the contraction
-    (one random row per 256 rows, one random column per 128 columns), plus the first and
-    last residue and, when padded, both sides of the valid boundary."""
+    """Complete rows and columns that pass through every tile of the contraction, 256 rows
+    by 128 or 256 columns (one random row per 256 rows, one random column per 128
+    columns), plus the first and last residue and, when padded, both sides of the valid
+    boundary."""
     rows = [int(rng.integers(r, min(n, r + 256))) for r in range(0, n, 256)]
     cols = [int(rng.integers(c0, min(n, c0 + 128))) for c0 in range(0, n, 128)]
     edge = [0, n - 1] + ([valid - 1, valid] if valid is not None and valid < n else [])

@@ -176,7 +176,7 @@ def test_chained_pair_update(dtype, B, N, c_z, c):
 
 def test_chained_headline_workload_lines():
     """The masked N = 512 workload, chained in place; complete output rows and columns
-    through every 256 x 128 contraction tile, for both steps."""
+    through every contraction tile (256 rows by 128 or 256 columns), for both steps."""
     d = make_workload("n512_cz128_c128_bf16_masked", seed=0)
     w_in = make_weights(np.random.default_rng(1), 128, 128)
     z, m, z_host, m_host = to_device(d, "bf16")
